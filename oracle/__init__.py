@@ -1,0 +1,214 @@
+"""Oracle: plain CPU reference for block-quantized decode matvec.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, ``__graft_entry__.smoke()`` and
+the benchmark's CPU-baseline leg may import this package. The GPU library under
+``quantized_decode_matvec_amd`` never imports it, and this package imports
+nothing from there: the two share no code. The arithmetic lives in
+``oracle.c`` (plain C, one IEEE operation per step, fp64 accumulation); this
+module only builds it with gcc and marshals numpy arrays through ctypes.
+
+Formats (codes and planes as numpy arrays; W is N x K row-major, K % 32 == 0):
+
+* int4: codes uint8 [N, K/2] (u = q + 8, element 2j in the low nibble),
+  scale uint16 [N, K/32] (fp16 bits).
+* fp4:  codes uint8 [N, K/2] (E2M1, sign in bit 3), scale uint8 [N, K/32] (e8m0).
+* int8: codes int8 [N, K], scale uint16 [N, K/32].
+* km4:  codes uint8 [N, K/2] (4-bit indices), lut uint16 [N, 16] (fp16 bits).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+FMT_INT4, FMT_FP4, FMT_INT8, FMT_KM4 = 0, 1, 2, 3
+FORMATS = {"int4": FMT_INT4, "fp4": FMT_FP4, "int8": FMT_INT8, "km4": FMT_KM4}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        L.orc_f16_to_f64.restype = ctypes.c_double
+        L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.orc_f64_to_f16.restype = ctypes.c_uint16
+        L.orc_f64_to_f16.argtypes = [ctypes.c_double]
+        L.orc_pack_fp4.argtypes = [P, i64, i64, P, P]
+        L.orc_pack_int4.argtypes = [P, i64, i64, ci, P, P]
+        L.orc_pack_int8.argtypes = [P, i64, i64, P, P]
+        L.orc_pack_km4.argtypes = [P, i64, i64, ci, P, P, P]
+        L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
+        L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
+        L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
+        L.orc_moe_ffn.argtypes = [P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
+        for f in ("orc_pack_fp4", "orc_pack_int4", "orc_pack_int8", "orc_pack_km4",
+                  "orc_dequant", "orc_matvec", "orc_moe_route", "orc_moe_ffn"):
+            getattr(L, f).restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_f32(W) -> np.ndarray:
+    """fp16 and fp32 weights both enter the packers as exact fp32 values."""
+    return np.ascontiguousarray(np.asarray(W).astype(np.float32))
+
+
+def _check_shape(W):
+    N, K = W.shape
+    if K % 32 != 0:
+        raise ValueError("K must be a multiple of 32")
+    return N, K
+
+
+# --- scalar fp16 helpers (written from the binary16 definition in oracle.c) ---
+
+def f16_to_f64(bits: int) -> float:
+    return lib().orc_f16_to_f64(int(bits) & 0xFFFF)
+
+
+def f64_to_f16(v: float) -> int:
+    return int(lib().orc_f64_to_f16(float(v)))
+
+
+# --- packers ---
+
+def pack_fp4(W):
+    W = _as_f32(W)
+    N, K = _check_shape(W)
+    codes = np.zeros((N, K // 2), np.uint8)
+    scale = np.zeros((N, K // 32), np.uint8)
+    lib().orc_pack_fp4(_p(W), N, K, _p(codes), _p(scale))
+    return codes, scale
+
+
+def pack_int4(W, clip_search: bool = True):
+    W = _as_f32(W)
+    N, K = _check_shape(W)
+    codes = np.zeros((N, K // 2), np.uint8)
+    scale = np.zeros((N, K // 32), np.uint16)
+    lib().orc_pack_int4(_p(W), N, K, 7 if clip_search else 1, _p(codes), _p(scale))
+    return codes, scale
+
+
+def pack_int8(W):
+    W = _as_f32(W)
+    N, K = _check_shape(W)
+    codes = np.zeros((N, K), np.int8)
+    scale = np.zeros((N, K // 32), np.uint16)
+    lib().orc_pack_int8(_p(W), N, K, _p(codes), _p(scale))
+    return codes, scale
+
+
+def pack_km4(W_f16, max_iter: int = 20, return_iters: bool = False):
+    W = np.ascontiguousarray(np.asarray(W_f16, dtype=np.float16)).view(np.uint16)
+    N, K = _check_shape(W)
+    codes = np.zeros((N, K // 2), np.uint8)
+    lut = np.zeros((N, 16), np.uint16)
+    iters = np.zeros((N,), np.int32)
+    lib().orc_pack_km4(_p(W), N, K, int(max_iter), _p(codes), _p(lut), _p(iters))
+    if return_iters:
+        return codes, lut, iters
+    return codes, lut
+
+
+def pack(fmt: str, W, **kw):
+    return {"int4": pack_int4, "fp4": pack_fp4, "int8": pack_int8, "km4": pack_km4}[fmt](W, **kw)
+
+
+# --- dequant and matvec ---
+
+def _kdim(fmt: str, codes: np.ndarray) -> int:
+    return codes.shape[1] if fmt == "int8" else codes.shape[1] * 2
+
+
+def dequant(fmt: str, codes, plane) -> np.ndarray:
+    codes = np.ascontiguousarray(codes)
+    plane = np.ascontiguousarray(plane)
+    N, K = codes.shape[0], _kdim(fmt, codes)
+    out = np.zeros((N, K), np.float64)
+    lib().orc_dequant(FORMATS[fmt], _p(codes), _p(plane), N, K, _p(out))
+    return out
+
+
+def matvec(fmt: str, codes, plane, x, rows=None) -> np.ndarray:
+    """y[b, i] = sum_k dequant(W)[row_i, k] * x[b, k], fp64 sequential sum.
+
+    x: [B, K] (any float dtype, converted exactly to fp64). rows: optional
+    index array; then y is [B, len(rows)].
+    """
+    codes = np.ascontiguousarray(codes)
+    plane = np.ascontiguousarray(plane)
+    N, K = codes.shape[0], _kdim(fmt, codes)
+    x = np.ascontiguousarray(np.atleast_2d(np.asarray(x)).astype(np.float64))
+    assert x.shape[1] == K
+    B = x.shape[0]
+    if rows is None:
+        M, rp, nr = N, None, 0
+    else:
+        rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        assert rows.min() >= 0 and rows.max() < N
+        M, rp, nr = len(rows), _p(rows), len(rows)
+    y = np.zeros((B, M), np.float64)
+    lib().orc_matvec(FORMATS[fmt], _p(codes), _p(plane), N, K, _p(x), B, rp, nr, _p(y))
+    return y
+
+
+# --- mixture of experts ---
+
+def moe_route(logits, topk: int):
+    logits = np.ascontiguousarray(np.asarray(logits, dtype=np.float32))
+    T, E = logits.shape
+    ids = np.zeros((T, topk), np.int32)
+    w = np.zeros((T, topk), np.float64)
+    lib().orc_moe_route(_p(logits), T, E, topk, _p(ids), _p(w))
+    return ids, w
+
+
+def moe_ffn(gu_codes, gu_scale, dn_codes, dn_scale, x, ids, weights, return_h: bool = False):
+    """gu_*: [E, 2I, H/2] / [E, 2I, H/32]; dn_*: [E, H, I/2] / [E, H, I/32]."""
+    gu_codes = np.ascontiguousarray(gu_codes)
+    gu_scale = np.ascontiguousarray(gu_scale)
+    dn_codes = np.ascontiguousarray(dn_codes)
+    dn_scale = np.ascontiguousarray(dn_scale)
+    E, I2, Hh = gu_codes.shape
+    I, H = I2 // 2, Hh * 2
+    assert dn_codes.shape == (E, H, I // 2)
+    x = np.ascontiguousarray(np.atleast_2d(np.asarray(x)).astype(np.float64))
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float64)
+    T, topk = ids.shape
+    assert ids.min() >= 0 and ids.max() < E
+    y = np.zeros((T, H), np.float64)
+    h = np.zeros((T, topk, I), np.float64)
+    lib().orc_moe_ffn(_p(gu_codes), _p(gu_scale), _p(dn_codes), _p(dn_scale), E, H, I,
+                      _p(x), T, topk, _p(ids), _p(weights), _p(h), _p(y))
+    return (y, h) if return_h else y

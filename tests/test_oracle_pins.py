@@ -1,0 +1,513 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected answer: a hand-worked block from the
+pages' definitions (tests/golden), a closed form, an invariant that
+characterises the result, a special case that reduces to a textbook or library
+routine (numpy), or brute force on tiny inputs.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _records(name):
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                yield [p.strip() for p in line.rstrip("\n").split(";")]
+
+
+def _f16(bits):
+    return np.array(bits, np.uint16).view(np.float16)
+
+
+# --------------------------------------------------------------------------
+# binary16 helpers against numpy's float16 conversion (library routine)
+# --------------------------------------------------------------------------
+
+def test_f16_round_trip_all_finite_codes():
+    bits = np.arange(0x10000, dtype=np.uint16)
+    vals = bits.view(np.float16)
+    finite = np.isfinite(vals)
+    for b, v in zip(bits[finite][::37], vals[finite][::37]):
+        assert oracle.f16_to_f64(int(b)) == float(v)
+        back = oracle.f64_to_f16(float(v))
+        assert back == int(b) or (float(v) == 0.0 and back == int(b))
+
+
+def test_f16_rounding_matches_numpy():
+    rng = np.random.default_rng(1)
+    mags = np.concatenate([
+        rng.uniform(0, 2 ** -14, 2000),            # subnormal range
+        np.exp(rng.uniform(-20, 11, 4000)),        # normal range
+        np.array([65504.0, 65519.99, 65520.0, 1e6, 2 ** -25, 3 * 2 ** -26, 2 ** -26]),
+    ])
+    # exact ties: midpoints between adjacent fp16 numbers
+    f = np.arange(0x0001, 0x7bff, 97, dtype=np.uint16).view(np.float16).astype(np.float64)
+    g = (np.arange(0x0001, 0x7bff, 97, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
+    vals = np.concatenate([mags, -mags, (f + g) / 2])
+    for v in vals:
+        want = int(np.array(v, np.float64).astype(np.float16).view(np.uint16))
+        assert oracle.f64_to_f16(float(v)) == want, v
+
+
+# --------------------------------------------------------------------------
+# FP4 E2M1 / e8m0
+# --------------------------------------------------------------------------
+
+def _e2m1_closed_form(code):
+    """Decode from the bit fields: sign, 2 exponent bits (bias 1), 1 mantissa bit."""
+    s = -1.0 if code & 8 else 1.0
+    e = (code >> 1) & 3
+    m = code & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+    return s * mag
+
+
+def test_e2m1_grid_closed_form():
+    # scale byte 127 is 2^0, so dequant returns the raw grid values
+    codes = np.array([[c | (c2 << 4) for c, c2 in zip(range(0, 16, 2), range(1, 16, 2))] + [0] * 8], np.uint8)
+    scale = np.array([[127]], np.uint8)
+    deq = oracle.dequant("fp4", codes, scale)[0, :16]
+    want = [_e2m1_closed_form(c) for c in range(16)]
+    assert list(deq) == want
+    assert sorted(set(abs(v) for v in want)) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_fp4_golden_blocks():
+    n = 0
+    for name, dt, nz, sbyte, bytes_hex, deq in _records("fp4_blocks.txt"):
+        if dt == "f16":
+            w = np.zeros(32, np.float16)
+            for item in filter(None, nz.split(",")):
+                i, h = item.split("=")
+                w[int(i)] = _f16(int(h, 16))
+        else:
+            w = np.zeros(32, np.float32)
+            for item in filter(None, nz.split(",")):
+                i, h = item.split("=")
+                w[int(i)] = np.array(int(h, 16), np.uint32).view(np.float32)
+        codes, scale = oracle.pack_fp4(w[None, :])
+        assert scale[0, 0] == int(sbyte, 16), name
+        want = bytes.fromhex(bytes_hex)
+        assert codes[0, :len(want)].tobytes() == want, name
+        d = oracle.dequant("fp4", codes, scale)[0]
+        idx = [int(it.split("=")[0]) for it in filter(None, nz.split(","))]
+        if deq:
+            assert [d[i] for i in idx] == [float(v) for v in deq.split(",")], name
+        n += 1
+    assert n == 8
+
+
+def _fp4_random_blocks(seed=3):
+    rng = np.random.default_rng(seed)
+    W = rng.standard_normal((64, 256)).astype(np.float32) * np.float32(0.02)
+    W[:, ::17] *= 40.0
+    W[3, :] = 0.0
+    W[5, 32:64] = np.float32(2 ** -130)              # subnormal fp32 block
+    W[6, 64:96] = rng.standard_normal(32).astype(np.float32) * np.float32(1e-38)
+    W[7, :32] *= np.float32(1e4)
+    return W
+
+
+def test_fp4_scale_invariant():
+    """E is the unique exponent with amax / 2^E in [4, 8) (clamped to e8m0)."""
+    W = _fp4_random_blocks()
+    codes, scale = oracle.pack_fp4(W)
+    blocks = W.reshape(W.shape[0], -1, 32)
+    amax = np.abs(blocks.astype(np.float64)).max(-1)
+    E = scale.astype(np.int64) - 127
+    for a, e in zip(amax.ravel(), E.ravel()):
+        if a == 0:
+            assert e == -127
+        elif math.ldexp(4.0, int(e)) <= a < math.ldexp(8.0, int(e)):
+            pass
+        else:
+            assert e == -127 and a < math.ldexp(4.0, -127)
+
+
+def test_fp4_codes_are_nearest_grid_points():
+    """Every dequantized value is a nearest point of the scaled grid to w;
+    on an exact tie it is the even-mantissa point; above 6 it saturates."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    W = _fp4_random_blocks()
+    codes, scale = oracle.pack_fp4(W)
+    D = oracle.dequant("fp4", codes, scale)
+    for n in range(W.shape[0]):
+        for k in range(W.shape[1]):
+            E = int(scale[n, k // 32]) - 127
+            v = math.ldexp(abs(float(W[n, k])), -E)
+            got = math.ldexp(abs(D[n, k]), -E)
+            dmin = min(abs(v - g) for g in grid)
+            assert abs(v - got) == dmin
+            ties = [i for i, g in enumerate(grid) if abs(v - g) == dmin]
+            if len(ties) == 2:
+                assert grid.index(got) % 2 == 0
+            byte = codes[n, k // 2]
+            c = byte & 15 if k % 2 == 0 else byte >> 4
+            assert bool(c & 8) == bool(np.signbit(W[n, k]))
+
+
+def test_fp4_tie_points():
+    # ties of the E2M1 grid at scale 2^0 (block amax 6 sets E = 0)
+    ties = {0.25: 0.0, 0.75: 1.0, 1.25: 1.0, 1.75: 2.0, 2.5: 2.0, 3.5: 4.0, 5.0: 4.0, 7.0: 6.0}
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 6.0
+    for i, v in enumerate(ties):
+        w[0, 1 + i] = v
+        w[0, 16 + i] = -v
+    codes, scale = oracle.pack_fp4(w)
+    assert scale[0, 0] == 127
+    d = oracle.dequant("fp4", codes, scale)[0]
+    for i, v in enumerate(ties):
+        assert d[1 + i] == ties[v] and d[16 + i] == -ties[v]
+
+
+# --------------------------------------------------------------------------
+# int4 / int8 symmetric blocks
+# --------------------------------------------------------------------------
+
+def _golden_int_blocks():
+    for name, fmt, clip, nz, s16, bytes_hex in _records("int_blocks.txt"):
+        w = np.zeros((1, 32), np.float32)
+        for item in nz.split(","):
+            i, h = item.split("=")
+            w[0, int(i)] = np.array(int(h, 16), np.uint32).view(np.float32)
+        yield name, fmt, clip == "1", w, int(s16, 16), bytes.fromhex(bytes_hex)
+
+
+def test_int_golden_blocks():
+    seen = 0
+    for name, fmt, clip, w, s16, want in _golden_int_blocks():
+        if fmt == "int4":
+            codes, scale = oracle.pack_int4(w, clip_search=clip)
+            got = codes[0, :len(want)].tobytes()
+        else:
+            codes, scale = oracle.pack_int8(w)
+            got = codes[0, :len(want)].view(np.uint8).tobytes()
+        assert scale[0, 0] == s16, name
+        assert got == want, name
+        seen += 1
+    assert seen == 3
+
+
+def _numpy_absmax(W, qmax):
+    """Textbook symmetric absmax quantization per block of 32 with numpy's
+    float32 operations and float16 cast (library routines)."""
+    B = W.reshape(W.shape[0], -1, 32).astype(np.float32)
+    amax = np.abs(B).max(-1, keepdims=True)
+    s = (amax / np.float32(qmax)).astype(np.float16)
+    sf = s.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(sf == 0, 0, np.clip(np.rint(B / sf), -qmax, qmax))
+    return q.astype(np.int64).reshape(W.shape), s[..., 0].view(np.uint16)
+
+
+def _unpack_nibbles(codes):
+    lo = (codes & 15).astype(np.int64)
+    hi = (codes >> 4).astype(np.int64)
+    return np.stack([lo, hi], -1).reshape(codes.shape[0], -1)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_int8_is_textbook_absmax(seed):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_t(3, (48, 256)) * 0.02).astype(np.float32)
+    W[2] = 0
+    W[4, :32] = np.float32(1e-9)
+    codes, scale = oracle.pack_int8(W)
+    q, s = _numpy_absmax(W, 127)
+    assert np.array_equal(scale, s)
+    assert np.array_equal(codes.astype(np.int64), q)
+    # the block's largest element always lands on +-127
+    B = W.reshape(48, -1, 32)
+    arg = np.abs(B).argmax(-1)
+    cb = codes.reshape(48, -1, 32)
+    for n in range(48):
+        for b in range(B.shape[1]):
+            if np.abs(B[n, b]).max() > 1e-6:
+                assert abs(int(cb[n, b, arg[n, b]])) == 127
+
+
+def test_int4_without_clip_search_is_textbook_absmax():
+    rng = np.random.default_rng(5)
+    W = (rng.standard_normal((40, 512)) * 0.02).astype(np.float32)
+    W[:, ::13] *= 20
+    W[7] = 0
+    codes, scale = oracle.pack_int4(W, clip_search=False)
+    q, s = _numpy_absmax(W, 7)
+    assert np.array_equal(scale, s)
+    assert np.array_equal(_unpack_nibbles(codes) - 8, q)
+
+
+def _block_sse64(w, s16, qmax):
+    s = float(_f16(s16))
+    if s == 0:
+        return float(np.sum(w.astype(np.float64) ** 2))
+    q = np.clip(np.rint(w.astype(np.float32) / np.float32(s)), -qmax, qmax)
+    return float(np.sum((w.astype(np.float64) - s * q) ** 2))
+
+
+def test_int4_clip_choice_is_the_error_minimum():
+    """Against an independent fp64 evaluation of the seven clip candidates:
+    the stored scale is one of them, its error is the minimum (within fp32
+    summation noise), and never above the plain absmax error."""
+    clips = [1.0, 0.95, 0.9, 0.85, 0.8, 0.75, 0.7]
+    rng = np.random.default_rng(11)
+    W = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    W[:, ::29] *= 20
+    codes, scale = oracle.pack_int4(W)
+    D = oracle.dequant("int4", codes, scale)
+    chosen_any_clip = 0
+    for n in range(W.shape[0]):
+        for b in range(W.shape[1] // 32):
+            w = W[n, 32 * b:32 * b + 32]
+            amax = np.float32(np.abs(w).max())
+            cands = [int(np.array(np.float32(np.float32(c) * amax) / np.float32(7)).astype(np.float16).view(np.uint16))
+                     for c in clips]
+            sse = [_block_sse64(w, s, 7) for s in cands]
+            got = int(scale[n, b])
+            assert got in cands
+            got_sse = float(np.sum((w.astype(np.float64) - D[n, 32 * b:32 * b + 32]) ** 2))
+            assert got_sse <= min(sse) * (1 + 1e-5) + 1e-30
+            assert got_sse <= sse[0] * (1 + 1e-6) + 1e-30
+            chosen_any_clip += got != cands[0]
+    assert chosen_any_clip > 0   # the search is not a no-op on such data
+
+
+def test_pack_layout_round_trip_all_bytes():
+    """Every byte value decodes to (low nibble, high nibble) as elements (2j, 2j+1)."""
+    codes = np.arange(256, dtype=np.uint8).reshape(16, 16)      # 16 rows, K = 32
+    one = np.full((16, 1), 0x3C00, np.uint16)                   # fp16 1.0
+    d = oracle.dequant("int4", codes, one)
+    for r in range(16):
+        for j in range(16):
+            b = 16 * r + j
+            assert d[r, 2 * j] == (b & 15) - 8 and d[r, 2 * j + 1] == (b >> 4) - 8
+    lut = np.tile(np.arange(16, dtype=np.float16).view(np.uint16), (16, 1))
+    d = oracle.dequant("km4", codes, lut)
+    for r in range(16):
+        for j in range(16):
+            b = 16 * r + j
+            assert d[r, 2 * j] == (b & 15) and d[r, 2 * j + 1] == (b >> 4)
+
+
+def test_weight_error_levels_are_sane():
+    """Soft check: per-32 block error levels on Gaussian weights sit near the
+    pages' reported relative errors (int8 ~0.0055, int4 MSE-clip ~0.095, fp4
+    ~0.117 on real weights; Gaussian int4 absmax is ~0.097)."""
+    rng = np.random.default_rng(2)
+    W = (rng.standard_normal((256, 1024)) * 0.02).astype(np.float32)
+
+    def rel(fmt, **kw):
+        c, s = oracle.pack(fmt, W, **kw)
+        D = oracle.dequant(fmt, c, s)
+        return np.linalg.norm(D - W) / np.linalg.norm(W)
+
+    assert 0.004 < rel("int8") < 0.007
+    assert 0.08 < rel("int4") < 0.10
+    assert rel("int4") < rel("int4", clip_search=False)
+    assert 0.09 < rel("fp4") < 0.13
+
+
+# --------------------------------------------------------------------------
+# km4 (k-means palettization)
+# --------------------------------------------------------------------------
+
+def test_km4_golden_rows():
+    n = 0
+    for name, pattern, lut_hex, bytes_hex in _records("km4_rows.txt"):
+        pat = [int(h, 16) for h in pattern.split(",")]
+        row = _f16(pat * 8)[None, :]
+        codes, lut = oracle.pack_km4(row)
+        assert [int(v) for v in lut[0]] == [int(h, 16) for h in lut_hex.split(",")], name
+        want = bytes.fromhex(bytes_hex)
+        assert codes[0, :len(want)].tobytes() == want, name
+        n += 1
+    assert n == 2
+
+
+def test_km4_few_distinct_values_are_exact():
+    rng = np.random.default_rng(4)
+    for d in (1, 2, 5, 16):
+        vals = rng.standard_normal(d).astype(np.float16)
+        row = rng.choice(vals, size=(3, 256)).astype(np.float16)
+        codes, lut = oracle.pack_km4(row)
+        D = oracle.dequant("km4", codes, lut)
+        assert np.array_equal(D, row.astype(np.float64))
+        assert np.all(np.diff(lut.view(np.float16).astype(np.float64), axis=1) >= 0)
+
+
+def _km4_check_invariants(W, codes, lut, iters, max_iter):
+    Lf = lut.view(np.float16).astype(np.float64)
+    idx = _unpack_nibbles(codes)
+    Wf = W.astype(np.float64)
+    assert np.all(np.diff(Lf, axis=1) >= 0), "table ascending"
+    for n in range(W.shape[0]):
+        dist = np.abs(Wf[n][:, None] - Lf[n][None, :])
+        best = dist.min(1)
+        # nearest entry, lowest index among equals
+        first = np.argmax(dist == best[:, None], axis=1)
+        assert np.array_equal(idx[n], first)
+        if iters[n] < max_iter:
+            # converged: every used entry is its members' mean rounded to fp16
+            for j in np.unique(idx[n]):
+                mem = W[n][idx[n] == j].astype(np.float64)
+                mean = sum(Fraction(float(v)) for v in mem) / len(mem)
+                c = Fraction(float(Lf[n, j]))
+                lo = Fraction(float(np.nextafter(np.float16(Lf[n, j]), np.float16(-np.inf))))
+                hi = Fraction(float(np.nextafter(np.float16(Lf[n, j]), np.float16(np.inf))))
+                assert abs(mean - c) <= abs(mean - lo) and abs(mean - c) <= abs(mean - hi)
+
+
+def test_km4_lloyd_invariants():
+    rng = np.random.default_rng(6)
+    W = (rng.standard_normal((12, 512)) * 0.02).astype(np.float16)
+    W[3, ::7] *= 30
+    codes, lut, iters = oracle.pack_km4(W, max_iter=200, return_iters=True)
+    assert np.all(iters < 200)
+    _km4_check_invariants(W, codes, lut, iters, 200)
+    # with the default 20 steps, the nearest-entry invariant still holds
+    codes, lut, iters = oracle.pack_km4(W, return_iters=True)
+    _km4_check_invariants(W, codes, lut, iters, 20)
+
+
+def test_km4_gaussian_reaches_lloyd_max_levels():
+    """A long Gaussian row converges to the 16-level Lloyd-Max quantizer of
+    N(0, 1) (Max, 1960: levels +-0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6181,
+    2.0690, 2.7326 sigma; normalised error 0.00950)."""
+    levels = np.array([0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6181, 2.0690, 2.7326])
+    want = np.concatenate([-levels[::-1], levels])
+    rng = np.random.default_rng(7)
+    row = rng.standard_normal((1, 32768)).astype(np.float16)
+    codes, lut, iters = oracle.pack_km4(row, max_iter=500, return_iters=True)
+    got = lut.view(np.float16).astype(np.float64)[0]
+    assert np.max(np.abs(got - want)) < 0.06
+    D = oracle.dequant("km4", codes, lut)
+    mse = np.mean((D - row.astype(np.float64)) ** 2) / np.var(row.astype(np.float64))
+    assert abs(mse - 0.0095) < 0.0006
+
+
+# --------------------------------------------------------------------------
+# matvec
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+def test_matvec_equals_dense_fp64_matmul(fmt):
+    rng = np.random.default_rng(8)
+    W = (rng.standard_normal((37, 96)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((3, 96)).astype(np.float16)
+    codes, plane = oracle.pack(fmt, W)
+    D = oracle.dequant(fmt, codes, plane)
+    y = oracle.matvec(fmt, codes, plane, x)
+    ref = x.astype(np.float64) @ D.T           # numpy fp64 GEMM (library routine)
+    assert np.allclose(y, ref, rtol=1e-13, atol=1e-15)
+    # unit vectors pick columns exactly
+    k = 41
+    e = np.zeros((1, 96), np.float16)
+    e[0, k] = 1
+    assert np.array_equal(oracle.matvec(fmt, codes, plane, e)[0], D[:, k])
+    # row subset agrees with the full result
+    rows = np.array([36, 0, 17])
+    assert np.array_equal(oracle.matvec(fmt, codes, plane, x, rows=rows), y[:, rows])
+
+
+def test_matvec_linearity():
+    rng = np.random.default_rng(9)
+    W = (rng.standard_normal((16, 64)) * 0.02).astype(np.float32)
+    codes, plane = oracle.pack_int4(W)
+    a = rng.standard_normal((1, 64))
+    b = rng.standard_normal((1, 64))
+    ya = oracle.matvec("int4", codes, plane, a)
+    yb = oracle.matvec("int4", codes, plane, b)
+    yab = oracle.matvec("int4", codes, plane, 2 * a - 3 * b)
+    assert np.allclose(yab, 2 * ya - 3 * yb, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# mixture of experts
+# --------------------------------------------------------------------------
+
+def test_moe_route_matches_numpy_sort_and_softmax():
+    rng = np.random.default_rng(10)
+    L = rng.standard_normal((8, 256)).astype(np.float32)
+    L[2, 10] = L[2, 200] = L[2].max() + 1          # equal logits: lower id first
+    ids, w = oracle.moe_route(L, 8)
+    for t in range(8):
+        order = np.argsort(-L[t].astype(np.float64), kind="stable")[:8]
+        assert np.array_equal(ids[t], order)
+        z = np.exp(L[t, order].astype(np.float64) - L[t, order].max())
+        assert np.allclose(w[t], z / z.sum(), rtol=1e-14)
+    assert ids[2, 0] == 10 and ids[2, 1] == 200
+
+
+def _small_moe(seed=12, E=6, H=64, I=32):
+    rng = np.random.default_rng(seed)
+    gu = (rng.standard_normal((E * 2 * I, H)) * 0.02).astype(np.float16)
+    dn = (rng.standard_normal((E * H, I)) * 0.02).astype(np.float16)
+    guc, gus = oracle.pack_int4(gu)
+    dnc, dns = oracle.pack_int4(dn)
+    return (guc.reshape(E, 2 * I, H // 2), gus.reshape(E, 2 * I, H // 32),
+            dnc.reshape(E, H, I // 2), dns.reshape(E, H, I // 32), rng)
+
+
+def test_moe_top1_reduces_to_one_expert_ffn():
+    guc, gus, dnc, dns, rng = _small_moe()
+    E, I2, Hh = guc.shape
+    H, I = 2 * Hh, I2 // 2
+    x = rng.standard_normal((1, H)).astype(np.float16)
+    e = 4
+    y = oracle.moe_ffn(guc, gus, dnc, dns, x, np.array([[e]]), np.array([[1.0]]))
+    Wg = oracle.dequant("int4", guc[e], gus[e])
+    Wd = oracle.dequant("int4", dnc[e], dns[e])
+    g = Wg @ x[0].astype(np.float64)                  # numpy GEMV
+    h = (g[:I] / (1 + np.exp(-g[:I])) * g[I:]).astype(np.float16).astype(np.float64)
+    ref = Wd @ h
+    assert np.allclose(y[0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_token_order_and_shared_experts():
+    guc, gus, dnc, dns, rng = _small_moe(seed=13)
+    H = 2 * guc.shape[2]
+    x = rng.standard_normal((4, H)).astype(np.float16)
+    L = rng.standard_normal((4, guc.shape[0])).astype(np.float32)
+    ids, w = oracle.moe_route(L, 3)
+    y = oracle.moe_ffn(guc, gus, dnc, dns, x, ids, w)
+    perm = np.array([2, 0, 3, 1])
+    yp = oracle.moe_ffn(guc, gus, dnc, dns, x[perm], ids[perm], w[perm])
+    assert np.array_equal(yp, y[perm])
+    # every token sending weight 1 to one shared expert: a batched single-expert FFN
+    ids1 = np.full((4, 1), 2, np.int32)
+    y1 = oracle.moe_ffn(guc, gus, dnc, dns, x, ids1, np.ones((4, 1)))
+    for t in range(4):
+        yt = oracle.moe_ffn(guc, gus, dnc, dns, x[t:t + 1], ids1[:1], np.ones((1, 1)))
+        assert np.array_equal(yt[0], y1[t])
+
+
+@pytest.mark.parametrize("pair,kept,other", [
+    ((1.0, 1.0 + 2 ** -10), 0x3C00, 0x3C01),                 # lower neighbour even
+    ((1.0 + 2 ** -10, 1.0 + 2 ** -9), 0x3C02, 0x3C01),       # upper neighbour even
+])
+def test_km4_mean_on_an_fp16_midpoint_rounds_to_even(pair, kept, other):
+    """Two members whose mean lies halfway between two fp16 numbers: the one
+    with the even significand is kept. Fifteen well-separated integer values
+    (each twice) occupy the other fifteen entries."""
+    ints = [v for v in range(-8, 8) if v != 1]
+    row = np.array(sorted(ints * 2 + list(pair)), np.float16)[None, :]
+    rng = np.random.default_rng(0)
+    row = row[:, rng.permutation(32)]
+    codes, lut, iters = oracle.pack_km4(row, return_iters=True)
+    L = [int(v) for v in lut[0]]
+    assert kept in L and other not in L
+    D = oracle.dequant("km4", codes, lut)[0]
+    kept_val = float(_f16(kept))
+    assert np.all(D[np.isin(row[0], np.array(pair, np.float16))] == kept_val)
+    for v in ints:
+        assert np.all(D[row[0] == v] == v)
