@@ -1,0 +1,262 @@
+"""Benchmark: effective weight GB/s and fraction of HBM peak of the 4-bit
+k-means-palettized (km4) lm_head matvec, 248320 x 2048, batch 1, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+
+A step is one call of the fused dequantize-matvec on the lm_head weights
+(the decode hot path; quantize-and-pack is export-time work and is timed once
+beside it). Inputs are seeded synthetic tensors of the lm_head's shape, packed
+on the GPU, resident in HBM before timing starts. Four copies of the packed
+weights (4 x 262 MB) are cycled so that no call finds its weights in the
+256 MB Infinity Cache. Time is taken with HIP events on the stream the kernel
+runs on, around exactly K calls after W warm-up calls.
+
+Prints one JSON line. `value` = algorithmic bytes per call (codes + tables,
+262,225,920 B) / mean time per call. `roofline` compares that to the 8 TB/s
+HBM peak; `traffic` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE counters
+recorded under profiles/ (null when no counter summary matches this kernel
+build). `cpu_baseline` times the plain CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+N_ROWS, K_DIM = 248320, 2048
+PEAK_GBS = 8000.0
+METRIC = "effective weight GB/s & % HBM peak for 4-bit lm_head matvec (248320×2048, B=1)"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def algo_bytes(fmt, N, K):
+    """Bytes a call must read from HBM: code plane plus scale/table plane."""
+    codes = N * K if fmt == "int8" else N * K // 2
+    plane = {"int4": N * (K // 32) * 2, "int8": N * (K // 32) * 2, "fp4": N * (K // 32), "km4": N * 16 * 2}[fmt]
+    return codes + plane
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--all", action="store_true", help="also time the int8 head and the MoE layer")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-metric", action="store_true", help="time the metric kernel only (for profiling)")
+    return ap.parse_args()
+
+
+def timed(fn, steps, warmup):
+    """Mean ms per call over `steps` calls, HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(steps):
+        fn(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def traffic_from_profiles(kernel_prefix):
+    """HBM bytes per launch recorded by the counter runs, if present."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        return d.get(kernel_prefix)
+    except Exception:
+        return None
+
+
+def cpu_baseline(c, x1):
+    """The oracle, untuned: pack a sample of rows, then time its matvec on them."""
+    import oracle
+    rows = 4096
+    codes, lut = oracle.pack_km4(c.W[:rows])
+    bytes_per_row = algo_bytes("km4", 1, K_DIM)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.matvec("km4", codes, lut, x1)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 5.0 or reps >= 200:
+            break
+    gbs = rows * bytes_per_row * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "km4 matvec over the first %d of 248320 lm_head rows (batch 1), %d repetitions, %.1f s"
+                      % (rows, reps, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU (torch.cuda.is_available() is False)", file=sys.stderr)
+        sys.exit(1)
+    import quantized_decode_matvec_amd as qmv
+    from quantized_decode_matvec_amd import workloads as wl
+
+    log("generating lm_head weights %dx%d" % (N_ROWS, K_DIM))
+    c = wl.lm_head_km4(batch=8)
+    W = torch.from_numpy(c.W).cuda()
+    x8 = torch.from_numpy(c.x).cuda()
+    x1 = x8[:1].contiguous()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    e0, e1 = ev(), ev()
+    e0.record()
+    codes, lut = qmv.qpack_km4(W)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    log("km4 pack %.1f ms" % pack_ms)
+    copies = [(codes, lut)] + [(codes.clone(), lut.clone()) for _ in range(args.copies - 1)]
+    y = torch.empty((8, N_ROWS), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        cc, ll = copies[i % len(copies)]
+        qmv.qmatvec_km4(cc, ll, x1, y=y[:1])
+
+    ms = timed(step, args.steps, args.warmup)
+    nbytes = algo_bytes("km4", N_ROWS, K_DIM)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("km4 B=1: %.2f us/call, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms * 1e3, gbs, gbs / PEAK_GBS * 100))
+
+    extras = {"km4_pack_ms": round(pack_ms, 3)}
+    if not args.only_metric:
+        # practical read ceiling over the same footprint
+        buf = torch.empty((len(copies), nbytes // 16 * 16), dtype=torch.uint8, device="cuda")
+        buf.random_(0, 255)
+        sink = torch.empty((int(qmv.lib().qmv_stream_read_sink_words(buf[0].numel())),), dtype=torch.int32,
+                           device="cuda")
+        ms_r = timed(lambda i: qmv.qmv_stream_read(buf[i % len(copies)], sink=sink), args.steps, args.warmup)
+        extras["stream_read_GBps"] = round(buf[0].numel() / (ms_r * 1e-3) / 1e9, 1)
+        del buf
+        log("stream read ceiling %.1f GB/s" % extras["stream_read_GBps"])
+
+        ms8 = timed(lambda i: qmv.qmatvec_km4(copies[i % len(copies)][0], copies[i % len(copies)][1], x8, y=y),
+                    args.steps // 2, args.warmup)
+        extras["km4_B8_us"] = round(ms8 * 1e3, 2)
+        extras["km4_B8_GBps"] = round(nbytes / (ms8 * 1e-3) / 1e9, 1)
+
+        for fmt in ("fp4", "int4"):
+            pk = [qmv.qpack(fmt, W)]
+            pk += [(a.clone(), b.clone()) for a, b in [pk[0]] * (len(copies) - 1)]
+            msf = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x1, y=y[:1]),
+                        args.steps, args.warmup)
+            nb = algo_bytes(fmt, N_ROWS, K_DIM)
+            extras["%s_B1_us" % fmt] = round(msf * 1e3, 2)
+            extras["%s_B1_GBps" % fmt] = round(nb / (msf * 1e-3) / 1e9, 1)
+            del pk
+        # fp16 dense GEMV on the same shape (torch), for the per-op ratio against fp16
+        wcp = [W] + [W.clone() for _ in range(1)]
+        msd = timed(lambda i: torch.matmul(x1, wcp[i % 2].t()), max(10, args.steps // 4), 5)
+        extras["fp16_dense_torch_us"] = round(msd * 1e3, 2)
+        extras["km4_speedup_vs_fp16_dense"] = round(msd / ms, 2)
+        del wcp
+        # attention projections of the pages' shapes (q: 2048 -> 4096, o: 4096 -> 2048)
+        for name, (n, k) in {"q_proj": (4096, 2048), "o_proj": (2048, 4096)}.items():
+            cc = wl.small_dense("km4", n, k, batch=1, seed=1)
+            Wq = torch.from_numpy(cc.W).cuda()
+            xq = torch.from_numpy(cc.x).cuda()
+            for fmt in ("km4", "fp4"):
+                p0 = qmv.qpack(fmt, Wq)
+                pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(127)]
+                msq = timed(lambda i: qmv.qmatvec(fmt, pk[i % 128][0], pk[i % 128][1], xq), args.steps, args.warmup)
+                extras["%s_%s_us" % (name, fmt)] = round(msq * 1e3, 2)
+                del pk
+        if args.all:
+            extras.update(bench_int8_head(args))
+            extras.update(bench_moe(args))
+
+    traffic = traffic_from_profiles("mv_fast_km4_b1")
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "lm_head km4 matvec 248320x2048, batch 1, fp16 x, fp32 accumulate",
+                   "N": N_ROWS, "K": K_DIM, "batch": 1, "format": "km4 (4-bit index + 16-entry fp16 table per row)",
+                   "algorithmic_bytes_per_call": nbytes, "weight_copies_cycled": len(copies)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
+        "extras": extras,
+    }
+    if not args.no_cpu and not args.only_metric:
+        log("cpu baseline (oracle)")
+        result["cpu_baseline"] = cpu_baseline(c, c.x[:1])
+    print(json.dumps(result), flush=True)
+
+
+def bench_int8_head(args):
+    import torch
+    import quantized_decode_matvec_amd as qmv
+    from quantized_decode_matvec_amd import workloads as wl
+    c = wl.int8_head()
+    W = torch.from_numpy(c.W).cuda()
+    x = torch.from_numpy(c.x).cuda()
+    p0 = qmv.qpack_int8(W)
+    del W
+    pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(2)]
+    ms = timed(lambda i: qmv.qmatvec_int8(pk[i % 3][0], pk[i % 3][1], x), args.steps, args.warmup)
+    nb = algo_bytes("int8", *c.W.shape)
+    return {"int8_head_us": round(ms * 1e3, 2), "int8_head_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+
+
+def bench_moe(args):
+    import torch
+    import quantized_decode_matvec_amd as qmv
+    from quantized_decode_matvec_amd import workloads as wl
+    c = wl.moe()
+    E, I2, H = c.W_gate_up.shape
+    I = I2 // 2
+    guc, gus = qmv.qpack_int4(torch.from_numpy(c.W_gate_up.reshape(E * I2, H)).cuda())
+    dnc, dns = qmv.qpack_int4(torch.from_numpy(c.W_down.reshape(E * H, I)).cuda())
+    guc, gus = guc.view(E, I2, H // 2), gus.view(E, I2, H // 32)
+    dnc, dns = dnc.view(E, H, I // 2), dns.view(E, H, I // 32)
+    out = {}
+    per_expert = algo_bytes("int4", I2, H) + algo_bytes("int4", H, I)
+    for T in (1, 4, 8):
+        x = torch.from_numpy(c.x[:T]).cuda()
+        lg = torch.from_numpy(c.logits[:T]).cuda()
+        ms = timed(lambda i: qmv.moe_ffn(guc, gus, dnc, dns, x, lg, c.topk), args.steps // 2, args.warmup)
+        ids, _ = qmv.qmoe_route(lg, c.topk)
+        uniq = len(np.unique(ids.cpu().numpy()))
+        out["moe_T%d_us" % T] = round(ms * 1e3, 2)
+        out["moe_T%d_GBps" % T] = round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)
+    return out
+
+
+if __name__ == "__main__":
+    main()

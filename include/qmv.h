@@ -1,0 +1,186 @@
+/*
+ * qmv.h - block-quantized decode matvec on AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels: quantize-and-pack fp16/fp32 weights
+ * into four block formats, and the fused dequantize-matvec y = dequant(Wq) x
+ * for decode batches of 1 to 8, plus the mixture-of-experts routed-expert
+ * gather used for expert FFNs.
+ *
+ * Sources (web pages of the "Core AI model zoo" knowledge base) cited below:
+ *  [S1] "Stream D - Quantization (FP4 + QAT-int4): feasibility, first result,
+ *       and plan", section 1 "Toolchain reality" and section 2 "The de-risk
+ *       experiment".
+ *  [S2] "Dense-path int4km coverage + flagship Qwen3.6-35B - session findings
+ *       & methods", sections 1 "The lever", 8 "FP4 (E2M1) dense matvec", 8b.
+ *  [S3] "coreai-optimization (coreai-opt) reference - quantization &
+ *       palettization", sections "Quantization", "Palettization",
+ *       "Pitfalls", "Theoretical size".
+ *  [S5] "Compression (palettization & quantization)", section "Per-channel
+ *       int8 on a big-vocab LM head: use per-block-32".
+ *
+ * Conventions shared by every entry point
+ *  - Layout. W is [N][K] row-major (N output rows, K inputs; the nn.Linear
+ *    out x in convention), blocks of 32 run along K [S1 sec. 1, S3
+ *    "Quantization"]. K must be a multiple of 32; a K that is not is refused
+ *    with QMV_E_SHAPE rather than skipped [S3 "Pitfalls"].
+ *    4-bit code planes are [N][K/2] bytes, element 2j in the low nibble of
+ *    byte j (the same bytes as eight codes per little-endian 32-bit word)
+ *    [S1 sec. 1, S2 sec. 8]. Scale and table planes are separate arrays.
+ *  - Memory. Every pointer argument is device memory owned by the caller.
+ *    The library never allocates, frees or synchronizes, and keeps no state
+ *    between calls other than a cached device-property query.
+ *  - Alignment. codes, W and x: 16 bytes. Planes, y, ids and weights: their
+ *    element size. A misaligned pointer returns QMV_E_ALIGN.
+ *  - Execution. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and runs asynchronously. Calls are thread-safe; on one
+ *    stream they run in order. Entry points taking a workspace may be
+ *    captured in a HIP graph.
+ *  - Errors. Arguments are validated before anything is enqueued; on any
+ *    error nothing is launched. A failure reported by the HIP runtime at
+ *    launch returns QMV_E_LAUNCH. Faults inside kernels surface on the
+ *    caller's next synchronization. Non-finite weights or logits and
+ *    out-of-range expert ids give unspecified results (not checked).
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_E_NULL = 1,      /* a required pointer is NULL */
+    QMV_E_SHAPE = 2,     /* a size is out of range (see each entry point) */
+    QMV_E_ALIGN = 3,     /* a pointer breaks the alignment rule above */
+    QMV_E_DTYPE = 4,     /* unknown dtype, format or epilogue value */
+    QMV_E_WORKSPACE = 5, /* workspace missing or smaller than required */
+    QMV_E_LAUNCH = 6     /* the HIP runtime refused or failed a launch */
+} qmv_status;
+
+typedef enum { QMV_F32 = 0, QMV_F16 = 1 } qmv_dtype;
+typedef enum { QMV_INT4 = 0, QMV_FP4 = 1, QMV_INT8 = 2, QMV_KM4 = 3 } qmv_format;
+typedef enum { QMV_EPI_NONE = 0, QMV_EPI_SWIGLU = 1, QMV_EPI_COMBINE = 2 } qmv_epilogue;
+
+/* Static string naming a status (never NULL). */
+const char *qmv_status_string(qmv_status s);
+
+/* ---------------------------------------------------------------------- */
+/* Quantize and pack. W: [N][K], wdt QMV_F16 or QMV_F32 (fp32 values must  */
+/* lie in the fp16 finite range for int4/int8). 1 <= N, K % 32 == 0.       */
+/* ---------------------------------------------------------------------- */
+
+/* Symmetric int4 per block of 32 with an MSE-chosen clip ratio and an fp16
+ * scale [S1 sec. 1 "Convert invocation" (the default 4-bit recipe), sec. 2
+ * (clip ratio per block chosen by squared error)]. For each clip c in
+ * 1.0, 0.95, ..., 0.7 (in that order): s = fp16(fp32(c*amax)/7), q =
+ * clamp(rint(w/s), -7, 7), err = sequential fmaf sum of (w - s*q)^2; the
+ * first strictly smallest err wins. Outputs: codes [N][K/2] of u = q + 8,
+ * scale [N][K/32] fp16 bits. Dequant: fp16(scale) * (u - 8). */
+qmv_status qpack_int4(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
+                      uint8_t *codes, uint16_t *scale, void *stream);
+
+/* FP4 E2M1 with an e8m0 scale per block of 32 [S1 sec. 1: E2M1 of the OCP MX
+ * family, scale 2^(floor(log2 amax) - 2), two codes per byte; S2 sec. 8].
+ * E = clamp(floor(log2 amax) - 2, -127, 127) (an all-zero block takes -127);
+ * the code is the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} to |w| * 2^-E (ties
+ * to the even mantissa, above 6 saturates) with the input's sign bit in bit
+ * 3. Outputs: codes [N][K/2]; scale [N][K/32] bytes E + 127. */
+qmv_status qpack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
+                     uint8_t *codes, uint8_t *scale, void *stream);
+
+/* Symmetric int8 per block of 32 with an fp16 scale, no clipping [S5]:
+ * s = fp16(amax/127), q = clamp(rint(w/s), -127, 127). Outputs: codes
+ * [N][K] int8, scale [N][K/32] fp16 bits. Dequant: fp16(scale) * q. */
+qmv_status qpack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
+                      int8_t *codes, uint16_t *scale, void *stream);
+
+/* 4-bit k-means palettization, one 16-entry fp16 table per output row
+ * [S2 secs. 1, 8, 8b (palettize_grouped, n_bits = 4); S3 "Palettization"
+ * (scalar k-means, per-channel grouping)]. W_f16: [N][K] fp16 bits,
+ * 32 <= K <= 8192. Exact integer arithmetic on w * 2^24: a row with at most
+ * 16 distinct values keeps them (ascending, padded with the largest);
+ * otherwise centroids start at the order statistics of rank (2j+1)K/32 and
+ * take at most max_iter (1..1000) Lloyd steps (nearest centroid, ties to the
+ * lower index; each non-empty centroid moves to its members' mean rounded
+ * to the nearest fp16, ties to even; stop when nothing moves); a final
+ * assignment gives the indices. Outputs: codes [N][K/2] of indices; lut
+ * [N][16] fp16 bits, ascending. */
+qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
+                     uint8_t *codes, uint16_t *lut, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Fused dequantize-matvec [S2 secs. 1 and 8: the fused 4-bit decode       */
+/* matvec; the same kernel structure for every format, only the dequant    */
+/* differs]. y[b][n] = sum_k dequant(W)[n][k] * x[b][k] with fp32          */
+/* accumulation. x: [B][K] (QMV_F16 or QMV_F32), y: [B][N] fp32            */
+/* (overwritten). 1 <= B <= 8, 1 <= N, K % 32 == 0, K <= 65536.            */
+/* ---------------------------------------------------------------------- */
+
+qmv_status qmatvec_int4(const uint8_t *codes, const uint16_t *scale, int64_t N, int64_t K,
+                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+qmv_status qmatvec_fp4(const uint8_t *codes, const uint8_t *scale, int64_t N, int64_t K,
+                       const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+qmv_status qmatvec_int8(const int8_t *codes, const uint16_t *scale, int64_t N, int64_t K,
+                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                       const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+
+/* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
+ * weight is exact in fp32) [S3 "Theoretical size" for the plane shapes]. */
+qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
+                    float *W_hat, void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Mixture of experts: routed-expert gather [S1 sec. 1 (gather_qmm over    */
+/* expert slabs blocked along K, [1,1,1,32]); S2 sec. 1 (only routed       */
+/* experts are kernelized)].                                              */
+/* ---------------------------------------------------------------------- */
+
+/* Top-k routing: logits [T][E] fp32 -> ids [T][topk] int32 (largest logit
+ * first, equal logits in increasing id order) and weights [T][topk] fp32,
+ * the softmax over the selected logits. 1 <= T <= 64, 1 <= topk <= min(E, 64),
+ * E <= 4096. */
+qmv_status qmoe_route(const float *logits, int T, int E, int topk,
+                      int32_t *ids, float *weights, void *stream);
+
+/* Bytes of workspace gather_qmatvec needs for these sizes (0 if none). */
+size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epilogue epi);
+
+/* Matvec against the experts chosen in ids, reading each chosen expert's
+ * weights once however many tokens chose it.
+ *  codes/plane: E stacked expert matrices [E][N][...] in `fmt`'s layout.
+ *  x: x_per_slot == 0: [T][K] (one input per token, shared by its slots);
+ *     x_per_slot == 1: [T][topk][K] (one input per token and slot).
+ *  ids [T][topk] int32 in [0, E); weights [T][topk] fp32 (COMBINE only).
+ *  epi == QMV_EPI_NONE:    y fp32 [T][topk][N].
+ *  epi == QMV_EPI_SWIGLU:  rows [0, N/2) are gate, [N/2, N) up; y fp16
+ *                          [T][topk][N/2] = fp16(silu(gate) * up); N even.
+ *  epi == QMV_EPI_COMBINE: y fp32 [T][N] = sum over slots of
+ *                          weights[t][slot] * (W[ids[t][slot]] x)[n].
+ * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096. The workspace must hold
+ * gather_qmatvec_workspace_bytes(...) bytes, 256-byte aligned. */
+qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane,
+                          int E, int64_t N, int64_t K,
+                          const void *x, qmv_dtype xdt, int x_per_slot,
+                          int T, int topk, const int32_t *ids, const float *weights,
+                          qmv_epilogue epi, void *y, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/* ---------------------------------------------------------------------- */
+/* Measurement aid: read `bytes` (a multiple of 16) from buf with 128-bit   */
+/* loads and write one checksum word per workgroup to sink[0..grid); the   */
+/* practical HBM read ceiling for the kernels above. sink must hold        */
+/* qmv_stream_read_sink_words(bytes) uint32 words.                          */
+/* ---------------------------------------------------------------------- */
+size_t qmv_stream_read_sink_words(size_t bytes);
+qmv_status qmv_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

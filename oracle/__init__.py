@@ -65,6 +65,8 @@ def lib():
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
         L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
         L.orc_moe_ffn.argtypes = [P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = ci
         for f in ("orc_pack_fp4", "orc_pack_int4", "orc_pack_int8", "orc_pack_km4",
                   "orc_dequant", "orc_matvec", "orc_moe_route", "orc_moe_ffn"):
             getattr(L, f).restype = None
@@ -87,6 +89,11 @@ def _check_shape(W):
     if K % 32 != 0:
         raise ValueError("K must be a multiple of 32")
     return N, K
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_num_threads())
 
 
 # --- scalar fp16 helpers (written from the binary16 definition in oracle.c) ---

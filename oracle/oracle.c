@@ -35,6 +35,7 @@
  * code that implements it.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -506,4 +507,10 @@ void orc_moe_ffn(const uint8_t *gu_codes, const uint16_t *gu_scale,
     free(h);
     free(g);
     free(part);
+}
+
+/* Threads the OpenMP loops above use (for reporting the CPU baseline). */
+int orc_num_threads(void)
+{
+    return omp_get_max_threads();
 }

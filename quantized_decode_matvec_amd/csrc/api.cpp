@@ -1,0 +1,200 @@
+// C ABI of the library: argument validation, then one or two kernel launches
+// on the caller's stream. Nothing here allocates, frees or synchronizes.
+// The contract of each entry point is documented in include/qmv.h.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "qmv.h"
+#include "qmv_launch.h"
+
+namespace qmv {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+}  // namespace qmv
+
+namespace {
+
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline qmv_status launch_status(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_E_LAUNCH; }
+
+qmv_status check_wk(const void *W, qmv_dtype wdt, int64_t N, int64_t K) {
+    if (!W) return QMV_E_NULL;
+    if (wdt != QMV_F16 && wdt != QMV_F32) return QMV_E_DTYPE;
+    if (N < 1 || K < 32 || K % 32 != 0) return QMV_E_SHAPE;
+    if (N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
+    if (!aligned(W, 16)) return QMV_E_ALIGN;
+    return QMV_OK;
+}
+
+qmv_status check_mv(const void *codes, const void *plane, size_t plane_align, int64_t N, int64_t K, const void *x,
+                    qmv_dtype xdt, int B, const float *y) {
+    if (!codes || !plane || !x || !y) return QMV_E_NULL;
+    if (xdt != QMV_F16 && xdt != QMV_F32) return QMV_E_DTYPE;
+    if (N < 1 || K < 32 || K % 32 != 0 || K > 65536 || B < 1 || B > 8) return QMV_E_SHAPE;
+    if (N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(x, 16) || !aligned(plane, plane_align) || !aligned(y, 4)) return QMV_E_ALIGN;
+    return QMV_OK;
+}
+
+size_t plane_alignment(qmv_format f) {
+    switch (f) {
+    case QMV_FP4: return 1;
+    case QMV_KM4: return 4;   // tables are read as 32-bit words
+    default: return 2;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmv_status_string(qmv_status s) {
+    switch (s) {
+    case QMV_OK: return "QMV_OK";
+    case QMV_E_NULL: return "QMV_E_NULL: a required pointer is NULL";
+    case QMV_E_SHAPE: return "QMV_E_SHAPE: a size is out of range";
+    case QMV_E_ALIGN: return "QMV_E_ALIGN: a pointer is misaligned";
+    case QMV_E_DTYPE: return "QMV_E_DTYPE: unknown dtype, format or epilogue";
+    case QMV_E_WORKSPACE: return "QMV_E_WORKSPACE: workspace missing or too small";
+    case QMV_E_LAUNCH: return "QMV_E_LAUNCH: the HIP runtime failed a launch";
+    }
+    return "unknown qmv_status";
+}
+
+qmv_status qpack_int4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint16_t *scale,
+                      void *stream) {
+    qmv_status s = check_wk(W, wdt, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !scale) return QMV_E_NULL;
+    if (!aligned(codes, 16) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_int4(W, wdt, N, K, codes, scale, as_stream(stream)));
+}
+
+qmv_status qpack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint8_t *scale,
+                     void *stream) {
+    qmv_status s = check_wk(W, wdt, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !scale) return QMV_E_NULL;
+    if (!aligned(codes, 16)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_fp4(W, wdt, N, K, codes, scale, as_stream(stream)));
+}
+
+qmv_status qpack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, int8_t *codes, uint16_t *scale,
+                      void *stream) {
+    qmv_status s = check_wk(W, wdt, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !scale) return QMV_E_NULL;
+    if (!aligned(codes, 16) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_int8(W, wdt, N, K, codes, scale, as_stream(stream)));
+}
+
+qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
+                     void *stream) {
+    qmv_status s = check_wk(W_f16, QMV_F16, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !lut) return QMV_E_NULL;
+    if (K > 4096 || max_iter < 1 || max_iter > 1000) return QMV_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(lut, 2)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_km4(W_f16, N, K, max_iter, codes, lut, as_stream(stream)));
+}
+
+qmv_status qmatvec_int4(const uint8_t *codes, const uint16_t *scale, int64_t N, int64_t K, const void *x,
+                        qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, scale, 2, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    return launch_status(qmv::launch_matvec(QMV_INT4, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
+qmv_status qmatvec_fp4(const uint8_t *codes, const uint8_t *scale, int64_t N, int64_t K, const void *x,
+                       qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, scale, 1, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    return launch_status(qmv::launch_matvec(QMV_FP4, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
+qmv_status qmatvec_int8(const int8_t *codes, const uint16_t *scale, int64_t N, int64_t K, const void *x,
+                        qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, scale, 2, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    return launch_status(qmv::launch_matvec(QMV_INT8, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
+qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const void *x,
+                       qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, lut, 4, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    return launch_status(qmv::launch_matvec(QMV_KM4, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
+qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *W_hat,
+                    void *stream) {
+    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (!codes || !plane || !W_hat) return QMV_E_NULL;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(W_hat, 16)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_dequant(fmt, codes, plane, N, K, W_hat, as_stream(stream)));
+}
+
+qmv_status qmoe_route(const float *logits, int T, int E, int topk, int32_t *ids, float *weights, void *stream) {
+    if (!logits || !ids || !weights) return QMV_E_NULL;
+    if (T < 1 || T > 64 || E < 1 || E > 4096 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
+    if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_moe_route(logits, T, E, topk, ids, weights, as_stream(stream)));
+}
+
+size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epilogue epi) {
+    if (T < 1 || topk < 1 || N < 1) return 0;
+    return qmv::gather_workspace_bytes(T, topk, E, N, epi);
+}
+
+qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, int E, int64_t N, int64_t K,
+                          const void *x, qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids,
+                          const float *weights, qmv_epilogue epi, void *y, void *workspace, size_t ws_bytes,
+                          void *stream) {
+    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (epi != QMV_EPI_NONE && epi != QMV_EPI_SWIGLU && epi != QMV_EPI_COMBINE) return QMV_E_DTYPE;
+    if (xdt != QMV_F16) return QMV_E_DTYPE;
+    if (!codes || !plane || !x || !ids || !y) return QMV_E_NULL;
+    if (epi == QMV_EPI_COMBINE && !weights) return QMV_E_NULL;
+    if (E < 1 || E > 4096 || N < 1 || K < 32 || K % 32 != 0 || K > 8192) return QMV_E_SHAPE;
+    if (T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
+    if (x_per_slot != 0 && x_per_slot != 1) return QMV_E_SHAPE;
+    if (epi == QMV_EPI_SWIGLU && N % 2 != 0) return QMV_E_SHAPE;
+    if (N > (int64_t(1) << 40) / K / E) return QMV_E_SHAPE;
+    size_t need = qmv::gather_workspace_bytes(T, topk, E, N, epi);
+    if (need > 0 && (!workspace || ws_bytes < need)) return QMV_E_WORKSPACE;
+    if (need > 0 && !aligned(workspace, 256)) return QMV_E_ALIGN;
+    if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(ids, 4) ||
+        !aligned(y, epi == QMV_EPI_SWIGLU ? 2 : 4) || (weights && !aligned(weights, 4)))
+        return QMV_E_ALIGN;
+    return launch_status(qmv::launch_gather(fmt, codes, plane, E, N, K, x, xdt, x_per_slot, T, topk, ids, weights,
+                                            epi, y, workspace, as_stream(stream)));
+}
+
+size_t qmv_stream_read_sink_words(size_t bytes) { return qmv::stream_read_grid(bytes); }
+
+qmv_status qmv_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink) return QMV_E_NULL;
+    if (bytes == 0 || bytes % 16 != 0) return QMV_E_SHAPE;
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_stream_read(buf, bytes, sink, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,371 @@
+// Fused dequantize-matvec y[b][n] = sum_k dequant(W)[n][k] * x[b][k]
+// ("Dense-path int4km coverage + flagship Qwen3.6-35B - session findings &
+// methods", sections 1 and 8: one fused decode matvec whose structure is the
+// same for every 4-bit format, only the dequant differs).
+//
+// gfx950 design. The op reads each packed weight byte once and is bound by
+// HBM bandwidth at small batch. A wavefront owns whole rows: lane l of a row
+// group loads 16-byte chunks l, l + LPR, ... of the row's code plane, so one
+// wave-wide load instruction covers 64 x 16 B of contiguous bytes. The x
+// slices that belong to the lane's chunks are loaded into registers once and
+// reused for every row the wave visits. Decoding happens in registers (or
+// from a 32-byte per-row table in LDS for km4), products accumulate in fp32
+// via v_dot2_f32_f16 and the block scale multiplies the block sum. Row
+// groups are reduced across their lanes with cross-lane shuffles.
+#include "qmv_device.h"
+#include "qmv_launch.h"
+
+namespace qmv {
+
+// ---------------------------------------------------------------------------
+// Fast path: x fp16 in registers.
+//   FMT  format, BT batch width compiled (runtime B <= BT, extra rows zero),
+//   LPR  lanes per row (64, 32 or 16), CPL chunks per lane, R row groups per
+//   wave iteration.
+// ---------------------------------------------------------------------------
+template <int FMT, int BT, int LPR, int CPL, int R>
+__global__ __launch_bounds__(256) void mv_fast(const uint8_t *__restrict__ codes,
+                                               const void *__restrict__ plane, int64_t N, int K,
+                                               const _Float16 *__restrict__ x, int B,
+                                               float *__restrict__ y) {
+    constexpr int RPW = kWave / LPR;            // rows per row group
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    constexpr int ROWS_IT = R * RPW;            // rows per wave iteration
+    __shared__ _Float16 lut_lds[(FMT == KM4) ? 4 * ROWS_IT * 16 : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane % LPR;
+    const int rsub = lane / LPR;
+    const int cpr = (FMT == INT8) ? K / 16 : K / 32;   // chunks per row
+    const int nb = K / 32;                              // blocks per row
+    const int64_t row_bytes = (FMT == INT8) ? K : K / 2;
+
+    // x slices for this lane's chunks, every batch row
+    uint32_t xr[CPL][BT][XW];
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+        int c = sub + LPR * j;
+#pragma unroll
+        for (int b = 0; b < BT; b++) load_x_slice<FMT>(x + (size_t)b * K, c, c < cpr && b < B, xr[j][b]);
+    }
+
+    const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+    _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
+
+    for (int64_t row0 = gw * ROWS_IT; row0 < N; row0 += waves_total * ROWS_IT) {
+        uint4 cw[R][CPL];
+        float sc[R][CPL];
+        // issue all loads of the iteration first
+#pragma unroll
+        for (int g = 0; g < R; g++) {
+            int64_t row = row0 + g * RPW + rsub;
+            bool rv = row < N;
+            const uint8_t *rp = codes + (rv ? row : 0) * row_bytes;
+#pragma unroll
+            for (int j = 0; j < CPL; j++) {
+                int c = sub + LPR * j;
+                bool v = rv && c < cpr;
+                cw[g][j] = v ? *reinterpret_cast<const uint4 *>(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+                if constexpr (FMT == INT4 || FMT == INT8) {
+                    const uint16_t *s = reinterpret_cast<const uint16_t *>(plane);
+                    int blk = (FMT == INT8) ? c / 2 : c;
+                    sc[g][j] = v ? f16_bits_to_f32(s[(rv ? row : 0) * nb + blk]) : 0.f;
+                } else if constexpr (FMT == FP4) {
+                    const uint8_t *s = reinterpret_cast<const uint8_t *>(plane);
+                    sc[g][j] = v ? e8m0_to_f32(s[(rv ? row : 0) * nb + c]) : 0.f;
+                } else {
+                    sc[g][j] = 1.f;
+                }
+            }
+        }
+        if constexpr (FMT == KM4) {
+            // stage the tables of this iteration's rows: 8 dwords per row
+            const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane);
+            uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
+            for (int i = lane; i < ROWS_IT * 8; i += kWave) {
+                int64_t row = row0 + i / 8;
+                ldst[i] = row < N ? lsrc[row * 8 + (i % 8)] : 0u;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        float acc[R][BT];
+#pragma unroll
+        for (int g = 0; g < R; g++)
+#pragma unroll
+            for (int b = 0; b < BT; b++) acc[g][b] = 0.f;
+#pragma unroll
+        for (int g = 0; g < R; g++) {
+#pragma unroll
+            for (int j = 0; j < CPL; j++) {
+#pragma unroll
+                for (int b = 0; b < BT; b++) {
+                    float d;
+                    if constexpr (FMT == INT4) d = chunk_dot_int4(cw[g][j], xr[j][b]);
+                    else if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[g][j], xr[j][b]);
+                    else if constexpr (FMT == INT8) d = chunk_dot_int8(cw[g][j], xr[j][b]);
+                    else d = chunk_dot_km4(cw[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
+                    acc[g][b] = __builtin_fmaf(d, sc[g][j], acc[g][b]);
+                }
+            }
+        }
+        if constexpr (FMT == KM4) {
+            // the next iteration rewrites the tables: keep the reads above it
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+#pragma unroll
+        for (int g = 0; g < R; g++) {
+            int64_t row = row0 + g * RPW + rsub;
+#pragma unroll
+            for (int b = 0; b < BT; b++) {
+                float s = group_sum<LPR>(acc[g][b]);
+                if (sub == 0 && row < N && b < B) y[(size_t)b * N + row] = s;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Generic path: any K % 32 == 0, B <= 8, x fp16 or fp32. One wave per row,
+// decode to fp32 and fma against x read through the cache.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__device__ __forceinline__ void decode_chunk_f32(const uint8_t *__restrict__ codes, const void *__restrict__ plane,
+                                                 int64_t row, int K, int c, float (&w)[32]) {
+    const int nb = K / 32;
+    if constexpr (FMT == INT8) {
+        const int8_t *p = reinterpret_cast<const int8_t *>(codes) + row * (int64_t)K + (int64_t)c * 16;
+        float s = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(plane)[row * nb + c / 2]);
+#pragma unroll
+        for (int i = 0; i < 16; i++) w[i] = s * (float)p[i];
+    } else {
+        uint4 cw = *reinterpret_cast<const uint4 *>(codes + row * (int64_t)(K / 2) + (int64_t)c * 16);
+        uint32_t wd[4] = {cw.x, cw.y, cw.z, cw.w};
+        if constexpr (FMT == FP4) {
+            float s = e8m0_to_f32(reinterpret_cast<const uint8_t *>(plane)[row * nb + c]);
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                h2 v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 0),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 1),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 2),
+                           __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd[d], 1.0f, 3)};
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    w[8 * d + 2 * i] = (float)v[i].x * s;
+                    w[8 * d + 2 * i + 1] = (float)v[i].y * s;
+                }
+            }
+        } else if constexpr (FMT == INT4) {
+            float s = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(plane)[row * nb + c]);
+#pragma unroll
+            for (int d = 0; d < 4; d++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) w[8 * d + i] = s * (float)((int)((wd[d] >> (4 * i)) & 15u) - 8);
+        } else {
+            const uint16_t *lut = reinterpret_cast<const uint16_t *>(plane) + row * 16;
+#pragma unroll
+            for (int d = 0; d < 4; d++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) w[8 * d + i] = f16_bits_to_f32(lut[(wd[d] >> (4 * i)) & 15u]);
+        }
+    }
+}
+
+template <typename XT>
+__device__ __forceinline__ float load_x(const XT *p) { return (float)*p; }
+
+template <int FMT, typename XT>
+__global__ __launch_bounds__(256) void mv_generic(const uint8_t *__restrict__ codes,
+                                                  const void *__restrict__ plane, int64_t N, int K,
+                                                  const XT *__restrict__ x, int B, float *__restrict__ y) {
+    constexpr int E = ChunkTraits<FMT>::kElems;
+    const int lane = threadIdx.x & 63;
+    const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int cpr = K / E;
+    for (int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); row < N; row += waves_total) {
+        float acc[8];
+#pragma unroll
+        for (int b = 0; b < 8; b++) acc[b] = 0.f;
+        for (int c = lane; c < cpr; c += kWave) {
+            float w[32];
+            decode_chunk_f32<FMT>(codes, plane, row, K, c, w);
+#pragma unroll
+            for (int b = 0; b < 8; b++) {
+                if (b < B) {
+                    const XT *xp = x + (size_t)b * K + (size_t)c * E;
+#pragma unroll
+                    for (int i = 0; i < E; i++) acc[b] = __builtin_fmaf(w[i], load_x(xp + i), acc[b]);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 8; b++) {
+            if (b < B) {
+                float s = group_sum<64>(acc[b]);
+                if (lane == 0) y[(size_t)b * N + row] = s;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dequant (test support): one thread per 32-element block.
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes, const void *__restrict__ plane,
+                                                      int64_t N, int K, float *__restrict__ out) {
+    const int nb = K / 32;
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= N * nb) return;
+    int64_t row = gid / nb;
+    int blk = (int)(gid % nb);
+    float w[32];
+    if constexpr (FMT == INT8) {
+        decode_chunk_f32<FMT>(codes, plane, row, K, 2 * blk, w);
+        float w2[32];
+        decode_chunk_f32<FMT>(codes, plane, row, K, 2 * blk + 1, w2);
+#pragma unroll
+        for (int i = 0; i < 16; i++) w[16 + i] = w2[i];
+    } else {
+        decode_chunk_f32<FMT>(codes, plane, row, K, blk, w);
+    }
+    float4 *o = reinterpret_cast<float4 *>(out + row * (int64_t)K + (int64_t)blk * 32);
+#pragma unroll
+    for (int i = 0; i < 8; i++) o[i] = make_float4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch (called from the C ABI after validation).
+// ---------------------------------------------------------------------------
+static int grid_for_waves(int64_t waves_needed) {
+    int64_t cap = (int64_t)device_cu_count() * 32;   // 8 WGs x 4 waves per CU
+    int64_t waves = waves_needed < cap ? waves_needed : cap;
+    if (waves < 1) waves = 1;
+    return (int)((waves + 3) / 4);
+}
+
+template <int FMT, int BT, int LPR, int CPL>
+static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                              float *y, hipStream_t st) {
+    constexpr int R = (BT <= 2) ? 4 : (BT <= 4 ? 2 : 1);
+    constexpr int ROWS_IT = R * (kWave / LPR);
+    int grid = grid_for_waves((N + ROWS_IT - 1) / ROWS_IT);
+    hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, R>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
+                       reinterpret_cast<const _Float16 *>(x), B, y);
+    return hipGetLastError();
+}
+
+template <int FMT, int LPR, int CPL>
+static hipError_t dispatch_b(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                             float *y, hipStream_t st, bool *handled) {
+    *handled = true;
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    // register budget for x: CPL * BT * XW words
+    if (B == 1) return launch_fast<FMT, 1, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+    if (B == 2) return launch_fast<FMT, 2, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+    if constexpr (CPL * 4 * XW <= 128) {
+        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+    }
+    if constexpr (CPL * 8 * XW <= 128) {
+        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+    }
+    *handled = false;
+    return hipSuccess;
+}
+
+template <int FMT>
+static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x,
+                             qmv_dtype xdt, int B, float *y, hipStream_t st) {
+    constexpr int E = ChunkTraits<FMT>::kElems;
+    const int cpr = K / E;
+    bool handled = false;
+    hipError_t err = hipSuccess;
+    if (xdt == QMV_F16) {
+        if (cpr <= 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, y, st, &handled);
+        else if (cpr <= 32) err = dispatch_b<FMT, 32, 1>(codes, plane, N, K, x, B, y, st, &handled);
+        else if (cpr <= 64) err = dispatch_b<FMT, 64, 1>(codes, plane, N, K, x, B, y, st, &handled);
+        else if (cpr <= 128) err = dispatch_b<FMT, 64, 2>(codes, plane, N, K, x, B, y, st, &handled);
+        else if (cpr <= 192) err = dispatch_b<FMT, 64, 3>(codes, plane, N, K, x, B, y, st, &handled);
+        else if (cpr <= 256) err = dispatch_b<FMT, 64, 4>(codes, plane, N, K, x, B, y, st, &handled);
+        if (handled) return err;
+    }
+    int grid = grid_for_waves(N);
+    if (xdt == QMV_F16)
+        hipLaunchKernelGGL((mv_generic<FMT, _Float16>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
+                           reinterpret_cast<const _Float16 *>(x), B, y);
+    else
+        hipLaunchKernelGGL((mv_generic<FMT, float>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
+                           reinterpret_cast<const float *>(x), B, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                         qmv_dtype xdt, int B, float *y, hipStream_t st) {
+    const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
+    switch (fmt) {
+    case INT4: return matvec_fmt<INT4>(c, plane, N, (int)K, x, xdt, B, y, st);
+    case FP4: return matvec_fmt<FP4>(c, plane, N, (int)K, x, xdt, B, y, st);
+    case INT8: return matvec_fmt<INT8>(c, plane, N, (int)K, x, xdt, B, y, st);
+    default: return matvec_fmt<KM4>(c, plane, N, (int)K, x, xdt, B, y, st);
+    }
+}
+
+hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *out,
+                          hipStream_t st) {
+    const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
+    int64_t blocks = N * (K / 32);
+    int grid = (int)((blocks + 255) / 256);
+    switch (fmt) {
+    case INT4: hipLaunchKernelGGL(dequant_kernel<INT4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
+    case FP4: hipLaunchKernelGGL(dequant_kernel<FP4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
+    case INT8: hipLaunchKernelGGL(dequant_kernel<INT8>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
+    default: hipLaunchKernelGGL(dequant_kernel<KM4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Streaming-read ceiling: every lane reads 16-byte words, a grid-stride loop
+// with four loads in flight per lane; one xor checksum per workgroup.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p, int64_t n16,
+                                                          uint32_t *__restrict__ sink) {
+    uint32_t acc = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        uint4 a = p[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int k = 0; k < 256; k++) t ^= red[k];
+        sink[blockIdx.x] = t;
+    }
+}
+
+size_t stream_read_grid(size_t bytes) {
+    (void)bytes;
+    return (size_t)device_cu_count() * 8;
+}
+
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
+    int grid = (int)stream_read_grid(bytes);
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const uint4 *>(buf),
+                       (int64_t)(bytes / 16), sink);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

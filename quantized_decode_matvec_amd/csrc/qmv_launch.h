@@ -1,0 +1,39 @@
+// Internal host-side interface between the C ABI (api.cpp) and the kernel
+// translation units. Every launcher enqueues on `st` and returns the HIP
+// runtime's launch status; arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "qmv.h"
+
+namespace qmv {
+
+int device_cu_count();   // compute units of the current device (cached per device)
+
+hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                         qmv_dtype xdt, int B, float *y, hipStream_t st);
+hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *out,
+                          hipStream_t st);
+size_t stream_read_grid(size_t bytes);
+hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st);
+
+hipError_t launch_pack_int4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint16_t *scale,
+                            hipStream_t st);
+hipError_t launch_pack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, int8_t *codes, uint16_t *scale,
+                            hipStream_t st);
+hipError_t launch_pack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint8_t *scale,
+                           hipStream_t st);
+hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
+                           hipStream_t st);
+
+hipError_t launch_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, float *weights,
+                            hipStream_t st);
+size_t gather_workspace_bytes(int T, int topk, int E, int64_t N, int epi);
+hipError_t launch_gather(int fmt, const void *codes, const void *plane, int E, int64_t N, int64_t K, const void *x,
+                         qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids, const float *weights,
+                         int epi, void *y, void *workspace, hipStream_t st);
+
+}  // namespace qmv

@@ -1,0 +1,93 @@
+"""The C ABI library loads, exports every symbol include/qmv.h declares, and
+refuses invalid arguments before anything is launched (no GPU needed: every
+call below fails validation, so no device memory is touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_decode_matvec_amd as qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qmv.LIB_PATH):
+        import quantized_decode_matvec_amd.build as b
+        b.build()
+    return qmv.lib()
+
+
+def test_header_declares_exactly_the_exports():
+    assert _declared() == sorted(qmv.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert L.qmv_status_string(s).decode().startswith("QMV_")
+    assert L.qmv_status_string(99) == b"unknown qmv_status"
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced
+ODD = ctypes.c_void_p(0x10001)        # misaligned
+NUL = ctypes.c_void_p(0)
+S = ctypes.c_void_p(0)
+
+
+def test_pack_validation(L):
+    assert L.qpack_int4(NUL, 1, 4, 64, FAKE, FAKE, S) == E_NULL
+    assert L.qpack_int4(FAKE, 1, 4, 48, FAKE, FAKE, S) == E_SHAPE      # K % 32
+    assert L.qpack_int4(FAKE, 1, 0, 64, FAKE, FAKE, S) == E_SHAPE      # N < 1
+    assert L.qpack_int4(FAKE, 7, 4, 64, FAKE, FAKE, S) == E_DTYPE
+    assert L.qpack_int4(ODD, 1, 4, 64, FAKE, FAKE, S) == E_ALIGN
+    assert L.qpack_fp4(FAKE, 1, 4, 64, NUL, FAKE, S) == E_NULL
+    assert L.qpack_int8(FAKE, 0, 4, 64, ODD, FAKE, S) == E_ALIGN
+    assert L.qpack_km4(FAKE, 4, 8192, 20, FAKE, FAKE, S) == E_SHAPE    # K too large for the row sort
+    assert L.qpack_km4(FAKE, 4, 64, 0, FAKE, FAKE, S) == E_SHAPE       # max_iter < 1
+
+
+@pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4"])
+def test_matvec_validation(L, name):
+    f = getattr(L, name)
+    assert f(NUL, FAKE, 8, 64, FAKE, 1, 1, FAKE, S) == E_NULL
+    assert f(FAKE, FAKE, 8, 64, FAKE, 1, 0, FAKE, S) == E_SHAPE        # B = 0
+    assert f(FAKE, FAKE, 8, 64, FAKE, 1, 9, FAKE, S) == E_SHAPE        # B = 9
+    assert f(FAKE, FAKE, 8, 80, FAKE, 1, 1, FAKE, S) == E_SHAPE        # K % 32
+    assert f(FAKE, FAKE, 8, 64, FAKE, 5, 1, FAKE, S) == E_DTYPE
+    assert f(ODD, FAKE, 8, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
+    assert f(FAKE, FAKE, 8, 64, ODD, 1, 1, FAKE, S) == E_ALIGN
+
+
+def test_dequant_and_moe_validation(L):
+    assert L.qdequant(9, FAKE, FAKE, 4, 64, FAKE, S) == E_DTYPE
+    assert L.qdequant(0, FAKE, FAKE, 4, 33, FAKE, S) == E_SHAPE
+    assert L.qmoe_route(FAKE, 2, 256, 0, FAKE, FAKE, S) == E_SHAPE
+    assert L.qmoe_route(FAKE, 2, 4, 8, FAKE, FAKE, S) == E_SHAPE       # topk > E
+    assert L.qmoe_route(NUL, 2, 256, 8, FAKE, FAKE, S) == E_NULL
+    # gather: T > 8, missing workspace, bad epilogue, fp32 x
+    g = L.gather_qmatvec
+    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 9, 8, FAKE, FAKE, 2, FAKE, NUL, 0, S) == E_SHAPE
+    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 4, 8, FAKE, FAKE, 2, FAKE, NUL, 0, S) == E_WORKSPACE
+    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 4, 8, FAKE, FAKE, 7, FAKE, NUL, 0, S) == E_DTYPE
+    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 0, 1, 4, 8, FAKE, FAKE, 0, FAKE, NUL, 0, S) == E_DTYPE
+    assert g(0, FAKE, FAKE, 256, 1023, 512, FAKE, 1, 0, 4, 8, FAKE, FAKE, 1, FAKE, NUL, 0, S) == E_SHAPE  # odd N
+    assert L.gather_qmatvec_workspace_bytes(4, 8, 256, 2048, 2) == 4 * 8 * 2048 * 4
+    assert L.gather_qmatvec_workspace_bytes(4, 8, 256, 2048, 1) == 0
+    assert L.qmv_stream_read(FAKE, 24, FAKE, S) == E_SHAPE

@@ -1,0 +1,159 @@
+"""GPU parity at the five full workload sizes, in the launch configuration the
+benchmark times (the same entry points on the same shapes):
+
+  tiny int4   256 x 512 fp32, x fp32 [1, 512]
+  fp4         4096 x 4096 fp16, x fp16 batch 1 and 4
+  km4 lm_head 248320 x 2048 fp16, x fp16 batch 1 and 8
+  int8 head   130560 x 2560 fp16 with heavy-tailed rows, x fp16 batch 1
+  MoE         256 experts (gate/up 2 x 512 x 2048, down 2048 x 512, int4),
+              top-8 routing, 1..8 tokens
+
+Where the oracle cannot do the whole tensor in seconds (k-means over 248320
+rows, the 256-expert slabs) it checks sampled rows / the routed experts one by
+one; everything else is compared in full."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_decode_matvec_amd as qmv
+from quantized_decode_matvec_amd import workloads as wl
+from tests.gpu_helpers import RTOL, dev, host, rel_err, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_int4_full():
+    c = wl.tiny_int4()
+    codes, scale = oracle.pack_int4(c.W)
+    gc, gs = qmv.qpack_int4(dev(c.W))
+    assert np.array_equal(codes, host(gc)) and np.array_equal(scale, host(gs))
+    y = host(qmv.qmatvec_int4(gc, gs, dev(c.x)))
+    assert rel_err(y, oracle.matvec("int4", codes, scale, c.x)) <= RTOL
+
+
+def test_fp4_4096_full():
+    c = wl.fp4_square()
+    codes, scale = oracle.pack_fp4(c.W)
+    gc, gs = qmv.qpack_fp4(dev(c.W))
+    assert np.array_equal(codes, host(gc)) and np.array_equal(scale, host(gs))
+    for B in (1, 4):
+        y = host(qmv.qmatvec_fp4(gc, gs, dev(c.x[:B])))
+        assert rel_err(y, oracle.matvec("fp4", codes, scale, c.x[:B])) <= RTOL
+
+
+@pytest.fixture(scope="module")
+def lm_head():
+    c = wl.lm_head_km4()
+    W = dev(c.W)
+    codes, lut = qmv.qpack_km4(W)
+    return c, codes, lut
+
+
+def test_km4_lm_head_pack_sampled_rows(lm_head):
+    c, codes, lut = lm_head
+    rows = sample_rows(c.W.shape[0], 256)
+    oc, ol = oracle.pack_km4(c.W[rows])
+    assert np.array_equal(oc, host(codes[rows]))
+    assert np.array_equal(ol, host(lut[rows]))
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_km4_lm_head_matvec_sampled_rows(lm_head, B):
+    c, codes, lut = lm_head
+    x = c.x[:B]
+    y = host(qmv.qmatvec_km4(codes, lut, dev(x)))
+    rows = sample_rows(c.W.shape[0], 512, seed=B)
+    oc, ol = oracle.pack_km4(c.W[rows])
+    want = oracle.matvec("km4", oc, ol, x)
+    # normalise by the full output's scale: rel err against max |y| over all rows
+    got = y[:, rows].astype(np.float64)
+    den = np.abs(y).max(axis=1, keepdims=True)
+    assert np.max(np.abs(got - want) / den) <= RTOL
+    assert rel_err(got, want) <= 2 * RTOL
+
+
+def test_int8_head_full_and_high_rows():
+    c = wl.int8_head()
+    codes, scale = oracle.pack_int8(c.W)
+    gc, gs = qmv.qpack_int8(dev(c.W))
+    assert np.array_equal(codes, host(gc)) and np.array_equal(scale, host(gs))
+    y = host(qmv.qmatvec_int8(gc, gs, dev(c.x)))[0]
+    want = oracle.matvec("int8", codes, scale, c.x)[0]
+    assert rel_err(y, want) <= RTOL
+    # rows from 65024 up must be live wherever the reference is nonzero
+    hi = np.arange(65024, c.W.shape[0])
+    live = want[hi] != 0
+    assert live.sum() > 0.99 * len(hi)
+    assert np.all(y[hi][live] != 0)
+    assert np.max(np.abs(y[hi] - want[hi])) <= RTOL * np.max(np.abs(want))
+
+
+@pytest.fixture(scope="module")
+def moe_case():
+    c = wl.moe()
+    E, I2, H = c.W_gate_up.shape
+    I = I2 // 2
+    gu = dev(c.W_gate_up.reshape(E * I2, H))
+    dn = dev(c.W_down.reshape(E * H, I))
+    guc, gus = qmv.qpack_int4(gu)
+    dnc, dns = qmv.qpack_int4(dn)
+    del gu, dn
+    return c, guc.view(E, I2, H // 2), gus.view(E, I2, H // 32), dnc.view(E, H, I // 2), dns.view(E, H, I // 32)
+
+
+def _oracle_experts(c, experts):
+    """Oracle-packed slabs for the listed experts (others left zero)."""
+    E, I2, H = c.W_gate_up.shape
+    I = I2 // 2
+    guc = np.zeros((E, I2, H // 2), np.uint8)
+    gus = np.zeros((E, I2, H // 32), np.uint16)
+    dnc = np.zeros((E, H, I // 2), np.uint8)
+    dns = np.zeros((E, H, I // 32), np.uint16)
+    for e in experts:
+        guc[e], gus[e] = oracle.pack_int4(c.W_gate_up[e])
+        dnc[e], dns[e] = oracle.pack_int4(c.W_down[e])
+    return guc, gus, dnc, dns
+
+
+def test_moe_route_parity(moe_case):
+    c = moe_case[0]
+    ids, w = qmv.qmoe_route(dev(c.logits), c.topk)
+    oids, ow = oracle.moe_route(c.logits, c.topk)
+    assert np.array_equal(host(ids), oids)
+    assert np.allclose(host(w), ow, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_moe_layer_parity(moe_case, T):
+    c, guc, gus, dnc, dns = moe_case
+    logits, x = c.logits[:T], c.x[:T]
+    oids, ow = oracle.moe_route(logits, c.topk)
+    experts = np.unique(oids)
+    ogu, ogs, odc, ods = _oracle_experts(c, experts)
+    for e in experts:   # the GPU packed the routed experts bit-exactly
+        assert np.array_equal(ogu[e], host(guc[e])) and np.array_equal(ogs[e], host(gus[e]))
+        assert np.array_equal(odc[e], host(dnc[e])) and np.array_equal(ods[e], host(dns[e]))
+    want, h_want = oracle.moe_ffn(ogu, ogs, odc, ods, x, oids, ow, return_h=True)
+    y, ids, w = qmv.moe_ffn(guc, gus, dnc, dns, dev(x), dev(logits), c.topk)
+    assert np.array_equal(host(ids), oids)
+    assert rel_err(host(y), want) <= RTOL
+    # the fused SwiGLU activations agree to within one fp16 step
+    h = host(qmv.gather_qmatvec("int4", guc, gus, dev(x), ids, epi="swiglu")).astype(np.float64)
+    step = np.abs(h_want) * 2.0 ** -10 + 2.0 ** -24
+    assert np.all(np.abs(h - h_want) <= step)
+
+
+def test_moe_gather_none_matches_per_slot_matvec(moe_case):
+    c, guc, gus, dnc, dns = moe_case
+    T = 3
+    oids, _ = oracle.moe_route(c.logits[:T], c.topk)
+    y = host(qmv.gather_qmatvec("int4", dnc, dns, dev(np.ascontiguousarray(
+        np.random.default_rng(1).standard_normal((T, c.topk, 512)).astype(np.float16))),
+        dev(oids), epi="none", x_per_slot=True))
+    xs = np.random.default_rng(1).standard_normal((T, c.topk, 512)).astype(np.float16)
+    for t in range(T):
+        for s in range(c.topk):
+            e = oids[t, s]
+            oc, os_ = oracle.pack_int4(c.W_down[e])
+            want = oracle.matvec("int4", oc, os_, xs[t, s][None])[0]
+            assert rel_err(y[t, s], want) <= RTOL

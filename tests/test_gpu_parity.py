@@ -1,0 +1,163 @@
+"""GPU parity against the CPU oracle at sizes the oracle finishes in seconds:
+packing bit-exact, dequant exact, matvec within the relative-error bound,
+across every kernel variant (lanes per row, chunks per lane, batch width),
+ragged row counts and the special blocks of each format."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_decode_matvec_amd as qmv
+from quantized_decode_matvec_amd import workloads as wl
+from tests.gpu_helpers import RTOL, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["int4", "fp4", "int8", "km4"]
+# (N, K): short K (16 lanes per row), 32 lanes, one chunk per lane at 64 lanes,
+# two/three/four chunks per lane, a K beyond the register fast path, ragged N
+SHAPES = [(37, 96), (50, 512), (65, 1024), (129, 2048), (33, 2560), (47, 4096), (21, 6144), (8, 8192)]
+
+
+def _special_rows(K, dtype):
+    """Rows that hit the formats' corner cases: all zero, tiny values, exact
+    E2M1 ties at E = 0, a single outlier per block, negative zeros."""
+    rows = np.zeros((6, K), np.float32)
+    rows[1, :] = 2.0 ** -24
+    ties = np.array([6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -2.5, -5.0], np.float32)
+    rows[2, :] = np.resize(ties, K)
+    rows[2, ::32] = 6.0
+    rows[3, ::32] = 1.0
+    rows[4, :] = -0.0
+    rows[4, 1::2] = np.linspace(-1, 1, K // 2)
+    rows[5, :] = np.resize(np.array([-0.5, 0.0, 0.25, 1.0], np.float32), K)
+    return rows.astype(dtype)
+
+
+def _case(fmt, N, K, B=1, dtype=np.float16, seed=0):
+    c = wl.small_dense(fmt, N, K, batch=B, seed=seed, dtype=dtype, outlier_frac=0.01)
+    W = c.W.copy()
+    sp = _special_rows(K, dtype)
+    W[: min(len(sp), N)] = sp[: min(len(sp), N)]
+    return W, c.x
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", SHAPES[:6])
+def test_pack_bit_exact(fmt, N, K):
+    W, _ = _case(fmt, N, K)
+    if fmt == "km4" and K > 4096:
+        pytest.skip("km4 packing takes K <= 4096")
+    want = oracle.pack(fmt, W)
+    got = qmv.qpack(fmt, dev(W))
+    for a, b in zip(want, got):
+        assert np.array_equal(a, host(b)), fmt
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8"])
+def test_pack_fp32_input_bit_exact(fmt):
+    c = wl.tiny_int4()
+    W = c.W.copy()
+    W[:6] = _special_rows(W.shape[1], np.float32)
+    W[6, :32] = np.float32(0.99999994)
+    W[7, :32] = np.float32(2.0 ** -130)
+    want = oracle.pack(fmt, W)
+    got = qmv.qpack(fmt, dev(W))
+    for a, b in zip(want, got):
+        assert np.array_equal(a, host(b))
+
+
+@pytest.mark.parametrize("max_iter", [1, 3, 20])
+def test_km4_pack_iterations_bit_exact(max_iter):
+    W, _ = _case("km4", 96, 512, seed=3)
+    want = oracle.pack_km4(W, max_iter=max_iter)
+    got = qmv.qpack_km4(dev(W), max_iter=max_iter)
+    assert np.array_equal(want[0], host(got[0]))
+    assert np.array_equal(want[1], host(got[1]))
+
+
+def test_km4_pack_midpoint_means():
+    """Rows whose cluster means fall on fp16 midpoints (ties to even)."""
+    ints = [v for v in range(-8, 8) if v != 1]
+    rows = []
+    for pair in [(1.0, 1.0 + 2 ** -10), (1.0 + 2 ** -10, 1.0 + 2 ** -9)]:
+        r = np.array(sorted(ints * 2 + list(pair)), np.float16)
+        rows.append(r[np.random.default_rng(len(rows)).permutation(32)])
+    W = np.stack(rows)
+    want = oracle.pack_km4(W)
+    got = qmv.qpack_km4(dev(W))
+    assert np.array_equal(want[1], host(got[1]))
+    assert np.array_equal(want[0], host(got[0]))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_dequant_exact(fmt):
+    W, _ = _case(fmt, 41, 2560 if fmt != "km4" else 2048)
+    codes, plane = oracle.pack(fmt, W)
+    D = host(qmv.qdequant(fmt, dev(codes), dev(plane)))
+    assert np.array_equal(D.astype(np.float64), oracle.dequant(fmt, codes, plane))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+def test_matvec_parity(fmt, N, K, B):
+    W, x = _case(fmt, N, K, B=B, seed=N + B)
+    if fmt == "km4":
+        codes, plane = oracle.pack_km4(W, max_iter=4)
+    else:
+        codes, plane = oracle.pack(fmt, W)
+    want = oracle.matvec(fmt, codes, plane, x)
+    y = host(qmv.qmatvec(fmt, dev(codes), dev(plane), dev(x)))
+    assert rel_err(y, want) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", [1, 5])
+def test_matvec_fp32_x(fmt, B):
+    W, x = _case(fmt, 70, 512, B=B, dtype=np.float32, seed=7)
+    if fmt == "km4":
+        W = W.astype(np.float16)
+    codes, plane = oracle.pack(fmt, W)
+    want = oracle.matvec(fmt, codes, plane, x)
+    y = host(qmv.qmatvec(fmt, dev(codes), dev(plane), dev(x.astype(np.float32))))
+    assert rel_err(y, want) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_matvec_unit_vectors_pick_columns_exactly(fmt):
+    W, _ = _case(fmt, 64, 2048, seed=5)
+    codes, plane = oracle.pack(fmt, W)
+    D = oracle.dequant(fmt, codes, plane)
+    ks = [0, 1, 31, 32, 1000, 2047]
+    x = np.zeros((len(ks), 2048), np.float16)
+    for i, k in enumerate(ks):
+        x[i, k] = 1.0
+    y = host(qmv.qmatvec(fmt, dev(codes), dev(plane), dev(x)))
+    for i, k in enumerate(ks):
+        assert np.array_equal(y[i].astype(np.float64), D[:, k])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_matvec_deterministic(fmt):
+    W, x = _case(fmt, 300, 2048, B=2, seed=9)
+    codes, plane = oracle.pack(fmt, W) if fmt != "km4" else oracle.pack_km4(W, max_iter=2)
+    c, p, xx = dev(codes), dev(plane), dev(x)
+    y1 = host(qmv.qmatvec(fmt, c, p, xx))
+    y2 = host(qmv.qmatvec(fmt, c, p, xx))
+    assert np.array_equal(y1, y2)
+
+
+def test_gpu_pack_then_gpu_matvec_matches_oracle_end_to_end():
+    for fmt in FMTS:
+        W, x = _case(fmt, 200, 2048, B=1, seed=11)
+        codes, plane = qmv.qpack(fmt, dev(W))
+        y = host(qmv.qmatvec(fmt, codes, plane, dev(x)))
+        oc, op = oracle.pack(fmt, W)
+        assert rel_err(y, oracle.matvec(fmt, oc, op, x)) <= RTOL
+
+
+def test_stream_read_checksum():
+    rng = np.random.default_rng(0)
+    a = rng.integers(0, 2 ** 32, size=(1 << 20) + 4, dtype=np.uint32)
+    sink = host(qmv.qmv_stream_read(dev(a.view(np.int32))))
+    assert np.bitwise_xor.reduce(sink.view(np.uint32)) == np.bitwise_xor.reduce(a)
