@@ -21,112 +21,135 @@ namespace qmv {
 // Fast path: x fp16 in registers.
 //   FMT  format, BT batch width compiled (runtime B <= BT, extra rows zero),
 //   LPR  lanes per row (64, 32 or 16), CPL chunks per lane, R row groups per
-//   wave iteration.
+//   iteration, ITERS iterations per wave, WAVES waves per workgroup.
+// Each wave handles ITERS * R * (64 / LPR) consecutive rows and exits; a
+// workgroup's rows are consecutive, so every workgroup streams one contiguous
+// stretch of the code plane. The x slices are loaded once per wave, so ITERS
+// grows with the batch width to amortize them.
 // ---------------------------------------------------------------------------
-template <int FMT, int BT, int LPR, int CPL, int R>
-__global__ __launch_bounds__(256) void mv_fast(const uint8_t *__restrict__ codes,
-                                               const void *__restrict__ plane, int64_t N, int K,
-                                               const _Float16 *__restrict__ x, int B,
-                                               float *__restrict__ y) {
+template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK>
+__global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict__ codes,
+                                                      const void *__restrict__ plane, int64_t N, int K,
+                                                      const _Float16 *__restrict__ x, int B,
+                                                      float *__restrict__ y) {
     constexpr int RPW = kWave / LPR;            // rows per row group
     constexpr int XW = ChunkTraits<FMT>::kXWords;
-    constexpr int ROWS_IT = R * RPW;            // rows per wave iteration
-    __shared__ _Float16 lut_lds[(FMT == KM4) ? 4 * ROWS_IT * 16 : 1];
+    constexpr int ROWS_IT = R * RPW;            // rows per iteration
+    // with one wave per workgroup and one row per row group the km4 tables sit
+    // at compile-time LDS offsets
+    constexpr bool KM4_IMM = (FMT == KM4) && WAVES == 1 && RPW == 1;
+    __shared__ __align__(16) _Float16 lut_lds[(FMT == KM4) ? WAVES * ROWS_IT * 16 : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = (WAVES == 1) ? 0 : (threadIdx.x >> 6);
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
-    const int cpr = (FMT == INT8) ? K / 16 : K / 32;   // chunks per row
-    const int nb = K / 32;                              // blocks per row
-    const int64_t row_bytes = (FMT == INT8) ? K : K / 2;
+    // FULLK: K fills the lanes exactly (chunks per row == LPR * CPL)
+    const int cpr = FULLK ? LPR * CPL : ((FMT == INT8) ? K / 16 : K / 32);   // chunks per row
+    const int nb = K / 32;                                                   // blocks per row
+    const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
+    const int64_t wrow0 = ((int64_t)blockIdx.x * WAVES + wave) * ROWS_IT * ITERS;
+    if (wrow0 >= N) return;
 
-    // x slices for this lane's chunks, every batch row
+    // x slices for this lane's chunks, every batch row (rows b >= B are zero)
     uint32_t xr[CPL][BT][XW];
 #pragma unroll
     for (int j = 0; j < CPL; j++) {
         int c = sub + LPR * j;
 #pragma unroll
-        for (int b = 0; b < BT; b++) load_x_slice<FMT>(x + (size_t)b * K, c, c < cpr && b < B, xr[j][b]);
+        for (int b = 0; b < BT; b++)
+            load_x_slice<FMT>(x + (size_t)(b < B ? b : 0) * K, c, (FULLK || c < cpr) && (BT == 1 || b < B),
+                              xr[j][b]);
     }
 
-    const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
-    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+#pragma unroll 1
+    for (int it = 0; it < ITERS; it++) {
+    const int64_t row0 = wrow0 + (int64_t)it * ROWS_IT;
+    if (row0 >= N) break;
+    // Wave-uniform bases, 32-bit per-lane offsets. Loads are unconditional: a
+    // row past the end reads row N-1 and a chunk past the end of the row reads
+    // chunk 0; their x slices are zero and their rows are never stored, so
+    // they contribute nothing.
+    const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);   // last valid row offset
+    const uint8_t *cbase = codes + row0 * (int64_t)row_bytes;
+    uint4 cw[R][CPL];
+    float sc[R][CPL];
+#pragma unroll
+    for (int g = 0; g < R; g++) {
+        int rr = g * RPW + rsub;
+        rr = rr <= last ? rr : last;
+#pragma unroll
+        for (int j = 0; j < CPL; j++) {
+            int c = sub + LPR * j;
+            int cc = (FULLK || c < cpr) ? c : 0;
+            cw[g][j] = load_stream16(cbase + ((uint32_t)rr * row_bytes + (uint32_t)cc * 16u));
+            if constexpr (FMT == INT4 || FMT == INT8) {
+                const uint16_t *s = reinterpret_cast<const uint16_t *>(plane) + row0 * nb;
+                int blk = (FMT == INT8) ? cc / 2 : cc;
+                sc[g][j] = f16_bits_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)blk]);
+            } else if constexpr (FMT == FP4) {
+                const uint8_t *s = reinterpret_cast<const uint8_t *>(plane) + row0 * nb;
+                sc[g][j] = e8m0_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)cc]);
+            } else {
+                sc[g][j] = 1.f;
+            }
+        }
+    }
     _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
-
-    for (int64_t row0 = gw * ROWS_IT; row0 < N; row0 += waves_total * ROWS_IT) {
-        uint4 cw[R][CPL];
-        float sc[R][CPL];
-        // issue all loads of the iteration first
+    if constexpr (FMT == KM4) {
+        // stage this iteration's tables: 8 dwords per row
+        const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane) + row0 * 8;
+        uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
 #pragma unroll
-        for (int g = 0; g < R; g++) {
-            int64_t row = row0 + g * RPW + rsub;
-            bool rv = row < N;
-            const uint8_t *rp = codes + (rv ? row : 0) * row_bytes;
+        for (int i0 = 0; i0 < ROWS_IT * 8; i0 += kWave) {
+            int i = i0 + lane;
+            if (ROWS_IT * 8 % kWave == 0 || i < ROWS_IT * 8) {
+                int rr = i / 8;
+                rr = rr <= last ? rr : last;
+                ldst[i] = lsrc[rr * 8 + (i % 8)];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    float acc[R * BT];
+#pragma unroll
+    for (int g = 0; g < R; g++) {
+#pragma unroll
+        for (int b = 0; b < BT; b++) {
+            float a = 0.f;
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
-                int c = sub + LPR * j;
-                bool v = rv && c < cpr;
-                cw[g][j] = v ? *reinterpret_cast<const uint4 *>(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
-                if constexpr (FMT == INT4 || FMT == INT8) {
-                    const uint16_t *s = reinterpret_cast<const uint16_t *>(plane);
-                    int blk = (FMT == INT8) ? c / 2 : c;
-                    sc[g][j] = v ? f16_bits_to_f32(s[(rv ? row : 0) * nb + blk]) : 0.f;
-                } else if constexpr (FMT == FP4) {
-                    const uint8_t *s = reinterpret_cast<const uint8_t *>(plane);
-                    sc[g][j] = v ? e8m0_to_f32(s[(rv ? row : 0) * nb + c]) : 0.f;
-                } else {
-                    sc[g][j] = 1.f;
-                }
+                float d;
+                if constexpr (FMT == INT4) d = chunk_dot_int4(cw[g][j], xr[j][b]);
+                else if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[g][j], xr[j][b]);
+                else if constexpr (FMT == INT8) d = chunk_dot_int8(cw[g][j], xr[j][b]);
+                else if constexpr (KM4_IMM)
+                    d = chunk_dot_km4_imm(cw[g][j], reinterpret_cast<const char *>(lut_lds) + g * 32, xr[j][b]);
+                else d = chunk_dot_km4(cw[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
+                a = (FMT == KM4) ? a + d : __builtin_fmaf(d, sc[g][j], a);
             }
+            acc[g * BT + b] = a;
         }
-        if constexpr (FMT == KM4) {
-            // stage the tables of this iteration's rows: 8 dwords per row
-            const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane);
-            uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
-            for (int i = lane; i < ROWS_IT * 8; i += kWave) {
-                int64_t row = row0 + i / 8;
-                ldst[i] = row < N ? lsrc[row * 8 + (i % 8)] : 0u;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        float acc[R][BT];
+    }
+    using Red = GroupReduce<R * BT, LPR>;
+    Red::run(acc, lane);
+    if (Red::writer(lane)) {
+        const int base = Red::base(lane);
 #pragma unroll
-        for (int g = 0; g < R; g++)
-#pragma unroll
-            for (int b = 0; b < BT; b++) acc[g][b] = 0.f;
-#pragma unroll
-        for (int g = 0; g < R; g++) {
-#pragma unroll
-            for (int j = 0; j < CPL; j++) {
-#pragma unroll
-                for (int b = 0; b < BT; b++) {
-                    float d;
-                    if constexpr (FMT == INT4) d = chunk_dot_int4(cw[g][j], xr[j][b]);
-                    else if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[g][j], xr[j][b]);
-                    else if constexpr (FMT == INT8) d = chunk_dot_int8(cw[g][j], xr[j][b]);
-                    else d = chunk_dot_km4(cw[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
-                    acc[g][b] = __builtin_fmaf(d, sc[g][j], acc[g][b]);
-                }
-            }
-        }
-        if constexpr (FMT == KM4) {
-            // the next iteration rewrites the tables: keep the reads above it
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-#pragma unroll
-        for (int g = 0; g < R; g++) {
+        for (int j = 0; j < Red::live; j++) {
+            int idx = base + j, g = idx / BT, b = idx % BT;
             int64_t row = row0 + g * RPW + rsub;
-#pragma unroll
-            for (int b = 0; b < BT; b++) {
-                float s = group_sum<LPR>(acc[g][b]);
-                if (sub == 0 && row < N && b < B) y[(size_t)b * N + row] = s;
-            }
+            if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
         }
+    }
+    if constexpr (FMT == KM4 && ITERS > 1) {
+        // the next iteration rewrites the tables: keep this iteration's reads above it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     }
 }
 
@@ -249,14 +272,31 @@ static int grid_for_waves(int64_t waves_needed) {
     return (int)((waves + 3) / 4);
 }
 
+// Launch shape per format and batch width (rows per iteration R, iterations
+// per wave ITERS, waves per workgroup WAVES), chosen by measurement on MI355X
+// at the lm_head shape (248320 x 2048). km4 needs one wave per workgroup for
+// its compile-time table offsets; more batch rows need more rows per wave to
+// amortize the x slices held in registers.
+template <int FMT, int BT> struct LaunchShape {
+    static constexpr int R = (BT == 1) ? ((FMT == INT4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
+    static constexpr int ITERS = (FMT == KM4) ? ((BT == 1) ? 4 : (BT == 8 ? 16 : 2))
+                                              : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
+    static constexpr int WAVES = (FMT == KM4) ? 1 : 4;
+};
+
 template <int FMT, int BT, int LPR, int CPL>
 static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
                               float *y, hipStream_t st) {
-    constexpr int R = (BT <= 2) ? 4 : (BT <= 4 ? 2 : 1);
-    constexpr int ROWS_IT = R * (kWave / LPR);
-    int grid = grid_for_waves((N + ROWS_IT - 1) / ROWS_IT);
-    hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, R>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
-                       reinterpret_cast<const _Float16 *>(x), B, y);
+    using S = LaunchShape<FMT, BT>;
+    constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
+    int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
+    const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+    if (cpr == LPR * CPL)
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true>), dim3((unsigned)grid),
+                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+    else
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false>), dim3((unsigned)grid),
+                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
     return hipGetLastError();
 }
 
@@ -330,21 +370,23 @@ hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t
 }
 
 // ---------------------------------------------------------------------------
-// Streaming-read ceiling: every lane reads 16-byte words, a grid-stride loop
-// with four loads in flight per lane; one xor checksum per workgroup.
+// Streaming-read ceiling: the matvec's access pattern with no arithmetic.
+// Each 256-thread workgroup reads one contiguous 16 KiB stretch with four
+// non-temporal 16-byte loads per lane; one xor checksum per workgroup.
 // ---------------------------------------------------------------------------
+constexpr int kReadChunk16 = 1024;   // 16-byte words per workgroup
+
 __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restrict__ p, int64_t n16,
                                                           uint32_t *__restrict__ sink) {
+    const int64_t beg = (int64_t)blockIdx.x * kReadChunk16;
     uint32_t acc = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
-    }
-    for (; i < n16; i += stride) {
-        uint4 a = p[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+#pragma unroll
+    for (int u = 0; u < kReadChunk16 / 256; u++) {
+        int64_t i = beg + threadIdx.x + 256 * u;
+        if (i < n16) {
+            uint4 a = load_stream16(p + i);
+            acc ^= a.x ^ a.y ^ a.z ^ a.w;
+        }
     }
     __shared__ uint32_t red[256];
     red[threadIdx.x] = acc;
@@ -356,14 +398,11 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4 *__restric
     }
 }
 
-size_t stream_read_grid(size_t bytes) {
-    (void)bytes;
-    return (size_t)device_cu_count() * 8;
-}
+size_t stream_read_grid(size_t bytes) { return (bytes / 16 + kReadChunk16 - 1) / kReadChunk16; }
 
 hipError_t launch_stream_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t st) {
-    int grid = (int)stream_read_grid(bytes);
-    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const uint4 *>(buf),
+    size_t grid = stream_read_grid(bytes);
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(256), 0, st, reinterpret_cast<const uint4 *>(buf),
                        (int64_t)(bytes / 16), sink);
     return hipGetLastError();
 }

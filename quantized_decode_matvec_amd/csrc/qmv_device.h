@@ -45,20 +45,17 @@ template <int FMT>
 __device__ __forceinline__ void load_x_slice(const _Float16 *__restrict__ xrow, int chunk, bool valid,
                                              uint32_t (&xw)[ChunkTraits<FMT>::kXWords]) {
     constexpr int E = ChunkTraits<FMT>::kElems;
-    if (!valid) {
-#pragma unroll
-        for (int i = 0; i < E / 2; i++) xw[i] = 0;
-        return;
-    }
-    const uint4 *p = reinterpret_cast<const uint4 *>(xrow + (size_t)chunk * E);
+    // always load (from chunk 0 when invalid) and zero afterwards: a predicated
+    // load would become a branch that serializes the loads around it
+    const uint4 *p = reinterpret_cast<const uint4 *>(xrow + (size_t)(valid ? chunk : 0) * E);
     uint32_t nat[E / 2];
 #pragma unroll
     for (int i = 0; i < E / 8; i++) {
         uint4 v = p[i];
-        nat[4 * i + 0] = v.x;
-        nat[4 * i + 1] = v.y;
-        nat[4 * i + 2] = v.z;
-        nat[4 * i + 3] = v.w;
+        nat[4 * i + 0] = valid ? v.x : 0u;
+        nat[4 * i + 1] = valid ? v.y : 0u;
+        nat[4 * i + 2] = valid ? v.z : 0u;
+        nat[4 * i + 3] = valid ? v.w : 0u;
     }
     if constexpr (FMT == INT4) {
         // nat[4d + m] = (x[8d+2m], x[8d+2m+1])
@@ -83,18 +80,27 @@ __device__ __forceinline__ void load_x_slice(const _Float16 *__restrict__ xrow, 
 // INT4: (w & 0x000F000F) | 0x64006400 is the half2 (1024 + u_lo, 1024 + u_hi);
 // the 0x00F0 nibbles land 4 bits higher, i.e. 1024 + 16u. Removing the bias
 // exactly gives (u - 8) and 16 (u - 8); the factor 16 is taken out at the end.
+// (v & mask) | magic as one v_and_or_b32 (the compiler would otherwise emit an
+// AND and an OR, since a VOP3 instruction cannot take two literal constants)
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask), "v"(magic));
+    return r;
+}
+
 __device__ __forceinline__ float chunk_dot_int4(uint4 cw, const uint32_t (&xw)[16]) {
     const h2 b0 = as_h2(0x64086408u);   // (1032, 1032)
     const h2 b1 = as_h2(0x64806480u);   // (1152, 1152)
+    const uint32_t magic = 0x64006400u;
     float lo = 0.f, hi = 0.f;
     uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
 #pragma unroll
     for (int d = 0; d < 4; d++) {
         uint32_t v = w[d], v8 = v >> 8;
-        h2 a04 = as_h2((v & 0x000F000Fu) | 0x64006400u) - b0;
-        h2 a15 = as_h2((v & 0x00F000F0u) | 0x64006400u) - b1;
-        h2 a26 = as_h2((v8 & 0x000F000Fu) | 0x64006400u) - b0;
-        h2 a37 = as_h2((v8 & 0x00F000F0u) | 0x64006400u) - b1;
+        h2 a04 = as_h2(and_or(v, 0x000F000Fu, magic)) - b0;
+        h2 a15 = as_h2(and_or(v, 0x00F000F0u, magic)) - b1;
+        h2 a26 = as_h2(and_or(v8, 0x000F000Fu, magic)) - b0;
+        h2 a37 = as_h2(and_or(v8, 0x00F000F0u, magic)) - b1;
         lo = dot2(a04, as_h2(xw[4 * d + 0]), lo);
         lo = dot2(a26, as_h2(xw[4 * d + 1]), lo);
         hi = dot2(a15, as_h2(xw[4 * d + 2]), hi);
@@ -136,6 +142,7 @@ __device__ __forceinline__ float chunk_dot_int8(uint4 cw, const uint32_t (&xw)[8
 }
 
 // KM4: table lookups from the row's 16-entry fp16 table staged in LDS.
+// Generic form: any table address.
 __device__ __forceinline__ float chunk_dot_km4(uint4 cw, const _Float16 *__restrict__ lut,
                                                const uint32_t (&xw)[16]) {
     float acc = 0.f;
@@ -151,6 +158,53 @@ __device__ __forceinline__ float chunk_dot_km4(uint4 cw, const _Float16 *__restr
         }
     }
     return acc;
+}
+
+// (byte S of w) & 0x1E in one SDWA instruction.
+template <int S>
+__device__ __forceinline__ uint32_t byte_and_1e(uint32_t w) {
+    uint32_t r;
+    if constexpr (S == 0)
+        asm("v_and_b32_sdwa %0, 30, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (S == 1)
+        asm("v_and_b32_sdwa %0, 30, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (S == 2)
+        asm("v_and_b32_sdwa %0, 30, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_and_b32_sdwa %0, 30, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
+// KM4 with the table at a compile-time LDS byte offset: every code's table
+// byte offset 2c is one SDWA AND of a pre-shifted code word (w << 1 holds the
+// even nibbles at bits 1-4 of each byte, w >> 3 the odd ones), and the row's
+// table base folds into the LDS instruction's immediate offset.
+// L must be a compile-time constant LDS address after unrolling (a static
+// __shared__ array in a one-wave workgroup plus a constant row offset).
+__device__ __forceinline__ float chunk_dot_km4_imm(uint4 cw, const char *L, const uint32_t (&xw)[16]) {
+    float acc = 0.f;
+    uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        uint32_t w1 = w[d] << 1, w3 = w[d] >> 3;
+        uint32_t a[8] = {byte_and_1e<0>(w1), byte_and_1e<0>(w3), byte_and_1e<1>(w1), byte_and_1e<1>(w3),
+                         byte_and_1e<2>(w1), byte_and_1e<2>(w3), byte_and_1e<3>(w1), byte_and_1e<3>(w3)};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            h2 v;
+            v.x = *reinterpret_cast<const _Float16 *>(L + a[2 * i]);
+            v.y = *reinterpret_cast<const _Float16 *>(L + a[2 * i + 1]);
+            acc = dot2(v, as_h2(xw[4 * d + i]), acc);
+        }
+    }
+    return acc;
+}
+
+// 16-byte load that bypasses cache allocation (the code planes are streamed once)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void *p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // fp16 bits -> fp32 (exact)
@@ -171,5 +225,75 @@ __device__ __forceinline__ float group_sum(float v) {
     for (int m = width / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, width);
     return v;
 }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over each row of 16 lanes with DPP (quad swaps, half-row mirror, row
+// mirror); every lane of the row receives the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);   // row_half_mirror
+    v += dpp_mov<0x140>(v);   // row_mirror
+    return v;
+}
+
+// Reduce V partial sums per lane over groups of LPR lanes (LPR = 16, 32 or 64).
+// Instead of V separate butterflies, each cross-row step exchanges half of the
+// values and keeps the other half ("transposed" reduction), so a step costs
+// V/2 shuffles and the set of live values halves. On return v[0 .. live) hold
+// group sums, identical in every lane of a 16-lane row; value j of lane l is
+// the original index base + j (see live/base below).
+template <int V, int LPR>
+struct GroupReduce {
+    static constexpr bool kH32 = (LPR == 64 && V >= 2);
+    static constexpr int kV1 = kH32 ? V / 2 : V;
+    static constexpr bool kH16 = (LPR >= 32 && kV1 >= 2);
+    static constexpr int live = kH16 ? kV1 / 2 : kV1;
+
+    __device__ __forceinline__ static void run(float (&v)[V], int lane) {
+        if constexpr (kH32) {
+            const bool up = lane & 32;
+#pragma unroll
+            for (int j = 0; j < V / 2; j++) {
+                float send = up ? v[j] : v[j + V / 2];
+                float keep = up ? v[j + V / 2] : v[j];
+                v[j] = keep + __shfl_xor(send, 32);
+            }
+        } else if constexpr (LPR == 64) {
+            v[0] += __shfl_xor(v[0], 32);
+        }
+        if constexpr (kH16) {
+            const bool up = lane & 16;
+#pragma unroll
+            for (int j = 0; j < kV1 / 2; j++) {
+                float send = up ? v[j] : v[j + kV1 / 2];
+                float keep = up ? v[j + kV1 / 2] : v[j];
+                v[j] = keep + __shfl_xor(send, 16);
+            }
+        } else if constexpr (LPR >= 32) {
+            v[0] += __shfl_xor(v[0], 16);
+        }
+#pragma unroll
+        for (int j = 0; j < live; j++) v[j] = row16_sum(v[j]);
+    }
+    // original index of v[0] in this lane
+    __device__ __forceinline__ static int base(int lane) {
+        int b = 0;
+        if constexpr (kH32) b += (lane & 32) ? V / 2 : 0;
+        if constexpr (kH16) b += (lane & 16) ? kV1 / 2 : 0;
+        return b;
+    }
+    // true for the one lane per (16-lane row, distinct value set) that stores
+    __device__ __forceinline__ static bool writer(int lane) {
+        if (lane & 15) return false;
+        if constexpr (LPR == 64 && !kH32) { if (lane & 32) return false; }
+        if constexpr (LPR >= 32 && !kH16) { if (lane & 16) return false; }
+        return true;
+    }
+};
 
 }  // namespace qmv

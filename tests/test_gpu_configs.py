@@ -53,8 +53,8 @@ def test_km4_lm_head_pack_sampled_rows(lm_head):
     c, codes, lut = lm_head
     rows = sample_rows(c.W.shape[0], 256)
     oc, ol = oracle.pack_km4(c.W[rows])
-    assert np.array_equal(oc, host(codes[rows]))
-    assert np.array_equal(ol, host(lut[rows]))
+    assert np.array_equal(oc, host(codes)[rows])
+    assert np.array_equal(ol, host(lut)[rows])
 
 
 @pytest.mark.parametrize("B", [1, 8])
@@ -65,11 +65,7 @@ def test_km4_lm_head_matvec_sampled_rows(lm_head, B):
     rows = sample_rows(c.W.shape[0], 512, seed=B)
     oc, ol = oracle.pack_km4(c.W[rows])
     want = oracle.matvec("km4", oc, ol, x)
-    # normalise by the full output's scale: rel err against max |y| over all rows
-    got = y[:, rows].astype(np.float64)
-    den = np.abs(y).max(axis=1, keepdims=True)
-    assert np.max(np.abs(got - want) / den) <= RTOL
-    assert rel_err(got, want) <= 2 * RTOL
+    assert rel_err(y[:, rows], want) <= RTOL
 
 
 def test_int8_head_full_and_high_rows():
@@ -147,10 +143,8 @@ def test_moe_gather_none_matches_per_slot_matvec(moe_case):
     c, guc, gus, dnc, dns = moe_case
     T = 3
     oids, _ = oracle.moe_route(c.logits[:T], c.topk)
-    y = host(qmv.gather_qmatvec("int4", dnc, dns, dev(np.ascontiguousarray(
-        np.random.default_rng(1).standard_normal((T, c.topk, 512)).astype(np.float16))),
-        dev(oids), epi="none", x_per_slot=True))
     xs = np.random.default_rng(1).standard_normal((T, c.topk, 512)).astype(np.float16)
+    y = host(qmv.gather_qmatvec("int4", dnc, dns, dev(xs), dev(oids), epi="none", x_per_slot=True))
     for t in range(T):
         for s in range(c.topk):
             e = oids[t, s]
