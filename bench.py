@@ -49,7 +49,29 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time the int8 head and the MoE layer")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-metric", action="store_true", help="time the metric kernel only (for profiling)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run a plain 1 GiB device copy and a 1 GiB streaming read, for HBM byte-counter calibration")
     return ap.parse_args()
+
+
+def calibrate():
+    """Known-size traffic for scaling the FETCH_SIZE / WRITE_SIZE counters:
+    5 device-to-device copies of 1 GiB (torch's copy kernel: 1 GiB read and
+    1 GiB written each) and 5 streaming reads of 1 GiB (qmv_stream_read)."""
+    import torch
+    import quantized_decode_matvec_amd as qmv
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    dst = torch.empty_like(src)
+    sink = torch.empty((int(qmv.lib().qmv_stream_read_sink_words(n)),), dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    for _ in range(5):
+        qmv.qmv_stream_read(src, sink=sink)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_bytes_per_copy": n, "copies": 5, "stream_reads": 5}))
 
 
 def gpu_warm(seconds=0.5):
@@ -84,16 +106,20 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def traffic_from_profiles(kernel_prefix):
-    """HBM bytes per launch recorded by the counter runs, if present."""
+def traffic_from_profiles(key):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel sources (otherwise None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
+    from quantized_decode_matvec_amd.rocprof_summary import kernel_source_hash
     try:
-        d = json.load(open(path))
-        return d.get(kernel_prefix)
-    except Exception:
+        rec = json.load(open(path)).get(key)
+    except ValueError:
         return None
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec["traffic_bytes"]
 
 
 def cpu_baseline(c, x1):
@@ -126,6 +152,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU (torch.cuda.is_available() is False)", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate:
+        calibrate()
+        return
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
 
@@ -204,7 +233,7 @@ def main():
             extras.update(bench_int8_head(args))
             extras.update(bench_moe(args))
 
-    traffic = traffic_from_profiles("mv_fast_km4_b1")
+    traffic = traffic_from_profiles("km4_lm_head_b1")
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
