@@ -38,6 +38,8 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     // with one wave per workgroup and one row per row group the km4 tables sit
     // at compile-time LDS offsets
     constexpr bool KM4_IMM = (FMT == KM4) && WAVES == 1 && RPW == 1;
+    constexpr int LUT_WORDS = ROWS_IT * 8;      // km4 table dwords per iteration
+    constexpr int LUT_PER_LANE = (LUT_WORDS + kWave - 1) / kWave;
     __shared__ __align__(16) _Float16 lut_lds[(FMT == KM4) ? WAVES * ROWS_IT * 16 : 1];
 
     const int lane = threadIdx.x & 63;
@@ -51,6 +53,50 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     const int64_t wrow0 = ((int64_t)blockIdx.x * WAVES + wave) * ROWS_IT * ITERS;
     if (wrow0 >= N) return;
 
+    // Loads of one iteration. Wave-uniform bases, 32-bit per-lane offsets.
+    // Loads are unconditional: a row past the end reads row N-1 and a chunk
+    // past the end of the row reads chunk 0; their x slices are zero and their
+    // rows are never stored, so they contribute nothing.
+    uint4 cw[R][CPL];
+    float sc[R][CPL];
+    uint32_t lutv[LUT_PER_LANE];
+    auto issue_loads = [&](int64_t row0) {
+        const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);   // last valid row offset
+        const uint8_t *cbase = codes + row0 * (int64_t)row_bytes;
+#pragma unroll
+        for (int g = 0; g < R; g++) {
+            int rr = g * RPW + rsub;
+            rr = rr <= last ? rr : last;
+#pragma unroll
+            for (int j = 0; j < CPL; j++) {
+                int c = sub + LPR * j;
+                int cc = (FULLK || c < cpr) ? c : 0;
+                cw[g][j] = load_stream16(cbase + ((uint32_t)rr * row_bytes + (uint32_t)cc * 16u));
+                if constexpr (FMT == INT4 || FMT == INT8) {
+                    const uint16_t *s = reinterpret_cast<const uint16_t *>(plane) + row0 * nb;
+                    int blk = (FMT == INT8) ? cc / 2 : cc;
+                    sc[g][j] = f16_bits_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)blk]);
+                } else if constexpr (FMT == FP4) {
+                    const uint8_t *s = reinterpret_cast<const uint8_t *>(plane) + row0 * nb;
+                    sc[g][j] = e8m0_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)cc]);
+                } else {
+                    sc[g][j] = 1.f;
+                }
+            }
+        }
+        if constexpr (FMT == KM4) {
+            // this iteration's tables: 8 dwords per row, LUT_PER_LANE dwords per lane
+            const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane) + row0 * 8;
+#pragma unroll
+            for (int q = 0; q < LUT_PER_LANE; q++) {
+                int i = q * kWave + lane;
+                int rr = (i < LUT_WORDS ? i : LUT_WORDS - 1) / 8;
+                rr = rr <= last ? rr : last;
+                lutv[q] = lsrc[rr * 8 + (i % 8)];
+            }
+        }
+    };
+
     // x slices for this lane's chunks, every batch row (rows b >= B are zero)
     uint32_t xr[CPL][BT][XW];
 #pragma unroll
@@ -62,94 +108,73 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                               xr[j][b]);
     }
 
+    issue_loads(wrow0);
 #pragma unroll 1
     for (int it = 0; it < ITERS; it++) {
-    const int64_t row0 = wrow0 + (int64_t)it * ROWS_IT;
-    if (row0 >= N) break;
-    // Wave-uniform bases, 32-bit per-lane offsets. Loads are unconditional: a
-    // row past the end reads row N-1 and a chunk past the end of the row reads
-    // chunk 0; their x slices are zero and their rows are never stored, so
-    // they contribute nothing.
-    const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);   // last valid row offset
-    const uint8_t *cbase = codes + row0 * (int64_t)row_bytes;
-    uint4 cw[R][CPL];
-    float sc[R][CPL];
+        const int64_t row0 = wrow0 + (int64_t)it * ROWS_IT;
+        if (row0 >= N) break;
+        // take this iteration's data, then start the next iteration's loads so
+        // they are in flight while this one computes
+        uint4 cwc[R][CPL];
+        float scc[R][CPL];
 #pragma unroll
-    for (int g = 0; g < R; g++) {
-        int rr = g * RPW + rsub;
-        rr = rr <= last ? rr : last;
-#pragma unroll
-        for (int j = 0; j < CPL; j++) {
-            int c = sub + LPR * j;
-            int cc = (FULLK || c < cpr) ? c : 0;
-            cw[g][j] = load_stream16(cbase + ((uint32_t)rr * row_bytes + (uint32_t)cc * 16u));
-            if constexpr (FMT == INT4 || FMT == INT8) {
-                const uint16_t *s = reinterpret_cast<const uint16_t *>(plane) + row0 * nb;
-                int blk = (FMT == INT8) ? cc / 2 : cc;
-                sc[g][j] = f16_bits_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)blk]);
-            } else if constexpr (FMT == FP4) {
-                const uint8_t *s = reinterpret_cast<const uint8_t *>(plane) + row0 * nb;
-                sc[g][j] = e8m0_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)cc]);
-            } else {
-                sc[g][j] = 1.f;
-            }
-        }
-    }
-    _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
-    if constexpr (FMT == KM4) {
-        // stage this iteration's tables: 8 dwords per row
-        const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane) + row0 * 8;
-        uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
-#pragma unroll
-        for (int i0 = 0; i0 < ROWS_IT * 8; i0 += kWave) {
-            int i = i0 + lane;
-            if (ROWS_IT * 8 % kWave == 0 || i < ROWS_IT * 8) {
-                int rr = i / 8;
-                rr = rr <= last ? rr : last;
-                ldst[i] = lsrc[rr * 8 + (i % 8)];
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    float acc[R * BT];
-#pragma unroll
-    for (int g = 0; g < R; g++) {
-#pragma unroll
-        for (int b = 0; b < BT; b++) {
-            float a = 0.f;
+        for (int g = 0; g < R; g++)
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
-                float d;
-                if constexpr (FMT == INT4) d = chunk_dot_int4(cw[g][j], xr[j][b]);
-                else if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[g][j], xr[j][b]);
-                else if constexpr (FMT == INT8) d = chunk_dot_int8(cw[g][j], xr[j][b]);
-                else if constexpr (KM4_IMM)
-                    d = chunk_dot_km4_imm(cw[g][j], reinterpret_cast<const char *>(lut_lds) + g * 32, xr[j][b]);
-                else d = chunk_dot_km4(cw[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
-                a = (FMT == KM4) ? a + d : __builtin_fmaf(d, sc[g][j], a);
+                cwc[g][j] = cw[g][j];
+                scc[g][j] = sc[g][j];
             }
-            acc[g * BT + b] = a;
-        }
-    }
-    using Red = GroupReduce<R * BT, LPR>;
-    Red::run(acc, lane);
-    if (Red::writer(lane)) {
-        const int base = Red::base(lane);
+        _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
+        if constexpr (FMT == KM4) {
+            uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
 #pragma unroll
-        for (int j = 0; j < Red::live; j++) {
-            int idx = base + j, g = idx / BT, b = idx % BT;
-            int64_t row = row0 + g * RPW + rsub;
-            if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
+            for (int q = 0; q < LUT_PER_LANE; q++) {
+                int i = q * kWave + lane;
+                if (LUT_WORDS % kWave == 0 || i < LUT_WORDS) ldst[i] = lutv[q];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
-    }
-    if constexpr (FMT == KM4 && ITERS > 1) {
-        // the next iteration rewrites the tables: keep this iteration's reads above it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+        if (ITERS > 1 && it + 1 < ITERS && row0 + ROWS_IT < N) issue_loads(row0 + ROWS_IT);
+
+        float acc[R * BT];
+#pragma unroll
+        for (int g = 0; g < R; g++) {
+#pragma unroll
+            for (int b = 0; b < BT; b++) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < CPL; j++) {
+                    float d;
+                    if constexpr (FMT == INT4) d = chunk_dot_int4(cwc[g][j], xr[j][b]);
+                    else if constexpr (FMT == FP4) d = chunk_dot_fp4(cwc[g][j], xr[j][b]);
+                    else if constexpr (FMT == INT8) d = chunk_dot_int8(cwc[g][j], xr[j][b]);
+                    else if constexpr (KM4_IMM)
+                        d = chunk_dot_km4_imm(cwc[g][j], reinterpret_cast<const char *>(lut_lds) + g * 32, xr[j][b]);
+                    else d = chunk_dot_km4(cwc[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
+                    a = (FMT == KM4) ? a + d : __builtin_fmaf(d, scc[g][j], a);
+                }
+                acc[g * BT + b] = a;
+            }
+        }
+        if constexpr (FMT == KM4 && ITERS > 1) {
+            // the next iteration rewrites the tables: keep this iteration's reads above it
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        using Red = GroupReduce<R * BT, LPR>;
+        Red::run(acc, lane);
+        if (Red::writer(lane)) {
+            const int base = Red::base(lane);
+#pragma unroll
+            for (int j = 0; j < Red::live; j++) {
+                int idx = base + j, g = idx / BT, b = idx % BT;
+                int64_t row = row0 + g * RPW + rsub;
+                if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
+            }
+        }
     }
 }
 
@@ -279,7 +304,7 @@ static int grid_for_waves(int64_t waves_needed) {
 // amortize the x slices held in registers.
 template <int FMT, int BT> struct LaunchShape {
     static constexpr int R = (BT == 1) ? ((FMT == INT4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
-    static constexpr int ITERS = (FMT == KM4) ? ((BT == 1) ? 4 : (BT == 8 ? 16 : 2))
+    static constexpr int ITERS = (FMT == KM4) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
                                               : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
     static constexpr int WAVES = (FMT == KM4) ? 1 : 4;
 };
