@@ -64,7 +64,7 @@ def lib():
         L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
         L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
-        L.orc_moe_ffn.argtypes = [P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
+        L.orc_moe_ffn.argtypes = [ci, P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ci
         for f in ("orc_pack_fp4", "orc_pack_int4", "orc_pack_int8", "orc_pack_km4",
@@ -200,15 +200,16 @@ def moe_route(logits, topk: int):
     return ids, w
 
 
-def moe_ffn(gu_codes, gu_scale, dn_codes, dn_scale, x, ids, weights, return_h: bool = False):
-    """gu_*: [E, 2I, H/2] / [E, 2I, H/32]; dn_*: [E, H, I/2] / [E, H, I/32]."""
+def moe_ffn(gu_codes, gu_plane, dn_codes, dn_plane, x, ids, weights, return_h: bool = False, fmt: str = "int4"):
+    """gu_*: E stacked [2I, H] matrices packed in `fmt` (codes [E, 2I, ...],
+    plane [E, 2I, ...]); dn_*: E stacked [H, I] matrices."""
     gu_codes = np.ascontiguousarray(gu_codes)
-    gu_scale = np.ascontiguousarray(gu_scale)
+    gu_plane = np.ascontiguousarray(gu_plane)
     dn_codes = np.ascontiguousarray(dn_codes)
-    dn_scale = np.ascontiguousarray(dn_scale)
-    E, I2, Hh = gu_codes.shape
-    I, H = I2 // 2, Hh * 2
-    assert dn_codes.shape == (E, H, I // 2)
+    dn_plane = np.ascontiguousarray(dn_plane)
+    E, I2 = gu_codes.shape[:2]
+    I, H = I2 // 2, _kdim(fmt, gu_codes[0])
+    assert dn_codes.shape[:2] == (E, H) and _kdim(fmt, dn_codes[0]) == I
     x = np.ascontiguousarray(np.atleast_2d(np.asarray(x)).astype(np.float64))
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     weights = np.ascontiguousarray(weights, dtype=np.float64)
@@ -216,6 +217,6 @@ def moe_ffn(gu_codes, gu_scale, dn_codes, dn_scale, x, ids, weights, return_h: b
     assert ids.min() >= 0 and ids.max() < E
     y = np.zeros((T, H), np.float64)
     h = np.zeros((T, topk, I), np.float64)
-    lib().orc_moe_ffn(_p(gu_codes), _p(gu_scale), _p(dn_codes), _p(dn_scale), E, H, I,
+    lib().orc_moe_ffn(FORMATS[fmt], _p(gu_codes), _p(gu_plane), _p(dn_codes), _p(dn_plane), E, H, I,
                       _p(x), T, topk, _p(ids), _p(weights), _p(h), _p(y))
     return (y, h) if return_h else y

@@ -467,13 +467,23 @@ void orc_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, do
     }
 }
 
+/* Bytes of one row of codes, and of one row of the scale / table plane,
+   for a K-long row in format fmt (0 int4, 1 fp4, 2 int8, 3 km4). */
+static int64_t code_row_bytes(int fmt, int64_t K) { return fmt == 2 ? K : K / 2; }
+static int64_t plane_row_bytes(int fmt, int64_t K)
+{
+    if (fmt == 1) return K / 32;      /* one e8m0 byte per block */
+    if (fmt == 3) return 32;          /* sixteen fp16 table entries */
+    return 2 * (K / 32);              /* one fp16 scale per block */
+}
+
 /* One token's expert FFN for every selected slot, then the weighted sum.
-   gu_codes/gu_scale: E experts of [2I][H] int4 (rows 0..I-1 gate, I..2I-1 up);
-   dn_codes/dn_scale: E experts of [H][I] int4.
+   gu_codes/gu_plane: E experts of [2I][H] in format fmt (rows 0..I-1 gate,
+   I..2I-1 up); dn_codes/dn_plane: E experts of [H][I].
    x: T x H (fp64 of fp16 inputs). h_out (may be NULL): T x topk x I, the fp16
    activations silu(g)*u rounded to fp16, as fp64. y: T x H in fp64. */
-void orc_moe_ffn(const uint8_t *gu_codes, const uint16_t *gu_scale,
-                 const uint8_t *dn_codes, const uint16_t *dn_scale,
+void orc_moe_ffn(int fmt, const void *gu_codes, const void *gu_plane,
+                 const void *dn_codes, const void *dn_plane,
                  int E, int64_t H, int64_t I,
                  const double *x, int T, int topk, const int32_t *ids, const double *weights,
                  double *h_out, double *y)
@@ -482,14 +492,14 @@ void orc_moe_ffn(const uint8_t *gu_codes, const uint16_t *gu_scale,
     double *h = malloc(sizeof(double) * I);
     double *g = malloc(sizeof(double) * 2 * I);
     double *part = malloc(sizeof(double) * H);
+    const uint8_t *gu_c = gu_codes, *gu_p = gu_plane, *dn_c = dn_codes, *dn_p = dn_plane;
     for (int t = 0; t < T; t++) {
         for (int64_t n = 0; n < H; n++)
             y[t * H + n] = 0.0;
         for (int j = 0; j < topk; j++) {
             int64_t e = ids[t * topk + j];
-            const uint8_t *gc = gu_codes + e * (2 * I) * (H / 2);
-            const uint16_t *gs = gu_scale + e * (2 * I) * (H / 32);
-            orc_matvec(0, gc, gs, 2 * I, H, x + t * H, 1, NULL, 0, g);
+            orc_matvec(fmt, gu_c + e * 2 * I * code_row_bytes(fmt, H), gu_p + e * 2 * I * plane_row_bytes(fmt, H),
+                       2 * I, H, x + t * H, 1, NULL, 0, g);
             for (int64_t i = 0; i < I; i++) {
                 double gate = g[i], up = g[I + i];
                 double silu = gate / (1.0 + exp(-gate));
@@ -497,9 +507,8 @@ void orc_moe_ffn(const uint8_t *gu_codes, const uint16_t *gu_scale,
                 if (h_out)
                     h_out[((int64_t)t * topk + j) * I + i] = h[i];
             }
-            const uint8_t *dc = dn_codes + e * H * (I / 2);
-            const uint16_t *ds = dn_scale + e * H * (I / 32);
-            orc_matvec(0, dc, ds, H, I, h, 1, NULL, 0, part);
+            orc_matvec(fmt, dn_c + e * H * code_row_bytes(fmt, I), dn_p + e * H * plane_row_bytes(fmt, I),
+                       H, I, h, 1, NULL, 0, part);
             for (int64_t n = 0; n < H; n++)
                 y[t * H + n] += weights[t * topk + j] * part[n];
         }

@@ -448,29 +448,35 @@ def test_moe_route_matches_numpy_sort_and_softmax():
     assert ids[2, 0] == 10 and ids[2, 1] == 200
 
 
-def _small_moe(seed=12, E=6, H=64, I=32):
+def _small_moe(seed=12, E=6, H=64, I=32, fmt="int4"):
     rng = np.random.default_rng(seed)
     gu = (rng.standard_normal((E * 2 * I, H)) * 0.02).astype(np.float16)
     dn = (rng.standard_normal((E * H, I)) * 0.02).astype(np.float16)
-    guc, gus = oracle.pack_int4(gu)
-    dnc, dns = oracle.pack_int4(dn)
-    return (guc.reshape(E, 2 * I, H // 2), gus.reshape(E, 2 * I, H // 32),
-            dnc.reshape(E, H, I // 2), dns.reshape(E, H, I // 32), rng)
+    guc, gus = oracle.pack(fmt, gu)
+    dnc, dns = oracle.pack(fmt, dn)
+    return (guc.reshape(E, 2 * I, -1), gus.reshape(E, 2 * I, -1),
+            dnc.reshape(E, H, -1), dns.reshape(E, H, -1), rng)
 
 
-def test_moe_top1_reduces_to_one_expert_ffn():
-    guc, gus, dnc, dns, rng = _small_moe()
-    E, I2, Hh = guc.shape
-    H, I = 2 * Hh, I2 // 2
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+def test_moe_top1_reduces_to_one_expert_ffn(fmt):
+    """One slot of weight 1 is that expert's SwiGLU FFN (numpy GEMVs over the
+    dequantized slabs); the last expert catches a wrong per-expert stride, and
+    two slots give the weighted sum of the two one-expert results."""
+    E, H, I = 6, 64, 32
+    guc, gus, dnc, dns, rng = _small_moe(E=E, H=H, I=I, fmt=fmt)
     x = rng.standard_normal((1, H)).astype(np.float16)
-    e = 4
-    y = oracle.moe_ffn(guc, gus, dnc, dns, x, np.array([[e]]), np.array([[1.0]]))
-    Wg = oracle.dequant("int4", guc[e], gus[e])
-    Wd = oracle.dequant("int4", dnc[e], dns[e])
-    g = Wg @ x[0].astype(np.float64)                  # numpy GEMV
-    h = (g[:I] / (1 + np.exp(-g[:I])) * g[I:]).astype(np.float16).astype(np.float64)
-    ref = Wd @ h
-    assert np.allclose(y[0], ref, rtol=1e-12, atol=1e-12)
+    refs = {}
+    for e in (1, E - 1):
+        y = oracle.moe_ffn(guc, gus, dnc, dns, x, np.array([[e]]), np.array([[1.0]]), fmt=fmt)
+        Wg = oracle.dequant(fmt, guc[e], gus[e])
+        Wd = oracle.dequant(fmt, dnc[e], dns[e])
+        g = Wg @ x[0].astype(np.float64)                  # numpy GEMV
+        h = (g[:I] / (1 + np.exp(-g[:I])) * g[I:]).astype(np.float16).astype(np.float64)
+        refs[e] = Wd @ h
+        assert np.allclose(y[0], refs[e], rtol=1e-12, atol=1e-12)
+    y2 = oracle.moe_ffn(guc, gus, dnc, dns, x, np.array([[E - 1, 1]]), np.array([[0.75, 0.25]]), fmt=fmt)
+    assert np.allclose(y2[0], 0.75 * refs[E - 1] + 0.25 * refs[1], rtol=1e-12, atol=1e-15)
 
 
 def test_moe_token_order_and_shared_experts():
