@@ -102,6 +102,32 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def timed_graph(fn, steps, per_graph=32):
+    """Mean ms per call with `per_graph` calls captured in one HIP graph and the
+    graph replayed (removes host launch overhead; for microsecond-scale ops)."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, steps // per_graph)
+    st = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        g.replay()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * per_graph)
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -226,8 +252,11 @@ def main():
             for fmt in ("km4", "fp4"):
                 p0 = qmv.qpack(fmt, Wq)
                 pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(127)]
-                msq = timed(lambda i: qmv.qmatvec(fmt, pk[i % 128][0], pk[i % 128][1], xq), args.steps, args.warmup)
+                yq = torch.empty((1, n), dtype=torch.float32, device="cuda")
+                msq = timed_graph(lambda i: qmv.qmatvec(fmt, pk[i % 128][0], pk[i % 128][1], xq, y=yq),
+                                  4 * args.steps, per_graph=128)
                 extras["%s_%s_us" % (name, fmt)] = round(msq * 1e3, 2)
+                extras["%s_%s_GBps" % (name, fmt)] = round(algo_bytes(fmt, n, k) / (msq * 1e-3) / 1e9, 1)
                 del pk
         if args.all:
             extras.update(bench_int8_head(args))
@@ -291,11 +320,26 @@ def bench_moe(args):
     for T in (1, 4, 8):
         x = torch.from_numpy(c.x[:T]).cuda()
         lg = torch.from_numpy(c.logits[:T]).cuda()
-        ms = timed(lambda i: qmv.moe_ffn(guc, gus, dnc, dns, x, lg, c.topk), args.steps // 2, args.warmup)
-        ids, _ = qmv.qmoe_route(lg, c.topk)
+        ids = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, c.topk), dtype=torch.float32, device="cuda")
+        h = torch.empty((T, c.topk, I), dtype=torch.float16, device="cuda")
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+        def layer(i):
+            qmv.qmoe_ffn("int4", guc, gus, dnc, dns, x, lg, c.topk, ids=ids, weights=w, h=h, y=y)
+
+        def layer3(i):
+            qmv.qmoe_route(lg, c.topk, ids=ids, weights=w)
+            qmv.gather_qmatvec("int4", guc, gus, x, ids, epi="swiglu", y=h)
+            qmv.gather_qmatvec("int4", dnc, dns, h, ids, weights=w, epi="combine", x_per_slot=True, y=y)
+
+        ms = timed_graph(layer, args.steps, per_graph=16)
+        ms3 = timed_graph(layer3, args.steps, per_graph=16)
         uniq = len(np.unique(ids.cpu().numpy()))
         out["moe_T%d_us" % T] = round(ms * 1e3, 2)
         out["moe_T%d_GBps" % T] = round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)
+        out["moe_T%d_3call_us" % T] = round(ms3 * 1e3, 2)
+        out["moe_T%d_experts" % T] = uniq
     return out
 
 

@@ -147,7 +147,8 @@ qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_
 qmv_status qmoe_route(const float *logits, int T, int E, int topk,
                       int32_t *ids, float *weights, void *stream);
 
-/* Bytes of workspace gather_qmatvec needs for these sizes (0 if none). */
+/* Bytes of workspace gather_qmatvec needs for these sizes (0 if none; the
+ * current kernels need none for any epilogue). */
 size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epilogue epi);
 
 /* Matvec against the experts chosen in ids, reading each chosen expert's
@@ -161,14 +162,36 @@ size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epi
  *                          [T][topk][N/2] = fp16(silu(gate) * up); N even.
  *  epi == QMV_EPI_COMBINE: y fp32 [T][N] = sum over slots of
  *                          weights[t][slot] * (W[ids[t][slot]] x)[n].
- * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096. The workspace must hold
- * gather_qmatvec_workspace_bytes(...) bytes, 256-byte aligned. */
+ * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096; 32 <= K <= 8192 (4096
+ * for INT8), K % 32 == 0. COMBINE sums the slots of a token in slot order,
+ * so the result does not depend on scheduling. The workspace, if
+ * gather_qmatvec_workspace_bytes(...) is nonzero, must hold that many
+ * bytes, 256-byte aligned; otherwise it may be NULL. */
 qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane,
                           int E, int64_t N, int64_t K,
                           const void *x, qmv_dtype xdt, int x_per_slot,
                           int T, int topk, const int32_t *ids, const float *weights,
                           qmv_epilogue epi, void *y, void *workspace, size_t ws_bytes,
                           void *stream);
+
+/* One decode MoE FFN layer: top-k routing (fused into the gate/up gather
+ * for T == 1, its own launch otherwise), the gate/up gather with the SwiGLU
+ * epilogue, then the down gather with the weighted combine [S1 sec. 1: routed experts' gather_qmm; S2 sec. 1:
+ * gate/up and down of the routed experts only; the SwiGLU FFN of the
+ * expert, silu(gate) * up, then down].
+ *  gu_codes/gu_plane: [E][2I][H] in `fmt`'s layout, gate rows [0, I) and
+ *                     up rows [I, 2I) of each expert.
+ *  dn_codes/dn_plane: [E][H][I].
+ *  logits [T][E] fp32; x [T][H] fp16.
+ *  Outputs: ids [T][topk] int32 and weights [T][topk] fp32 exactly as
+ *  qmoe_route; h [T][topk][I] fp16 = fp16(silu(gate) * up) per slot; y
+ *  [T][H] fp32 = sum over slots (in slot order) of weights * (W_down h).
+ * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096; H and I multiples of 32
+ * in [32, 8192] (4096 for INT8). Buffers must not overlap. */
+qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane,
+                    const void *dn_codes, const void *dn_plane, int E, int64_t H, int64_t I,
+                    const float *logits, const void *x, int T, int topk,
+                    int32_t *ids, float *weights, void *h, float *y, void *stream);
 
 /* ---------------------------------------------------------------------- */
 /* Measurement aid: read `bytes` (a multiple of 16) from buf with 128-bit   */

@@ -25,7 +25,7 @@ EPILOGUES = {"none": QMV_EPI_NONE, "swiglu": QMV_EPI_SWIGLU, "combine": QMV_EPI_
 # every symbol include/qmv.h declares
 EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4",
            "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qdequant",
-           "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec",
+           "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
            "qmv_stream_read_sink_words", "qmv_stream_read")
 
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "qmoe_route": ([P, ci, ci, ci, P, P, P], ci),
             "gather_qmatvec_workspace_bytes": ([ci, ci, ci, i64, ci], sz),
             "gather_qmatvec": ([ci, P, P, ci, i64, i64, P, ci, ci, ci, ci, P, P, ci, P, P, sz, P], ci),
+            "qmoe_ffn": ([ci, P, P, P, P, ci, i64, i64, P, P, ci, ci, P, P, P, P, P], ci),
             "qmv_stream_read_sink_words": ([sz], sz),
             "qmv_stream_read": ([P, sz, P, P], ci),
         }
@@ -235,8 +236,30 @@ def gather_qmatvec(fmt, codes, plane, x, ids, weights=None, epi="none", x_per_sl
     return y
 
 
+def qmoe_ffn(fmt, gu_codes, gu_plane, dn_codes, dn_plane, x, logits, topk, ids=None, weights=None, h=None,
+             y=None, stream=None):
+    """One decode MoE layer (routing, gate/up + SwiGLU, down + weighted combine).
+
+    gu_codes/gu_plane: [E, 2I, ...]; dn_codes/dn_plane: [E, H, ...]; x [T, H]
+    fp16; logits [T, E] fp32. Returns (y [T, H] fp32, ids, weights, h).
+    """
+    torch = _torch()
+    E, I2 = gu_codes.shape[0], gu_codes.shape[1]
+    H = dn_codes.shape[1]
+    I = I2 // 2
+    T = x.shape[0]
+    ids = _empty((T, topk), torch.int32, x) if ids is None else ids
+    weights = _empty((T, topk), torch.float32, x) if weights is None else weights
+    h = _empty((T, topk, I), torch.float16, x) if h is None else h
+    y = _empty((T, H), torch.float32, x) if y is None else y
+    _check("qmoe_ffn", lib().qmoe_ffn(
+        FORMATS[fmt], _ptr(gu_codes), _ptr(gu_plane), _ptr(dn_codes), _ptr(dn_plane), E, H, I,
+        _ptr(logits), _ptr(x), T, topk, _ptr(ids), _ptr(weights), _ptr(h), _ptr(y), _stream(stream)))
+    return y, ids, weights, h
+
+
 def moe_ffn(gu_codes, gu_scale, dn_codes, dn_scale, x, logits, topk, fmt="int4", stream=None):
-    """One decode MoE layer: route, gate/up + SwiGLU, down + weighted combine."""
+    """The same layer as three separate calls: route, gate/up + SwiGLU gather, down + combine gather."""
     ids, w = qmoe_route(logits, topk, stream=stream)
     h = gather_qmatvec(fmt, gu_codes, gu_scale, x, ids, epi="swiglu", stream=stream)
     return gather_qmatvec(fmt, dn_codes, dn_scale, h, ids, weights=w, epi="combine", x_per_slot=True,

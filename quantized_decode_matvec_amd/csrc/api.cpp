@@ -53,6 +53,9 @@ qmv_status check_mv(const void *codes, const void *plane, size_t plane_align, in
     return QMV_OK;
 }
 
+// largest K the expert gather handles: 256 chunks per row of codes
+int64_t gather_max_k(qmv_format f) { return f == QMV_INT8 ? 4096 : 8192; }
+
 size_t plane_alignment(qmv_format f) {
     switch (f) {
     case QMV_FP4: return 1;
@@ -173,7 +176,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
     if (xdt != QMV_F16) return QMV_E_DTYPE;
     if (!codes || !plane || !x || !ids || !y) return QMV_E_NULL;
     if (epi == QMV_EPI_COMBINE && !weights) return QMV_E_NULL;
-    if (E < 1 || E > 4096 || N < 1 || K < 32 || K % 32 != 0 || K > 8192) return QMV_E_SHAPE;
+    if (E < 1 || E > 4096 || N < 1 || K < 32 || K % 32 != 0 || K > gather_max_k(fmt)) return QMV_E_SHAPE;
     if (T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
     if (x_per_slot != 0 && x_per_slot != 1) return QMV_E_SHAPE;
     if (epi == QMV_EPI_SWIGLU && N % 2 != 0) return QMV_E_SHAPE;
@@ -186,6 +189,24 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
         return QMV_E_ALIGN;
     return launch_status(qmv::launch_gather(fmt, codes, plane, E, N, K, x, xdt, x_per_slot, T, topk, ids, weights,
                                             epi, y, workspace, as_stream(stream)));
+}
+
+qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane, const void *dn_codes,
+                    const void *dn_plane, int E, int64_t H, int64_t I, const float *logits, const void *x, int T,
+                    int topk, int32_t *ids, float *weights, void *h, float *y, void *stream) {
+    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (!gu_codes || !gu_plane || !dn_codes || !dn_plane || !logits || !x || !ids || !weights || !h || !y)
+        return QMV_E_NULL;
+    if (E < 1 || E > 4096 || T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
+    const int64_t kmax = gather_max_k(fmt);
+    if (H < 32 || H % 32 != 0 || H > kmax || I < 32 || I % 32 != 0 || I > kmax) return QMV_E_SHAPE;
+    const size_t pa = plane_alignment(fmt);
+    if (!aligned(gu_codes, 16) || !aligned(dn_codes, 16) || !aligned(gu_plane, pa) || !aligned(dn_plane, pa) ||
+        !aligned(logits, 4) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(h, 16) ||
+        !aligned(y, 4))
+        return QMV_E_ALIGN;
+    return launch_status(qmv::launch_moe_ffn(fmt, gu_codes, gu_plane, dn_codes, dn_plane, E, H, I, logits, x, T,
+                                             topk, ids, weights, h, y, as_stream(stream)));
 }
 
 size_t qmv_stream_read_sink_words(size_t bytes) { return qmv::stream_read_grid(bytes); }

@@ -4,96 +4,137 @@
 // coverage + flagship Qwen3.6-35B...", section 1: only the routed experts'
 // weights are read, avoiding the all-experts over-read).
 //
-// gfx950 design. Decode moves at most T*topk experts; each workgroup works
-// on one (unique expert, row tile) pair. The expert list is rebuilt in every
-// workgroup from the T*topk ids (at most 64 entries, a few hundred cycles),
-// so there is no separate bucketing launch and no host synchronization. The
-// tokens that chose an expert are processed against the same weight tile,
-// so a chosen expert's bytes come from HBM once; a second pair of tokens
-// re-reads the tile from L2. SwiGLU is fused into the gate/up pass; the
-// down pass writes one fp32 row per (token, slot) and a small combine
-// kernel sums the slots in slot order, so results are deterministic.
+// gfx950 design. Decode touches at most T*topk experts and is latency-bound
+// at small T, so the layer is two launches:
+//  1. gate/up + SwiGLU, expert-major: each workgroup takes one (unique
+//     expert, row tile). The unique-expert list is rebuilt in the workgroup
+//     from the T*topk ids (an LDS bitmap and wave ballots), so a chosen
+//     expert's weights are read once however many tokens chose it. For a
+//     single token the routing is fused in: every workgroup routes the token
+//     itself (DPP reductions over registers) and workgroup (0,0) publishes
+//     ids and weights for launch 2; for more tokens a small routing launch
+//     runs first.
+//  2. down + weighted combine, token-major: each workgroup takes one (token,
+//     row tile) and walks the token's slots in slot order, accumulating
+//     w * (W_down[e] h) in registers. No partial buffer, no combine launch,
+//     and the sum order is fixed, so results are deterministic. An expert
+//     chosen by several tokens is re-read from L2 / Infinity Cache.
 #include "qmv_device.h"
 #include "qmv_launch.h"
 
 namespace qmv {
 
+enum Epi { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_COMBINE = 2 };
+
 // ---------------------------------------------------------------------------
-// routing: one wave per token
+// routing
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// max over the wave, returned in every lane (DPP within 16-lane rows, then
+// the four row results read into scalars)
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_imov(int v) {
+    return __builtin_amdgcn_update_dpp(0x7fffffff, v, CTRL, 0xF, 0xF, false);
+}
+
+// min over the wave of a non-negative int, returned in every lane
+__device__ __forceinline__ int wave_min(int v) {
+    v = min(v, dpp_imov<0xB1>(v));
+    v = min(v, dpp_imov<0x4E>(v));
+    v = min(v, dpp_imov<0x141>(v));
+    v = min(v, dpp_imov<0x140>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// Top-k of one token's E logits, largest first, equal logits in increasing
+// expert order; softmax over the selected logits. Lane j < topk returns the
+// j-th id and weight. Lane l keeps logits l, l + 64, ... in registers.
+template <int PER_LANE>
+__device__ __forceinline__ void route_token(const float *__restrict__ l, int E, int topk, int lane, int &out_id,
+                                            float &out_w) {
+    float v[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; i++) {
+        int e = lane + 64 * i;
+        v[i] = l[e < E ? e : 0];
+    }
+    uint64_t taken = 0;
+    int my_i = 0;
+    float my_v = 0.f;
+    for (int j = 0; j < topk; j++) {
+        float best = -__builtin_inff();
+#pragma unroll
+        for (int i = 0; i < PER_LANE; i++)
+            if (lane + 64 * i < E && !((taken >> i) & 1ull)) best = fmaxf(best, v[i]);
+        const float m = wave_max(best);
+        // the lowest untaken expert id holding the maximum
+        int cand = 0x7fffffff;
+#pragma unroll
+        for (int i = PER_LANE - 1; i >= 0; i--)
+            if (lane + 64 * i < E && !((taken >> i) & 1ull) && v[i] == m) cand = lane + 64 * i;
+        const int sel = wave_min(cand);
+        if ((sel & 63) == lane) taken |= 1ull << (sel >> 6);
+        if (lane == j) {
+            my_i = sel;
+            my_v = m;
+        }
+    }
+    const float vmax = readlane_f(my_v, 0);
+    const float p = lane < topk ? expf(my_v - vmax) : 0.f;
+    const float z = wave_sum(p);
+    out_id = my_i;
+    out_w = p / z;
+}
+
+constexpr int route_per_lane(int E) { return E <= 256 ? 4 : (E <= 1024 ? 16 : 64); }
+
+template <int PER_LANE>
 __global__ __launch_bounds__(256) void route_kernel(const float *__restrict__ logits, int T, int E, int topk,
                                                     int32_t *__restrict__ ids, float *__restrict__ weights) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *l = logits + (int64_t)t * E;
-    uint64_t taken = 0;
-    float my_v = 0.f;
-    int my_i = 0;
-    for (int j = 0; j < topk; j++) {
-        float bv = -__builtin_inff();
-        int bi = 0x7fffffff;
-        for (int i = 0; lane + 64 * i < E; i++) {
-            int e = lane + 64 * i;
-            if (taken & (1ull << i)) continue;
-            float v = l[e];
-            if (v > bv || (v == bv && e < bi)) {
-                bv = v;
-                bi = e;
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            float ov = __shfl_xor(bv, m);
-            int oi = __shfl_xor(bi, m);
-            if (ov > bv || (ov == bv && oi < bi)) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-        if (lane == j) {
-            my_v = bv;
-            my_i = bi;
-        }
-    }
-    const float vmax = __shfl(my_v, 0);
-    float p = lane < topk ? expf(my_v - vmax) : 0.f;
-    float z = p;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) z += __shfl_xor(z, m);
+    int id;
+    float w;
+    route_token<PER_LANE>(logits + (int64_t)t * E, E, topk, lane, id, w);
     if (lane < topk) {
-        ids[(int64_t)t * topk + lane] = my_i;
-        weights[(int64_t)t * topk + lane] = p / z;
+        ids[(int64_t)t * topk + lane] = id;
+        weights[(int64_t)t * topk + lane] = w;
     }
 }
 
 hipError_t launch_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, float *weights,
                             hipStream_t st) {
-    hipLaunchKernelGGL(route_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, topk, ids, weights);
+    const int pl = route_per_lane(E);
+    if (pl == 4)
+        hipLaunchKernelGGL(route_kernel<4>, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, topk, ids, weights);
+    else if (pl == 16)
+        hipLaunchKernelGGL(route_kernel<16>, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, topk, ids, weights);
+    else
+        hipLaunchKernelGGL(route_kernel<64>, dim3((T + 3) / 4), dim3(256), 0, st, logits, T, E, topk, ids, weights);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// gather matvec
+// shared pieces
 // ---------------------------------------------------------------------------
-enum Epi { EPI_NONE = 0, EPI_SWIGLU = 1, EPI_COMBINE = 2 };
-
-struct GatherArgs {
-    const uint8_t *codes;
-    const void *plane;
-    int E;
-    int64_t N;          // rows per expert
-    int K;
-    const _Float16 *x;
-    int x_per_slot;
-    int T, topk;
-    const int32_t *ids;
-    void *out;          // NONE/COMBINE: fp32 rows per pair; SWIGLU: fp16 rows per pair
-    int64_t out_rows;   // logical rows per pair (N, or N/2 for SWIGLU)
-    int tile_rows;      // logical rows per workgroup
-};
-
 template <int FMT>
 __device__ __forceinline__ float plane_scale(const void *plane, int64_t row, int nb, int c) {
     if constexpr (FMT == INT4 || FMT == INT8) {
@@ -106,9 +147,67 @@ __device__ __forceinline__ float plane_scale(const void *plane, int64_t row, int
     }
 }
 
+template <int FMT>
+__device__ __forceinline__ int64_t code_row_bytes(int K) { return (FMT == INT8) ? K : K / 2; }
+
+// expert e's code and plane slabs
+template <int FMT>
+__device__ __forceinline__ void expert_slabs(const uint8_t *codes, const void *plane, int64_t e, int64_t N, int K,
+                                             const uint8_t *&codes_e, const void *&plane_e) {
+    codes_e = codes + e * N * code_row_bytes<FMT>(K);
+    if constexpr (FMT == FP4)
+        plane_e = reinterpret_cast<const uint8_t *>(plane) + e * N * (K / 32);
+    else if constexpr (FMT == KM4)
+        plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * 16;
+    else
+        plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * (K / 32);
+}
+
+template <int FMT>
+__device__ __forceinline__ float chunk_dot(uint4 cw, const uint32_t (&xw)[ChunkTraits<FMT>::kXWords],
+                                           const _Float16 *lut) {
+    if constexpr (FMT == INT4) return chunk_dot_int4(cw, xw);
+    else if constexpr (FMT == FP4) return chunk_dot_fp4(cw, xw);
+    else if constexpr (FMT == INT8) return chunk_dot_int8(cw, xw);
+    else return chunk_dot_km4(cw, lut, xw);
+}
+
+__device__ __forceinline__ void wave_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct GatherArgs {
+    const uint8_t *codes;
+    const void *plane;
+    int E;
+    int64_t N;          // rows per expert
+    int K;
+    const _Float16 *x;
+    int x_per_slot;
+    int T, topk;
+    const int32_t *ids;
+    const float *weights;
+    const float *logits;  // fused routing: logits [T][E]; ids/weights are then outputs
+    int32_t *ids_out;
+    float *weights_out;
+    void *out;
+    int64_t out_rows;   // logical rows per pair (N, or N/2 for SWIGLU)
+    int tile_rows;      // logical rows per workgroup
+};
+
+// ---------------------------------------------------------------------------
+// expert-major gather (NONE, SWIGLU)
+// ---------------------------------------------------------------------------
 // One pass over the workgroup's row tile for PB token slots (pairs).
 // R row groups per wave iteration; with SWIGLU the first R/2 groups are gate
-// rows and the last R/2 the matching up rows.
+// rows and the last R/2 the matching up rows. Loads are unconditional (rows
+// clamped into the tile, chunks past the row end read chunk 0 against a zero
+// x slice) and stream past the caches. An expert chosen by more than two
+// tokens is read once per pass; keeping its codes in registers across passes
+// instead costs more registers (fewer resident waves) than it saves, since
+// most chosen experts have one or two slots in a decode batch.
 template <int FMT, int PB, int LPR, int CPL, int R, int EPI>
 __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *__restrict__ codes_e,
                                             const void *__restrict__ plane_e, const int *pairs,
@@ -124,7 +223,7 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
     const int K = a.K;
     const int cpr = (FMT == INT8) ? K / 16 : K / 32;
     const int nb = K / 32;
-    const int64_t row_bytes = (FMT == INT8) ? K : K / 2;
+    const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
 
     uint32_t xr[CPL][PB][XW];
 #pragma unroll
@@ -143,21 +242,19 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
     for (int64_t l0 = tile0 + (int64_t)wave * LROWS; l0 < tile1; l0 += 4 * LROWS) {
         uint4 cw[R][CPL];
         float sc[R][CPL];
-        int64_t prow[R];
-        bool rvalid[R];
 #pragma unroll
         for (int g = 0; g < R; g++) {
             int gl = (EPI == EPI_SWIGLU) ? (g % G) : g;
             int64_t lrow = l0 + gl * RPW + rsub;
-            rvalid[g] = lrow < tile1;
-            prow[g] = (EPI == EPI_SWIGLU && g >= G) ? lrow + a.out_rows : lrow;
-            const uint8_t *rp = codes_e + (rvalid[g] ? prow[g] : 0) * row_bytes;
+            lrow = lrow < tile1 ? lrow : tile1 - 1;
+            int64_t prow = (EPI == EPI_SWIGLU && g >= G) ? lrow + a.out_rows : lrow;
+            const uint8_t *rp = codes_e + prow * (int64_t)row_bytes;
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
                 int c = sub + LPR * j;
-                bool v = rvalid[g] && c < cpr;
-                cw[g][j] = v ? *reinterpret_cast<const uint4 *>(rp + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
-                sc[g][j] = v ? plane_scale<FMT>(plane_e, prow[g], nb, c) : 0.f;
+                int cc = c < cpr ? c : 0;
+                cw[g][j] = load_stream16(rp + (uint32_t)cc * 16u);
+                sc[g][j] = plane_scale<FMT>(plane_e, prow, nb, cc);
             }
         }
         if constexpr (FMT == KM4) {
@@ -167,62 +264,66 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
                 int g = i / (RPW * 8), rs = (i / 8) % RPW;
                 int gl = (EPI == EPI_SWIGLU) ? (g % G) : g;
                 int64_t lrow = l0 + gl * RPW + rs;
+                lrow = lrow < tile1 ? lrow : tile1 - 1;
                 int64_t pr = (EPI == EPI_SWIGLU && g >= G) ? lrow + a.out_rows : lrow;
-                ldst[i] = lrow < tile1 ? lsrc[pr * 8 + (i % 8)] : 0u;
+                ldst[i] = lsrc[pr * 8 + (i % 8)];
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_fence();
         }
-        float acc[R][PB];
+        float acc[R * PB];
 #pragma unroll
         for (int g = 0; g < R; g++)
 #pragma unroll
-            for (int p = 0; p < PB; p++) acc[g][p] = 0.f;
+            for (int p = 0; p < PB; p++) {
+                float s = 0.f;
 #pragma unroll
-        for (int g = 0; g < R; g++)
-#pragma unroll
-            for (int j = 0; j < CPL; j++)
-#pragma unroll
-                for (int p = 0; p < PB; p++) {
-                    float d;
-                    if constexpr (FMT == INT4) d = chunk_dot_int4(cw[g][j], xr[j][p]);
-                    else if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[g][j], xr[j][p]);
-                    else if constexpr (FMT == INT8) d = chunk_dot_int8(cw[g][j], xr[j][p]);
-                    else d = chunk_dot_km4(cw[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][p]);
-                    acc[g][p] = __builtin_fmaf(d, sc[g][j], acc[g][p]);
+                for (int j = 0; j < CPL; j++) {
+                    float d = chunk_dot<FMT>(cw[g][j], xr[j][p], lut_w + (g * RPW + rsub) * 16);
+                    s = (FMT == KM4) ? s + d : __builtin_fmaf(d, sc[g][j], s);
                 }
-        if constexpr (FMT == KM4) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
+                acc[g * PB + p] = s;
+            }
+        if constexpr (FMT == KM4) wave_fence();   // the next iteration rewrites the tables
+        if constexpr (EPI == EPI_SWIGLU) {
+            // full reduction: every lane gets every row sum, so each gate sum
+            // meets its up sum (group g + G) in the same lane
 #pragma unroll
-        for (int g = 0; g < R; g++)
+            for (int q = 0; q < R * PB; q++) {
+                float v = row16_sum(acc[q]);
+                if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
+                if constexpr (LPR == 64) v += __shfl_xor(v, 32);
+                acc[q] = v;
+            }
+            if (sub == 0) {
 #pragma unroll
-            for (int p = 0; p < PB; p++) acc[g][p] = group_sum<LPR>(acc[g][p]);
-        if (sub == 0) {
+                for (int g = 0; g < G; g++) {
+                    int64_t lrow = l0 + g * RPW + rsub;
+                    if (lrow >= tile1) continue;
 #pragma unroll
-            for (int g = 0; g < G; g++) {
-                int64_t lrow = l0 + g * RPW + rsub;
-                if (lrow >= tile1) continue;
-#pragma unroll
-                for (int p = 0; p < PB; p++) {
-                    int64_t o = (int64_t)pairs[p] * a.out_rows + lrow;
-                    if constexpr (EPI == EPI_SWIGLU) {
-                        float gt = acc[g][p], up = acc[g + G][p];
+                    for (int p = 0; p < PB; p++) {
+                        float gt = acc[g * PB + p], up = acc[(g + G) * PB + p];
                         float h = gt / (1.0f + expf(-gt)) * up;
-                        reinterpret_cast<_Float16 *>(a.out)[o] = (_Float16)h;
-                    } else {
-                        reinterpret_cast<float *>(a.out)[o] = acc[g][p];
+                        reinterpret_cast<_Float16 *>(a.out)[(int64_t)pairs[p] * a.out_rows + lrow] = (_Float16)h;
                     }
+                }
+            }
+        } else {
+            using Red = GroupReduce<R * PB, LPR>;
+            Red::run(acc, lane);
+            if (Red::writer(lane)) {
+                const int base = Red::base(lane);
+#pragma unroll
+                for (int j = 0; j < Red::live; j++) {
+                    int idx = base + j, g = idx / PB, p = idx % PB;
+                    int64_t lrow = l0 + g * RPW + rsub;
+                    if (lrow < tile1) reinterpret_cast<float *>(a.out)[(int64_t)pairs[p] * a.out_rows + lrow] = acc[j];
                 }
             }
         }
     }
 }
 
-template <int FMT, int LPR, int CPL, int R, int EPI>
+template <int FMT, int LPR, int CPL, int R, int EPI, bool FUSED_ROUTE, int ROUTE_PL>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     constexpr int RPW = kWave / LPR;
     __shared__ int s_ids[512];
@@ -232,13 +333,31 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     __shared__ int s_expert;
     __shared__ _Float16 lut_lds[(FMT == KM4) ? 4 * R * RPW * 16 : 1];
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int npairs = a.T * a.topk;
     const int u = blockIdx.y;
     for (int i = tid; i < 128; i += blockDim.x) s_bits[i] = 0;
+    if constexpr (FUSED_ROUTE) {
+        // route the tokens here: wave w takes tokens w, w + 4
+        const bool publish = blockIdx.x == 0 && blockIdx.y == 0;
+        for (int t = tid >> 6; t < a.T; t += 4) {
+            int id;
+            float w;
+            route_token<ROUTE_PL>(a.logits + (int64_t)t * a.E, a.E, a.topk, lane, id, w);
+            if (lane < a.topk) {
+                s_ids[t * a.topk + lane] = id;
+                if (publish) {
+                    a.ids_out[t * a.topk + lane] = id;
+                    a.weights_out[t * a.topk + lane] = w;
+                }
+            }
+        }
+    } else {
+        for (int i = tid; i < npairs; i += blockDim.x) s_ids[i] = a.ids[i];
+    }
     __syncthreads();
     for (int i = tid; i < npairs; i += blockDim.x) {
-        int e = a.ids[i];
-        s_ids[i] = e;
+        int e = s_ids[i];
         atomicOr(&s_bits[e >> 5], 1u << (e & 31));
     }
     __syncthreads();
@@ -256,24 +375,28 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
             before += c;
         }
         s_expert = found;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // token slots that chose this expert, in slot order, via wave ballots
+        const int e = s_expert;
         int np = 0;
-        for (int i = 0; i < npairs && found >= 0; i++)
-            if (s_ids[i] == found && np < 8) s_pairs[np++] = i;
-        s_np = np;
+        for (int base = 0; base < npairs && e >= 0; base += 64) {
+            int i = base + tid;
+            uint64_t m = __ballot(i < npairs && s_ids[i] == e);
+            int before = __builtin_popcountll(m & ((1ull << tid) - 1));
+            if (((m >> tid) & 1ull) && np + before < 8) s_pairs[np + before] = i;
+            np += __builtin_popcountll(m);
+        }
+        if (tid == 0) s_np = np < 8 ? np : 8;
     }
     __syncthreads();
     const int e = s_expert;
     if (e < 0) return;
     const int np = s_np;
-    const int64_t row_bytes = (FMT == INT8) ? a.K : a.K / 2;
-    const uint8_t *codes_e = a.codes + (int64_t)e * a.N * row_bytes;
+    const uint8_t *codes_e;
     const void *plane_e;
-    if constexpr (FMT == FP4)
-        plane_e = reinterpret_cast<const uint8_t *>(a.plane) + (int64_t)e * a.N * (a.K / 32);
-    else if constexpr (FMT == KM4)
-        plane_e = reinterpret_cast<const uint16_t *>(a.plane) + (int64_t)e * a.N * 16;
-    else
-        plane_e = reinterpret_cast<const uint16_t *>(a.plane) + (int64_t)e * a.N * (a.K / 32);
+    expert_slabs<FMT>(a.codes, a.plane, e, a.N, a.K, codes_e, plane_e);
     _Float16 *lut_w = lut_lds + (tid >> 6) * R * RPW * 16;
     int p0 = 0;
     for (; p0 + 2 <= np; p0 += 2)
@@ -281,61 +404,211 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     if (p0 < np) gather_pass<FMT, 1, LPR, CPL, R, EPI>(a, codes_e, plane_e, s_pairs + p0, lut_w);
 }
 
-// y[t][n] = sum over slots (in order) of weights[t][slot] * part[t*topk+slot][n]
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part, const float *__restrict__ w,
-                                                      int T, int topk, int64_t N, float *__restrict__ y) {
-    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)T * N) return;
-    int t = (int)(gid / N);
-    int64_t n = gid % N;
-    float acc = 0.f;
-    for (int s = 0; s < topk; s++) acc = __builtin_fmaf(w[t * topk + s], part[((int64_t)t * topk + s) * N + n], acc);
-    y[gid] = acc;
+// ---------------------------------------------------------------------------
+// token-major down projection with the weighted combine fused
+//   y[t][n] = sum over slots s (in order) of w[t][s] * (W[ids[t][s]] x_{t,s})[n]
+// One wave per workgroup; the wave owns ROWS = R * (64 / LPR) rows of token t.
+// The slots are taken in batches of SB: the codes, scales and x slices of
+// every slot of a batch are loaded at once, so the wave waits for one memory
+// round trip per batch instead of one per slot.
+// ---------------------------------------------------------------------------
+template <int FMT, int R, int CPL>
+constexpr int combine_slot_batch() {
+    constexpr int per_slot = 5 * R * CPL + ChunkTraits<FMT>::kXWords * CPL + (FMT == KM4 ? 1 : 0);
+    constexpr int sb = 192 / per_slot;
+    return sb < 1 ? 1 : (sb > 8 ? 8 : sb);
 }
 
-size_t gather_workspace_bytes(int T, int topk, int E, int64_t N, int epi) {
-    (void)E;
-    if (epi != EPI_COMBINE) return 0;
-    return (size_t)T * topk * N * sizeof(float);
+template <int FMT, int LPR, int CPL, int R, int SB>
+__global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
+    constexpr int RPW = kWave / LPR;
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    constexpr int ROWS = R * RPW;
+    __shared__ _Float16 lut_lds[(FMT == KM4) ? SB * ROWS * 16 : 1];
+    const int lane = threadIdx.x;
+    const int sub = lane % LPR;
+    const int rsub = lane / LPR;
+    const int t = blockIdx.y;
+    const int K = a.K;
+    const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+    const int nb = K / 32;
+    const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
+    const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+    if (row0 >= a.N) return;
+    const int last = (int)((a.N - 1 - row0) < ROWS - 1 ? (a.N - 1 - row0) : ROWS - 1);
+
+    float acc[R];
+#pragma unroll
+    for (int g = 0; g < R; g++) acc[g] = 0.f;
+    for (int s0 = 0; s0 < a.topk; s0 += SB) {
+        uint4 cw[SB][R][CPL];
+        float sc[SB][R][CPL];
+        uint32_t xr[SB][CPL][XW];
+        float ws[SB];
+        uint32_t lutv[SB];
+#pragma unroll
+        for (int b = 0; b < SB; b++) {
+            // slots past topk repeat the last one with weight 0
+            const int s = s0 + b < a.topk ? s0 + b : a.topk - 1;
+            const int e = a.ids[t * a.topk + s];
+            ws[b] = s0 + b < a.topk ? a.weights[t * a.topk + s] : 0.f;
+            const uint8_t *codes_e;
+            const void *plane_e;
+            expert_slabs<FMT>(a.codes, a.plane, e, a.N, K, codes_e, plane_e);
+#pragma unroll
+            for (int g = 0; g < R; g++) {
+                int rr = g * RPW + rsub;
+                rr = rr <= last ? rr : last;
+                const int64_t row = row0 + rr;
+#pragma unroll
+                for (int j = 0; j < CPL; j++) {
+                    int c = sub + LPR * j;
+                    int cc = c < cpr ? c : 0;
+                    cw[b][g][j] = load_stream16(codes_e + row * (int64_t)row_bytes + (uint32_t)cc * 16u);
+                    sc[b][g][j] = plane_scale<FMT>(plane_e, row, nb, cc);
+                }
+            }
+            const _Float16 *xp = a.x + (int64_t)(a.x_per_slot ? t * a.topk + s : t) * K;
+#pragma unroll
+            for (int j = 0; j < CPL; j++) {
+                int c = sub + LPR * j;
+                load_x_slice<FMT>(xp, c, c < cpr, xr[b][j]);
+            }
+            if constexpr (FMT == KM4) {
+                int rr = (lane / 8) % ROWS;
+                rr = rr <= last ? rr : last;
+                lutv[b] = reinterpret_cast<const uint32_t *>(plane_e)[(row0 + rr) * 8 + (lane % 8)];
+            }
+        }
+        if constexpr (FMT == KM4) {
+#pragma unroll
+            for (int b = 0; b < SB; b++)
+                if (lane < ROWS * 8) reinterpret_cast<uint32_t *>(lut_lds)[b * ROWS * 8 + lane] = lutv[b];
+            wave_fence();
+        }
+#pragma unroll
+        for (int b = 0; b < SB; b++)
+#pragma unroll
+            for (int g = 0; g < R; g++)
+#pragma unroll
+                for (int j = 0; j < CPL; j++) {
+                    float d = chunk_dot<FMT>(cw[b][g][j], xr[b][j], lut_lds + (b * ROWS + g * RPW + rsub) * 16);
+                    acc[g] = __builtin_fmaf(d, ws[b] * sc[b][g][j], acc[g]);
+                }
+        if constexpr (FMT == KM4) wave_fence();   // the next batch rewrites the tables
+    }
+    using Red = GroupReduce<R, LPR>;
+    Red::run(acc, lane);
+    if (Red::writer(lane)) {
+        const int base = Red::base(lane);
+#pragma unroll
+        for (int j = 0; j < Red::live; j++) {
+            int64_t row = row0 + (base + j) * RPW + rsub;
+            if (row < a.N) reinterpret_cast<float *>(a.out)[(int64_t)t * a.N + row] = acc[j];
+        }
+    }
 }
 
-template <int FMT, int LPR, int CPL, int EPI>
-static hipError_t launch_gather_t(GatherArgs a, int umax, hipStream_t st) {
-    constexpr int R = (EPI == EPI_SWIGLU) ? 4 : 2;
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+size_t gather_workspace_bytes(int, int, int, int64_t, int) { return 0; }
+
+template <int FMT, int LPR, int CPL, int EPI, bool FUSED>
+static hipError_t launch_expert_major(GatherArgs a, int umax, hipStream_t st) {
+    // gate and up rows in pairs; fewer rows per iteration on long rows (and
+    // for table lookups, which hold more registers) to stay within the
+    // register file
+    constexpr int heavy = (FMT == KM4) ? CPL + 1 : CPL;
+    constexpr int R = (EPI == EPI_SWIGLU) ? (heavy >= 3 ? 2 : 4) : (heavy >= 3 ? 1 : 2);
     constexpr int RPW = kWave / LPR;
     constexpr int G = (EPI == EPI_SWIGLU) ? R / 2 : R;
-    // each wave takes two iterations of its tile
-    a.tile_rows = 4 * G * RPW * 2;
+    // one iteration per wave: many small workgroups keep every load in flight
+    a.tile_rows = 4 * G * RPW;
     int tiles = (int)((a.out_rows + a.tile_rows - 1) / a.tile_rows);
-    hipLaunchKernelGGL((gather_kernel<FMT, LPR, CPL, R, EPI>), dim3(tiles, umax), dim3(256), 0, st, a);
+    if constexpr (!FUSED) {
+        hipLaunchKernelGGL((gather_kernel<FMT, LPR, CPL, R, EPI, false, 4>), dim3(tiles, umax), dim3(256), 0, st, a);
+    } else {
+        const int pl = route_per_lane(a.E);
+        if (pl == 4)
+            hipLaunchKernelGGL((gather_kernel<FMT, LPR, CPL, R, EPI, true, 4>), dim3(tiles, umax), dim3(256), 0, st, a);
+        else if (pl == 16)
+            hipLaunchKernelGGL((gather_kernel<FMT, LPR, CPL, R, EPI, true, 16>), dim3(tiles, umax), dim3(256), 0, st,
+                               a);
+        else
+            hipLaunchKernelGGL((gather_kernel<FMT, LPR, CPL, R, EPI, true, 64>), dim3(tiles, umax), dim3(256), 0, st,
+                               a);
+    }
     return hipGetLastError();
 }
 
-template <int FMT, int EPI>
-static hipError_t launch_gather_shape(GatherArgs a, int umax, bool *handled, hipStream_t st) {
+template <int FMT, int LPR, int CPL>
+static hipError_t launch_token_major(GatherArgs a, hipStream_t st) {
+    constexpr int R = (LPR == 64) ? 4 : 1;
+    constexpr int ROWS = R * (kWave / LPR);
+    // few tokens: few waves, so each takes as many slots per round trip as
+    // registers allow; more tokens: smaller batches keep more waves resident
+    constexpr int SB_WIDE = combine_slot_batch<FMT, R, CPL>();
+    constexpr int SB_NARROW = SB_WIDE < 4 ? SB_WIDE : 4;
+    int tiles = (int)((a.N + ROWS - 1) / ROWS);
+    if (a.T <= 4)
+        hipLaunchKernelGGL((combine_gather_kernel<FMT, LPR, CPL, R, SB_WIDE>), dim3(tiles, a.T), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((combine_gather_kernel<FMT, LPR, CPL, R, SB_NARROW>), dim3(tiles, a.T), dim3(64), 0, st,
+                           a);
+    return hipGetLastError();
+}
+
+// dispatch on the row length: lanes per row and chunks per lane
+template <int FMT, int EPI, bool FUSED>
+static hipError_t launch_shape(GatherArgs a, int umax, bool *handled, hipStream_t st) {
     constexpr int E = ChunkTraits<FMT>::kElems;
     const int cpr = a.K / E;
     *handled = true;
-    if (cpr <= 16) return launch_gather_t<FMT, 16, 1, EPI>(a, umax, st);
-    if (cpr <= 32) return launch_gather_t<FMT, 32, 1, EPI>(a, umax, st);
-    if (cpr <= 64) return launch_gather_t<FMT, 64, 1, EPI>(a, umax, st);
-    if (cpr <= 128) return launch_gather_t<FMT, 64, 2, EPI>(a, umax, st);
-    if (cpr <= 192) return launch_gather_t<FMT, 64, 3, EPI>(a, umax, st);
-    if (cpr <= 256) return launch_gather_t<FMT, 64, 4, EPI>(a, umax, st);
+    if constexpr (EPI == EPI_COMBINE) {
+        (void)umax;
+        if (cpr <= 16) return launch_token_major<FMT, 16, 1>(a, st);
+        if (cpr <= 32) return launch_token_major<FMT, 32, 1>(a, st);
+        if (cpr <= 64) return launch_token_major<FMT, 64, 1>(a, st);
+        if (cpr <= 128) return launch_token_major<FMT, 64, 2>(a, st);
+        if (cpr <= 192) return launch_token_major<FMT, 64, 3>(a, st);
+        if (cpr <= 256) return launch_token_major<FMT, 64, 4>(a, st);
+    } else {
+        if (cpr <= 16) return launch_expert_major<FMT, 16, 1, EPI, FUSED>(a, umax, st);
+        if (cpr <= 32) return launch_expert_major<FMT, 32, 1, EPI, FUSED>(a, umax, st);
+        if (cpr <= 64) return launch_expert_major<FMT, 64, 1, EPI, FUSED>(a, umax, st);
+        if (cpr <= 128) return launch_expert_major<FMT, 64, 2, EPI, FUSED>(a, umax, st);
+        if (cpr <= 192) return launch_expert_major<FMT, 64, 3, EPI, FUSED>(a, umax, st);
+        if (cpr <= 256) return launch_expert_major<FMT, 64, 4, EPI, FUSED>(a, umax, st);
+    }
     *handled = false;
     return hipSuccess;
 }
 
 template <int FMT>
-static hipError_t launch_gather_fmt(GatherArgs a, int epi, int umax, bool *handled, hipStream_t st) {
-    if (epi == EPI_SWIGLU) return launch_gather_shape<FMT, EPI_SWIGLU>(a, umax, handled, st);
-    return launch_gather_shape<FMT, EPI_NONE>(a, umax, handled, st);
+static hipError_t launch_fmt(GatherArgs a, int epi, bool fused, int umax, bool *handled, hipStream_t st) {
+    if (epi == EPI_COMBINE) return launch_shape<FMT, EPI_COMBINE, false>(a, umax, handled, st);
+    if (epi == EPI_SWIGLU)
+        return fused ? launch_shape<FMT, EPI_SWIGLU, true>(a, umax, handled, st)
+                     : launch_shape<FMT, EPI_SWIGLU, false>(a, umax, handled, st);
+    return launch_shape<FMT, EPI_NONE, false>(a, umax, handled, st);
 }
 
-hipError_t launch_gather(int fmt, const void *codes, const void *plane, int E, int64_t N, int64_t K, const void *x,
-                         qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids, const float *weights,
-                         int epi, void *y, void *workspace, hipStream_t st) {
-    (void)xdt;
+static hipError_t launch_any(int fmt, GatherArgs a, int epi, bool fused, int umax, hipStream_t st) {
+    bool handled = false;
+    hipError_t err;
+    switch (fmt) {
+    case INT4: err = launch_fmt<INT4>(a, epi, fused, umax, &handled, st); break;
+    case FP4: err = launch_fmt<FP4>(a, epi, fused, umax, &handled, st); break;
+    case INT8: err = launch_fmt<INT8>(a, epi, fused, umax, &handled, st); break;
+    default: err = launch_fmt<KM4>(a, epi, fused, umax, &handled, st); break;
+    }
+    if (err != hipSuccess) return err;
+    return handled ? hipSuccess : hipErrorInvalidValue;
+}
+
+static GatherArgs make_args(const void *codes, const void *plane, int E, int64_t N, int64_t K, const void *x,
+                            int x_per_slot, int T, int topk, const int32_t *ids, const float *weights, void *out) {
     GatherArgs a;
     a.codes = reinterpret_cast<const uint8_t *>(codes);
     a.plane = plane;
@@ -347,28 +620,52 @@ hipError_t launch_gather(int fmt, const void *codes, const void *plane, int E, i
     a.T = T;
     a.topk = topk;
     a.ids = ids;
-    a.out = (epi == EPI_COMBINE) ? workspace : y;
-    a.out_rows = (epi == EPI_SWIGLU) ? N / 2 : N;
+    a.weights = weights;
+    a.logits = nullptr;
+    a.ids_out = nullptr;
+    a.weights_out = nullptr;
+    a.out = out;
+    a.out_rows = N;
     a.tile_rows = 0;
+    return a;
+}
+
+hipError_t launch_gather(int fmt, const void *codes, const void *plane, int E, int64_t N, int64_t K, const void *x,
+                         qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids, const float *weights,
+                         int epi, void *y, void *workspace, hipStream_t st) {
+    (void)xdt;
+    (void)workspace;
+    GatherArgs a = make_args(codes, plane, E, N, K, x, x_per_slot, T, topk, ids, weights, y);
+    if (epi == EPI_SWIGLU) a.out_rows = N / 2;
     int umax = T * topk < E ? T * topk : E;
-    bool handled = false;
-    hipError_t err;
-    switch (fmt) {
-    case INT4: err = launch_gather_fmt<INT4>(a, epi, umax, &handled, st); break;
-    case FP4: err = launch_gather_fmt<FP4>(a, epi, umax, &handled, st); break;
-    case INT8: err = launch_gather_fmt<INT8>(a, epi, umax, &handled, st); break;
-    default: err = launch_gather_fmt<KM4>(a, epi, umax, &handled, st); break;
+    return launch_any(fmt, a, epi, false, umax, st);
+}
+
+hipError_t launch_moe_ffn(int fmt, const void *gu_codes, const void *gu_plane, const void *dn_codes,
+                          const void *dn_plane, int E, int64_t H, int64_t I, const float *logits, const void *x, int T,
+                          int topk, int32_t *ids, float *weights, void *h, float *y, hipStream_t st) {
+    // gate/up + SwiGLU (h [T][topk][I]). For one token the routing is fused
+    // into it: each workgroup routes the token itself, which costs less than
+    // a separate launch. Beyond one token the duplicated routing work grows
+    // with T times the number of workgroups and a separate routing launch is
+    // cheaper.
+    GatherArgs g = make_args(gu_codes, gu_plane, E, 2 * I, H, x, 0, T, topk, ids, weights, h);
+    g.out_rows = I;
+    const bool fuse = (T == 1);
+    if (fuse) {
+        g.logits = logits;
+        g.ids_out = ids;
+        g.weights_out = weights;
+    } else {
+        hipError_t err = launch_moe_route(logits, T, E, topk, ids, weights, st);
+        if (err != hipSuccess) return err;
     }
+    int umax = T * topk < E ? T * topk : E;
+    hipError_t err = launch_any(fmt, g, EPI_SWIGLU, fuse, umax, st);
     if (err != hipSuccess) return err;
-    if (!handled) return hipErrorInvalidValue;
-    if (epi == EPI_COMBINE) {
-        int64_t tot = (int64_t)T * N;
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, st,
-                           reinterpret_cast<const float *>(workspace), weights, T, topk, N,
-                           reinterpret_cast<float *>(y));
-        return hipGetLastError();
-    }
-    return hipSuccess;
+    // launch 2: down projection with the weighted combine (y [T][H])
+    GatherArgs d = make_args(dn_codes, dn_plane, E, H, I, h, 1, T, topk, ids, weights, y);
+    return launch_any(fmt, d, EPI_COMBINE, false, umax, st);
 }
 
 }  // namespace qmv

@@ -35,5 +35,8 @@ size_t gather_workspace_bytes(int T, int topk, int E, int64_t N, int epi);
 hipError_t launch_gather(int fmt, const void *codes, const void *plane, int E, int64_t N, int64_t K, const void *x,
                          qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids, const float *weights,
                          int epi, void *y, void *workspace, hipStream_t st);
+hipError_t launch_moe_ffn(int fmt, const void *gu_codes, const void *gu_plane, const void *dn_codes,
+                          const void *dn_plane, int E, int64_t H, int64_t I, const float *logits, const void *x, int T,
+                          int topk, int32_t *ids, float *weights, void *h, float *y, hipStream_t st);
 
 }  // namespace qmv

@@ -81,13 +81,30 @@ def test_dequant_and_moe_validation(L):
     assert L.qmoe_route(FAKE, 2, 256, 0, FAKE, FAKE, S) == E_SHAPE
     assert L.qmoe_route(FAKE, 2, 4, 8, FAKE, FAKE, S) == E_SHAPE       # topk > E
     assert L.qmoe_route(NUL, 2, 256, 8, FAKE, FAKE, S) == E_NULL
-    # gather: T > 8, missing workspace, bad epilogue, fp32 x
+    # gather: T > 8, combine without weights, int8 K > 4096, bad epilogue, fp32 x
     g = L.gather_qmatvec
     assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 9, 8, FAKE, FAKE, 2, FAKE, NUL, 0, S) == E_SHAPE
-    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 4, 8, FAKE, FAKE, 2, FAKE, NUL, 0, S) == E_WORKSPACE
+    assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 4, 8, FAKE, NUL, 2, FAKE, NUL, 0, S) == E_NULL
+    assert g(2, FAKE, FAKE, 256, 2048, 8192, FAKE, 1, 1, 4, 8, FAKE, FAKE, 0, FAKE, NUL, 0, S) == E_SHAPE
     assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 1, 1, 4, 8, FAKE, FAKE, 7, FAKE, NUL, 0, S) == E_DTYPE
     assert g(0, FAKE, FAKE, 256, 2048, 512, FAKE, 0, 1, 4, 8, FAKE, FAKE, 0, FAKE, NUL, 0, S) == E_DTYPE
     assert g(0, FAKE, FAKE, 256, 1023, 512, FAKE, 1, 0, 4, 8, FAKE, FAKE, 1, FAKE, NUL, 0, S) == E_SHAPE  # odd N
-    assert L.gather_qmatvec_workspace_bytes(4, 8, 256, 2048, 2) == 4 * 8 * 2048 * 4
-    assert L.gather_qmatvec_workspace_bytes(4, 8, 256, 2048, 1) == 0
+    for epi in (0, 1, 2):
+        assert L.gather_qmatvec_workspace_bytes(4, 8, 256, 2048, epi) == 0
+    # fused MoE layer: fmt, null output, T > 8, topk > E, H not a multiple of 32, int8 I > 4096, misaligned h
+    f = L.qmoe_ffn
+    args = [0, FAKE, FAKE, FAKE, FAKE, 256, 2048, 512, FAKE, FAKE, 4, 8, FAKE, FAKE, FAKE, FAKE, S]
+
+    def call(**kw):
+        a = list(args)
+        for k, v in kw.items():
+            a[int(k[1:])] = v
+        return f(*a)
+    assert call(a0=7) == E_DTYPE
+    assert call(a15=NUL) == E_NULL
+    assert call(a10=9) == E_SHAPE
+    assert call(a5=4) == E_SHAPE
+    assert call(a6=2047) == E_SHAPE
+    assert call(a0=2, a7=8192) == E_SHAPE
+    assert call(a14=ODD) == E_ALIGN
     assert L.qmv_stream_read(FAKE, 24, FAKE, S) == E_SHAPE

@@ -151,3 +151,43 @@ def test_moe_gather_none_matches_per_slot_matvec(moe_case):
             oc, os_ = oracle.pack_int4(c.W_down[e])
             want = oracle.matvec("int4", oc, os_, xs[t, s][None])[0]
             assert rel_err(y[t, s], want) <= RTOL
+
+
+def test_moe_layer_replays_identically_in_a_hip_graph(moe_case):
+    """The MoE entry points allocate nothing and never synchronize, so a layer
+    can be captured in a HIP graph; every replay (with eager work between
+    replays) must equal the eager result bit for bit."""
+    import torch
+    c, guc, gus, dnc, dns = moe_case
+    T = 4
+    E, H, I = guc.shape[0], 2 * guc.shape[2], guc.shape[1] // 2
+    lg = dev(c.logits[:T])
+    x = dev(c.x[:T])
+    ids = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, c.topk), dtype=torch.float32, device="cuda")
+    h = torch.empty((T, c.topk, I), dtype=torch.float16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    ws = torch.empty((qmv.gather_qmatvec_workspace_bytes(T, c.topk, E, H, "combine"),), dtype=torch.uint8,
+                     device="cuda")
+
+    def layer():
+        qmv.qmoe_route(lg, c.topk, ids=ids, weights=w)
+        qmv.gather_qmatvec("int4", guc, gus, x, ids, epi="swiglu", y=h)
+        qmv.gather_qmatvec("int4", dnc, dns, h, ids, weights=w, epi="combine", x_per_slot=True, y=y, workspace=ws)
+
+    layer()
+    torch.cuda.synchronize()
+    ref = host(y).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for r in range(4):
+        y.fill_(-1.0)
+        ids.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref), "replay %d" % r
+        layer()                      # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref)

@@ -1,0 +1,140 @@
+"""GPU parity of the mixture-of-experts entry points in every weight format,
+on small expert sets that the oracle runs whole.
+
+Cases cover one token (routing fused into the gate/up launch) and several,
+one or several row tiles, ragged rows (96 = three 32-blocks), long gate/up
+rows (4096) and long down rows (2048), and expert counts past 256 and 1024
+(the wider routing layouts). Weights are packed by the oracle
+and uploaded, so these tests see the MoE kernels alone; the packers have
+their own bit-exact tests."""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_decode_matvec_amd as qmv
+from tests.gpu_helpers import RTOL, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["int4", "fp4", "int8", "km4"]
+# E, H, I, T, topk
+CASES = [
+    (16, 256, 128, 1, 3),
+    (16, 256, 128, 5, 3),
+    (300, 64, 32, 1, 8),
+    (1500, 64, 32, 1, 8),
+    (8, 96, 96, 8, 4),
+    (4, 4096, 64, 3, 2),
+    (6, 64, 2048, 2, 2),
+    (300, 64, 32, 4, 8),
+    (1500, 64, 32, 2, 8),
+]
+
+
+def _case(fmt, E, H, I, T, topk, seed=0):
+    rng = np.random.default_rng(seed + 7 * E + H + I)
+    gu = (rng.standard_normal((E * 2 * I, H)) * 0.02).astype(np.float16)
+    dn = (rng.standard_normal((E * H, I)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((T, H)).astype(np.float16)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    guc, gup = oracle.pack(fmt, gu)
+    dnc, dnp = oracle.pack(fmt, dn)
+    guc, gup = guc.reshape(E, 2 * I, -1), gup.reshape(E, 2 * I, -1)
+    dnc, dnp = dnc.reshape(E, H, -1), dnp.reshape(E, H, -1)
+    return guc, gup, dnc, dnp, x, logits
+
+
+def _h_close(h, h_want):
+    """fp16 activations: within one fp16 step of the oracle's, plus the fp32
+    accumulation error of the gate/up sums (1e-6 of the largest value)."""
+    h = np.asarray(h, np.float64)
+    tol = np.abs(h_want) * 2.0 ** -10 + 2.0 ** -24 + 1e-6 * np.abs(h_want).max()
+    return np.all(np.abs(h - h_want) <= tol)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("E,H,I,T,topk", CASES)
+def test_moe_ffn_matches_oracle(fmt, E, H, I, T, topk):
+    print("moe_ffn", fmt, E, H, I, T, topk, flush=True)
+    guc, gup, dnc, dnp, x, logits = _case(fmt, E, H, I, T, topk)
+    oids, ow = oracle.moe_route(logits, topk)
+    want, h_want = oracle.moe_ffn(guc, gup, dnc, dnp, x, oids, ow, return_h=True, fmt=fmt)
+    d = [dev(a) for a in (guc, gup, dnc, dnp)]
+    y, ids, w, h = qmv.qmoe_ffn(fmt, *d, dev(x), dev(logits), topk)
+    assert np.array_equal(host(ids), oids)
+    assert np.allclose(host(w), ow, rtol=1e-6, atol=1e-7)
+    assert _h_close(host(h), h_want)
+    assert rel_err(host(y), want) <= RTOL
+    # the three-call path (route, SwiGLU gather, combine gather) computes the
+    # same arithmetic in the same order: identical bits
+    y3, ids3, w3 = qmv.moe_ffn(*d, dev(x), dev(logits), topk, fmt=fmt)
+    assert np.array_equal(host(ids3), host(ids))
+    assert np.array_equal(host(w3), host(w))
+    assert np.array_equal(host(y3), host(y))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_gather_none_and_combine_with_shared_input(fmt):
+    """epi=none gives every slot's own matvec; combine with one input per
+    token (x_per_slot = 0) is the weighted sum over the token's slots."""
+    E, H, I, T, topk = 12, 160, 64, 6, 3
+    guc, gup, dnc, dnp, x, logits = _case(fmt, E, H, I, T, topk, seed=3)
+    oids, ow = oracle.moe_route(logits, topk)
+    codes, plane = dev(guc), dev(gup)
+    y = host(qmv.gather_qmatvec(fmt, codes, plane, dev(x), dev(oids), epi="none"))
+    yc = host(qmv.gather_qmatvec(fmt, codes, plane, dev(x), dev(oids), weights=dev(ow.astype(np.float32)),
+                                 epi="combine"))
+    for t in range(T):
+        acc = np.zeros(2 * I)
+        for s in range(topk):
+            e = oids[t, s]
+            want = oracle.matvec(fmt, guc[e], gup[e], x[t][None])[0]
+            assert rel_err(y[t, s], want) <= RTOL
+            acc += np.float64(np.float32(ow[t, s])) * want
+        assert rel_err(yc[t], acc) <= RTOL
+
+
+@pytest.mark.parametrize("E,T", [(256, 64), (300, 37), (1500, 5), (4096, 3)])
+def test_route_wide(E, T):
+    rng = np.random.default_rng(E + T)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, E // 3] = logits[0, E - 1] = logits[0].max() + 0.5   # a tie: lower id first
+    ids, w = qmv.qmoe_route(dev(logits), 8)
+    oids, ow = oracle.moe_route(logits, 8)
+    assert np.array_equal(host(ids), oids)
+    assert np.allclose(host(w), ow, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_moe_ffn_replays_identically_in_a_hip_graph(T):
+    """qmoe_ffn allocates nothing and never synchronizes, so it can be
+    captured; each replay (with eager work between) equals the eager call."""
+    import torch
+    fmt, E, H, I, topk = "km4", 16, 256, 128, 3
+    guc, gup, dnc, dnp, x, logits = _case(fmt, E, H, I, T, topk, seed=5)
+    d = [dev(a) for a in (guc, gup, dnc, dnp)]
+    xd, ld = dev(x), dev(logits)
+    ids = torch.empty((T, topk), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, topk), dtype=torch.float32, device="cuda")
+    h = torch.empty((T, topk, I), dtype=torch.float16, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def layer():
+        qmv.qmoe_ffn(fmt, *d, xd, ld, topk, ids=ids, weights=w, h=h, y=y)
+
+    layer()
+    torch.cuda.synchronize()
+    ref = host(y).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer()
+    for r in range(4):
+        y.fill_(-1.0)
+        ids.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref), "replay %d" % r
+        layer()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(y), ref)
