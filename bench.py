@@ -237,6 +237,12 @@ def main():
             nb = algo_bytes(fmt, N_ROWS, K_DIM)
             extras["%s_B1_us" % fmt] = round(msf * 1e3, 2)
             extras["%s_B1_GBps" % fmt] = round(nb / (msf * 1e-3) / 1e9, 1)
+            for bb in (4, 8):
+                xb = x8[:bb]
+                msb = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], xb, y=y[:bb]),
+                            args.steps // 2, args.warmup)
+                extras["%s_B%d_us" % (fmt, bb)] = round(msb * 1e3, 2)
+                extras["%s_B%d_GBps" % (fmt, bb)] = round(nb / (msb * 1e-3) / 1e9, 1)
             del pk
         # fp16 dense GEMV on the same shape (torch), for the per-op ratio against fp16
         wcp = [W] + [W.clone() for _ in range(1)]

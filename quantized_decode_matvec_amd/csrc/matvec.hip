@@ -351,6 +351,8 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
     bool handled = false;
     hipError_t err = hipSuccess;
     if (xdt == QMV_F16) {
+        err = launch_matvec_mfma(FMT, codes, plane, N, K, x, B, y, st, &handled);
+        if (handled) return err;
         if (cpr <= 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, y, st, &handled);
         else if (cpr <= 32) err = dispatch_b<FMT, 32, 1>(codes, plane, N, K, x, B, y, st, &handled);
         else if (cpr <= 64) err = dispatch_b<FMT, 64, 1>(codes, plane, N, K, x, B, y, st, &handled);

@@ -1,0 +1,380 @@
+// Batched decode matvec on the matrix cores: y[b][n] = sum_k dequant(W)[n][k]
+// * x[b][k] for a batch of up to 8 tokens ("Dense-path int4km coverage +
+// flagship Qwen3.6-35B - session findings & methods", sections 1 and 8: the
+// fused dequant-matvec at decode batch sizes; the next step the page lists
+// is the batched B = 4-8 form).
+//
+// gfx950 design. At batch b the dot2 path spends b times the VALU work of
+// batch 1 on multiplies while the decode work stays the same; here the
+// multiplies go to v_mfma_f32_16x16x32_f16, which takes 16 weight rows x 32
+// k against 16 batch columns per instruction, so the VALU only decodes.
+//   - Operands: A = x (16 batch rows, rows >= B read zeros), B = the
+//     decoded weights (32 k x 16 rows). Result D[batch][row]: lane (r, q),
+//     r = lane % 16, q = lane / 16, holds rows r, batches 4q .. 4q + 3.
+//   - Every lane of row r owns row r, so one MFMA result per block is scaled
+//     by that lane's own block scale (fp32 FMA) before accumulation; the
+//     decoded values stay exact in fp16 as in the dot2 path. The 16 rows of
+//     one MFMA all take the same 32-k block.
+//   - Codes reach the MFMA layout through a small per-wave LDS stage (global
+//     loads stay whole cache lines): lane (r, q) takes 16-byte chunk 4j + q
+//     of row r, and a 4 x 4 dword transpose across the four 16-lane rows
+//     (permlane32/16 swaps) gives it dword q of chunks 4j .. 4j + 3, exactly
+//     its share of the four MFMAs of those blocks (int8: two blocks of two
+//     chunks each).
+//   - x is staged once per workgroup in LDS, in the element order the
+//     decoder produces, one row per batch token, each row padded by 16 bytes
+//     so the 16 batch lanes of a read hit distinct banks.
+#include "qmv_device.h"
+#include "qmv_launch.h"
+
+namespace qmv {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+
+constexpr int kMfmaWaves = 4;
+
+// Lane (r, q) holds X[q][m] in w[m] (chunk q, dword m); afterwards it holds
+// X[m][q] (dword q of chunk m). permlane32_swap exchanges the upper two
+// 16-lane rows of its first operand with the lower two of its second;
+// permlane16_swap the odd rows of its first operand with the even rows of
+// its second.
+__device__ __forceinline__ void transpose4(uint32_t (&w)[4]) {
+    u2v s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+    u2v s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    u2v s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    u2v s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    w[0] = s01[0];
+    w[1] = s01[1];
+    w[2] = s23[0];
+    w[3] = s23[1];
+}
+
+__device__ __forceinline__ h8 h8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v v = {a, b, c, d};
+    return __builtin_bit_cast(h8, v);
+}
+
+// 8 weights of one 32-k block for one lane, in the order x is staged:
+//  INT4: one dword (nibbles n0..n7) -> n0 n4 n1 n5 n2 n6 n3 n7
+//  FP4 : one dword -> c0 .. c7
+//  INT8: two dwords (codes 4q..4q+3 and 16+4q..16+4q+3 of the block)
+template <int FMT>
+__device__ __forceinline__ h8 decode8(uint32_t v, uint32_t v2) {
+    if constexpr (FMT == INT4) {
+        const h2 b0 = as_h2(0x64086408u);   // (1032, 1032)
+        const uint32_t magic = 0x64006400u;
+        h2 a0 = as_h2(and_or(v, 0x000F000Fu, magic)) - b0;
+        h2 a1 = as_h2(and_or(v >> 4, 0x000F000Fu, magic)) - b0;
+        h2 a2 = as_h2(and_or(v >> 8, 0x000F000Fu, magic)) - b0;
+        h2 a3 = as_h2(and_or(v >> 12, 0x000F000Fu, magic)) - b0;
+        return h8_of(as_u32(a0), as_u32(a1), as_u32(a2), as_u32(a3));
+    } else if constexpr (FMT == FP4) {
+        return h8_of(as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0)),
+                     as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1)),
+                     as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2)),
+                     as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3)));
+    } else {
+        const h2 bias = as_h2(0x64806480u);   // (1152, 1152)
+        uint32_t u = v ^ 0x80808080u, u2 = v2 ^ 0x80808080u;
+        h2 a = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) - bias;
+        h2 b = as_h2(__builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) - bias;
+        h2 c = as_h2(__builtin_amdgcn_perm(0x64646464u, u2, 0x04010400u)) - bias;
+        h2 d = as_h2(__builtin_amdgcn_perm(0x64646464u, u2, 0x04030402u)) - bias;
+        return h8_of(as_u32(a), as_u32(b), as_u32(c), as_u32(d));
+    }
+}
+
+// One 8-element x group (16 bytes) in decoder order; group g of a row is
+// staged at halfs 8g .. 8g + 7. For INT8, group 4c + q holds elements
+// 32c + 4q .. +3 and 32c + 16 + 4q .. +3.
+template <int FMT>
+__device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, int g) {
+    if constexpr (FMT == INT8) {
+        const int c = g >> 2, q = g & 3;
+        uint2 lo = *reinterpret_cast<const uint2 *>(xrow + 32 * c + 4 * q);
+        uint2 hi = *reinterpret_cast<const uint2 *>(xrow + 32 * c + 16 + 4 * q);
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+        uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * g);
+        if constexpr (FMT == INT4) {
+            // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
+            return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                              __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+        }
+        return v;
+    }
+}
+
+// Per-wave LDS staging of one row group (16 rows): the codes of one load
+// step (16 rows x 256 bytes, rows padded by 16 bytes) and the group's scale
+// rows (padded by 8 or 4 bytes), so that the MFMA-layout reads hit distinct
+// banks; plus 256 zero bytes per workgroup for the A operand of batch lanes
+// >= B.
+constexpr int kCodeRowLds = 256 + 16;
+constexpr bool kLdsCodes = true;   // staged loads measured faster on MI355X
+constexpr int kZeroLds = 256;
+template <int FMT> constexpr int scale_pad() { return (FMT == INT4) ? 8 : 4; }
+template <int FMT> __host__ __device__ constexpr int scale_row_bytes(int K) {
+    return (FMT == FP4) ? K / 32 : K / 16;   // one e8m0 byte or one fp16 per block
+}
+template <int FMT, bool LDS_CODES> __host__ __device__ constexpr int wave_lds_bytes(int K) {
+    return (LDS_CODES ? 16 * kCodeRowLds : 0) + ((16 * (scale_row_bytes<FMT>(K) + scale_pad<FMT>()) + 15) / 16) * 16;
+}
+// 16-byte pieces per lane of a group's scales (16 rows x scale_row_bytes)
+template <int FMT> __host__ __device__ constexpr int scale_pieces(int K) {
+    return (16 * scale_row_bytes<FMT>(K) + 1023) / 1024;
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Each wave streams RG row groups of 16 rows. A load step covers 256 bytes
+// of every row of the group (four j-steps), read as four instructions of four
+// rows x 256 contiguous bytes (whole cache lines), and goes through LDS into
+// the MFMA layout (lane (r, q): chunk 4j + q of row r). A group's scales are
+// one contiguous stretch of the scale plane (SP 16-byte pieces per lane),
+// read whole with the group's first step. Loads run D steps ahead of the
+// arithmetic in a ring of registers, which keeps enough bytes in flight per
+// wave to cover the memory latency.
+template <int FMT, int RG, int SP, int D, bool LDS_CODES>
+__global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__restrict__ codes,
+                                                          const void *__restrict__ plane, int64_t N, int K,
+                                                          const _Float16 *__restrict__ x, int B,
+                                                          float *__restrict__ y) {
+    extern __shared__ __align__(16) _Float16 xs[];
+    constexpr int MPJ = (FMT == INT8) ? 2 : 4;   // blocks (MFMAs) per j-step
+    const int KP = K + 8;                         // padded x row in LDS, halfs
+    const int groups = K / 8;
+    for (int i = threadIdx.x; i < B * groups; i += 64 * kMfmaWaves) {
+        const int b = i / groups, g = i - b * groups;
+        *reinterpret_cast<uint4 *>(xs + b * KP + 8 * g) = stage_group<FMT>(x + (size_t)b * K, g);
+    }
+    uint8_t *const zl = reinterpret_cast<uint8_t *>(xs + B * KP);
+    if (threadIdx.x < kZeroLds / 16) reinterpret_cast<uint4 *>(zl)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: scalar branches
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t rows0 = ((int64_t)blockIdx.x * kMfmaWaves + wave) * (RG * 16);
+    if (rows0 >= N) return;
+    const int J = (FMT == INT8) ? K / 64 : K / 128;   // j-steps per row
+    const int cpr = 4 * J;                             // 16-byte chunks per row
+    const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
+    const int srb = scale_row_bytes<FMT>(K);
+    const int srs = srb + scale_pad<FMT>();            // padded scale row in LDS
+    uint8_t *wl = zl + kZeroLds + wave * wave_lds_bytes<FMT, LDS_CODES>(K);
+    uint8_t *cl = wl;                                       // codes [16][kCodeRowLds]
+    uint8_t *sl = wl + (LDS_CODES ? 16 * kCodeRowLds : 0);  // scales [16][srs]
+    // A operand of j-step j: xa + xstride * j, then 64 bytes per block. Batch
+    // lanes >= B read the zero bytes with stride 0.
+    const uint8_t *xa = (r < B) ? reinterpret_cast<const uint8_t *>(xs + r * KP + 8 * q) : zl + 16 * q;
+    const uint32_t xstride = (r < B) ? 64u * MPJ : 0u;
+    const int steps_per_group = (J + 3) / 4;
+    const int nsteps = RG * steps_per_group;
+
+    // Every step issues the same loads unconditionally (a branch around a
+    // load makes the compiler wait for all outstanding loads where the paths
+    // join, which would drain the ring): steps past the end reload the last
+    // step, and steps that do not start a group read their scale pieces from
+    // one uniform address (a single cached request).
+    uint4 cw[D][4];
+    uint4 sc[D][SP];
+    auto issue = [&](int s_in, uint4 (&c)[4], uint4 (&sv)[SP]) {
+        const int s = s_in < nsteps ? s_in : nsteps - 1;
+        const int g = s / steps_per_group;
+        const int t = s - g * steps_per_group;
+        const int64_t grow = rows0 + g * 16;
+        // wave-uniform base, 32-bit lane offsets; rows past N read row N - 1
+        const int64_t growc = grow < N ? grow : N - 1;
+        const int lim = (int)(N - 1 - growc < 15 ? N - 1 - growc : 15);
+        const uint8_t *cbase = codes + growc * (int64_t)row_bytes;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            // staged: four rows x 256 bytes per instruction; direct: lane (r, q)
+            // takes chunk 4j + q of row r of j-step j = 4t + i
+            int rr = LDS_CODES ? 4 * i + (lane >> 4) : r;
+            rr = rr < lim ? rr : lim;
+            int ch = LDS_CODES ? 16 * t + (lane & 15) : 16 * t + 4 * i + q;
+            ch = ch < cpr ? ch : 0;   // past the row end: any valid chunk, never used
+            c[i] = load_stream16(cbase + ((uint32_t)rr * row_bytes + (uint32_t)ch * 16u));
+        }
+        // the scale rows of 16 consecutive rows are contiguous: 16 * srb
+        // bytes. A last, partial group reads rows N - 16 .. N - 1 instead
+        // (N >= 16) and looks its rows up shifted by the difference.
+        const int64_t g0 = grow + 16 <= N ? grow : N - 16;
+        const uint8_t *sp = reinterpret_cast<const uint8_t *>(plane) + g0 * srb;
+#pragma unroll
+        for (int u = 0; u < SP; u++) {
+            int off = 16 * (lane + 64 * u);
+            off = (t == 0 && off + 16 <= 16 * srb) ? off : 0;
+            sv[u] = *reinterpret_cast<const uint4 *>((t == 0) ? sp + off : reinterpret_cast<const uint8_t *>(plane));
+        }
+    };
+
+#pragma unroll
+    for (int u = 0; u < D; u++) issue(u, cw[u], sc[u]);
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; u++) {
+            // The loads are issued on every path (no early exit between them):
+            // where paths with different loads in flight join, the compiler
+            // must wait for all of them, which would drain the ring. Steps past
+            // the end only skip their LDS work and arithmetic.
+            const int s = s0 + u;
+            const int sc_step = s < nsteps ? s : nsteps - 1;
+            const int g = sc_step / steps_per_group;
+            const int t = sc_step - g * steps_per_group;
+            const int64_t grow = rows0 + g * 16;
+            const bool valid = s < nsteps && grow < N;
+            if (valid) {
+                // stage this step's codes (and at a group's first step its scales)
+                if constexpr (LDS_CODES) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        *reinterpret_cast<uint4 *>(cl + (4 * i + (lane >> 4)) * kCodeRowLds + (lane & 15) * 16) =
+                            cw[u][i];
+                }
+                if (t == 0) {
+#pragma unroll
+                    for (int v = 0; v < SP; v++) {
+                        const uint32_t wv[4] = {sc[u][v].x, sc[u][v].y, sc[u][v].z, sc[u][v].w};
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            const int off = 16 * (lane + 64 * v) + 4 * e;   // byte offset in the group's scales
+                            if (off < 16 * srb) {
+                                const int row = off / srb, col = off - row * srb;
+                                *reinterpret_cast<uint32_t *>(sl + row * srs + col) = wv[e];
+                            }
+                        }
+                    }
+                }
+            }
+            wave_sync_lds();
+            uint4 cu[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) cu[i] = cw[u][i];
+            issue(s + D, cw[u], sc[u]);
+            if (valid) {
+                // LDS scale row of this lane's row (see the partial-group note above)
+                const int delta = (int)(grow + 16 <= N ? 0 : grow - (N - 16));
+                const int srow = r + delta < 16 ? r + delta : 15;
+#pragma unroll
+                for (int jj = 0; jj < 4; jj++) {
+                    const int j = 4 * t + jj;   // J % 4 == 0: no partial steps
+                    const uint4 c4 =
+                        LDS_CODES ? *reinterpret_cast<const uint4 *>(cl + r * kCodeRowLds + (4 * jj + q) * 16) : cu[jj];
+                    uint32_t w[4] = {c4.x, c4.y, c4.z, c4.w};
+                    transpose4(w);
+                    uint32_t s0w, s1w = 0;
+                    if constexpr (FMT == INT4) {
+                        const uint2 s2 = *reinterpret_cast<const uint2 *>(sl + srow * srs + 8 * j);
+                        s0w = s2.x;
+                        s1w = s2.y;
+                    } else {
+                        s0w = *reinterpret_cast<const uint32_t *>(sl + srow * srs + 4 * j);
+                    }
+                    // the j-step's MFMAs are independent: decode and read every
+                    // operand first, issue the MFMAs back to back, then scale
+                    // and accumulate
+                    h8 ax[MPJ], bw[MPJ];
+                    f4 d[MPJ];
+#pragma unroll
+                    for (int m = 0; m < MPJ; m++) {
+                        ax[m] = *reinterpret_cast<const h8 *>(xa + xstride * (uint32_t)j + 64 * m);
+                        bw[m] = (FMT == INT8) ? decode8<FMT>(w[2 * m], w[2 * m + 1]) : decode8<FMT>(w[m], 0u);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MPJ; m++) {
+                        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+                        d[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[m], bw[m], zero, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MPJ; m++) {
+                        float scl;
+                        if constexpr (FMT == INT4) {
+                            const uint32_t pr = (m < 2) ? s0w : s1w;
+                            scl = f16_bits_to_f32((uint16_t)((m & 1) ? (pr >> 16) : (pr & 0xFFFFu)));
+                        } else if constexpr (FMT == FP4) {
+                            scl = e8m0_to_f32((s0w >> (8 * m)) & 0xFFu);
+                        } else {
+                            scl = f16_bits_to_f32((uint16_t)(m ? (s0w >> 16) : (s0w & 0xFFFFu)));
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[v] = __builtin_fmaf(d[m][v], scl, acc[v]);
+                    }
+                }
+            }
+            wave_sync_lds();   // the next step rewrites the staging buffers
+            if (valid && t == steps_per_group - 1) {
+                // group done: lane (r, q) holds y[4q + v][row]
+                const int64_t row = grow + r;
+                if (row < N) {
+#pragma unroll
+                    for (int v = 0; v < 4; v++)
+                        if (4 * q + v < B) y[(size_t)(4 * q + v) * N + row] = acc[v];
+                }
+                acc = f4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+}
+
+template <int FMT>
+static size_t mfma_lds_bytes(int64_t K, int B) {
+    return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
+}
+
+// The batched matrix-core path takes fp16 x, 3 <= B <= 8 (below that the
+// dot2 path is as fast), whole j-steps (K % 128 == 0, int8 K % 64 == 0),
+// K <= 4096, N >= 16, a 16-byte aligned scale plane, and staging that fits
+// in 64 KiB of LDS.
+static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
+    if (fmt == KM4 || B < 3 || B > 8 || N < 16) return false;
+    if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
+    // a group's scales are read as 16-byte pieces
+    if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
+    size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
+                               : (fmt == FP4 ? mfma_lds_bytes<FP4>(K, B) : mfma_lds_bytes<INT8>(K, B));
+    return lds <= 64 * 1024;
+}
+
+template <int FMT, int SP>
+static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                                 float *y, hipStream_t st) {
+    constexpr int RG = 8, D = 2;
+    const int64_t rows_wg = (int64_t)kMfmaWaves * RG * 16;
+    const int64_t grid = (N + rows_wg - 1) / rows_wg;
+    hipLaunchKernelGGL((mv_mfma<FMT, RG, SP, D, kLdsCodes>), dim3((unsigned)grid), dim3(64 * kMfmaWaves),
+                       mfma_lds_bytes<FMT>(K, B), st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+    return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_mfma_fmt(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                                  float *y, hipStream_t st) {
+    const int sp = scale_pieces<FMT>(K);
+    if (sp <= 1) return launch_mfma_sp<FMT, 1>(codes, plane, N, K, x, B, y, st);
+    if (sp <= 2) return launch_mfma_sp<FMT, 2>(codes, plane, N, K, x, B, y, st);
+    return launch_mfma_sp<FMT, 4>(codes, plane, N, K, x, B, y, st);
+}
+
+hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                              int B, float *y, hipStream_t st, bool *handled) {
+    *handled = mfma_eligible(fmt, plane, N, K, B);
+    if (!*handled) return hipSuccess;
+    switch (fmt) {
+    case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st);
+    case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st);
+    default: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
+    }
+}
+
+}  // namespace qmv

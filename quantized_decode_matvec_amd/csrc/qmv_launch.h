@@ -15,6 +15,9 @@ int device_cu_count();   // compute units of the current device (cached per devi
 
 hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                          qmv_dtype xdt, int B, float *y, hipStream_t st);
+// batched matrix-core path; *handled is false when the shape is not one it takes
+hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                              int B, float *y, hipStream_t st, bool *handled);
 hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *out,
                           hipStream_t st);
 size_t stream_read_grid(size_t bytes);

@@ -111,6 +111,43 @@ def test_matvec_parity(fmt, N, K, B):
     assert rel_err(y, want) <= RTOL
 
 
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8"])
+@pytest.mark.parametrize("N,K,Bs", [(1000, 2048, (3, 5, 6, 7, 8)), (16, 512, (8,)), (17, 1536, (4, 8)),
+                                    (600, 4096, (3,)), (300, 3584, (8,)), (517, 640, (4,)), (260, 256, (8,))])
+def test_batched_matvec_parity(fmt, N, K, Bs):
+    """The matrix-core batched path: several workgroups and a ragged last row
+    group, every batch width it takes, a single row group (N = 16) and one
+    plus a row, one load step per row (K = 512) and three (K = 1536), the
+    largest K it stages (4096, at B = 3); and shapes it hands to the dot2
+    path (x too large for its LDS stage at K = 3584, K = 640 not a multiple
+    of 512, int8 K = 256 taken but the 4-bit formats not)."""
+    W, x = _case(fmt, N, K, B=8, seed=N + K)
+    codes, plane = oracle.pack(fmt, W)
+    dc, dp = dev(codes), dev(plane)
+    for B in Bs:
+        print("batched", fmt, N, K, B, flush=True)
+        want = oracle.matvec(fmt, codes, plane, x[:B])
+        y = host(qmv.qmatvec(fmt, dc, dp, dev(x[:B])))
+        assert rel_err(y, want) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["int4", "int8"])
+def test_batched_matvec_with_unaligned_scale_plane(fmt):
+    """A scale plane that is only 2-byte aligned is valid input; the batched
+    path, which reads scales as whole words, leaves it to the dot2 path."""
+    import torch
+    N, K, B = 96, 1024, 8
+    W, x = _case(fmt, N, K, B=B, seed=3)
+    codes, plane = oracle.pack(fmt, W)
+    want = oracle.matvec(fmt, codes, plane, x)
+    flat = np.concatenate([np.zeros(1, np.uint16), plane.reshape(-1)])
+    dflat = dev(flat)
+    dp = dflat[1:].view(plane.shape)
+    assert dp.data_ptr() % 4 == 2
+    y = host(qmv.qmatvec(fmt, dev(codes), dp, dev(x)))
+    assert rel_err(y, want) <= RTOL
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("B", [1, 5])
 def test_matvec_fp32_x(fmt, B):
