@@ -14,7 +14,9 @@
 //   - Every lane of row r owns row r, so one MFMA result per block is scaled
 //     by that lane's own block scale (fp32 FMA) before accumulation; the
 //     decoded values stay exact in fp16 as in the dot2 path. The 16 rows of
-//     one MFMA all take the same 32-k block.
+//     one MFMA all take the same 32-k block. km4 has no block scale: its
+//     MFMAs accumulate directly, and its codes are looked up in the 16 rows'
+//     tables in LDS (one SDWA add per code forms the address).
 //   - Codes reach the MFMA layout through a small per-wave LDS stage (global
 //     loads stay whole cache lines): lane (r, q) takes 16-byte chunk 4j + q
 //     of row r, and a 4 x 4 dword transpose across the four 16-lane rows
@@ -87,6 +89,42 @@ __device__ __forceinline__ h8 decode8(uint32_t v, uint32_t v2) {
     }
 }
 
+// KM4: the 8 codes of one dword looked up in the lane's row table in LDS
+// (tbase: its LDS byte address). Even codes' byte offsets 2c sit in the bytes
+// of (w << 1) & 0x1E1E1E1E, odd codes' in (w >> 3) & 0x1E1E1E1E; one SDWA
+// add per code forms the address. Result order c0 .. c7.
+template <int S>
+__device__ __forceinline__ uint32_t add_byte(uint32_t base, uint32_t w) {
+    uint32_t r;
+    if constexpr (S == 0)
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(base), "v"(w));
+    else if constexpr (S == 1)
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(base), "v"(w));
+    else if constexpr (S == 2)
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(base), "v"(w));
+    else
+        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(base), "v"(w));
+    return r;
+}
+
+__device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((size_t)addr);
+}
+
+__device__ __forceinline__ h8 decode8_km4(uint32_t w, uint32_t tbase) {
+    const uint32_t e = (w << 1) & 0x1E1E1E1Eu, o = (w >> 3) & 0x1E1E1E1Eu;
+    h2 v0, v1, v2, v3;
+    v0.x = lds_half(add_byte<0>(tbase, e));
+    v0.y = lds_half(add_byte<0>(tbase, o));
+    v1.x = lds_half(add_byte<1>(tbase, e));
+    v1.y = lds_half(add_byte<1>(tbase, o));
+    v2.x = lds_half(add_byte<2>(tbase, e));
+    v2.y = lds_half(add_byte<2>(tbase, o));
+    v3.x = lds_half(add_byte<3>(tbase, e));
+    v3.y = lds_half(add_byte<3>(tbase, o));
+    return h8_of(as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3));
+}
+
 // One 8-element x group (16 bytes) in decoder order; group g of a row is
 // staged at halfs 8g .. 8g + 7. For INT8, group 4c + q holds elements
 // 32c + 4q .. +3 and 32c + 16 + 4q .. +3.
@@ -116,9 +154,10 @@ __device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, 
 constexpr int kCodeRowLds = 256 + 16;
 constexpr bool kLdsCodes = true;   // staged loads measured faster on MI355X
 constexpr int kZeroLds = 256;
-template <int FMT> constexpr int scale_pad() { return (FMT == INT4) ? 8 : 4; }
+template <int FMT> constexpr int scale_pad() { return (FMT == INT4) ? 8 : (FMT == KM4 ? 0 : 4); }
+// per-row bytes of the scale plane (KM4: the row's 16-entry fp16 table)
 template <int FMT> __host__ __device__ constexpr int scale_row_bytes(int K) {
-    return (FMT == FP4) ? K / 32 : K / 16;   // one e8m0 byte or one fp16 per block
+    return (FMT == KM4) ? 32 : ((FMT == FP4) ? K / 32 : K / 16);   // one e8m0 byte or one fp16 per block
 }
 template <int FMT, bool LDS_CODES> __host__ __device__ constexpr int wave_lds_bytes(int K) {
     return (LDS_CODES ? 16 * kCodeRowLds : 0) + ((16 * (scale_row_bytes<FMT>(K) + scale_pad<FMT>()) + 15) / 16) * 16;
@@ -221,6 +260,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
 #pragma unroll
     for (int u = 0; u < D; u++) issue(u, cw[u], sc[u]);
     f4 acc = {0.f, 0.f, 0.f, 0.f};
+    f4 kacc[MPJ];
+#pragma unroll
+    for (int m = 0; m < MPJ; m++) kacc[m] = f4{0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsteps; s0 += D) {
 #pragma unroll
         for (int u = 0; u < D; u++) {
@@ -273,12 +315,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                         LDS_CODES ? *reinterpret_cast<const uint4 *>(cl + r * kCodeRowLds + (4 * jj + q) * 16) : cu[jj];
                     uint32_t w[4] = {c4.x, c4.y, c4.z, c4.w};
                     transpose4(w);
-                    uint32_t s0w, s1w = 0;
+                    uint32_t s0w = 0, s1w = 0;
                     if constexpr (FMT == INT4) {
                         const uint2 s2 = *reinterpret_cast<const uint2 *>(sl + srow * srs + 8 * j);
                         s0w = s2.x;
                         s1w = s2.y;
-                    } else {
+                    } else if constexpr (FMT != KM4) {
                         s0w = *reinterpret_cast<const uint32_t *>(sl + srow * srs + 4 * j);
                     }
                     // the j-step's MFMAs are independent: decode and read every
@@ -289,7 +331,18 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
 #pragma unroll
                     for (int m = 0; m < MPJ; m++) {
                         ax[m] = *reinterpret_cast<const h8 *>(xa + xstride * (uint32_t)j + 64 * m);
-                        bw[m] = (FMT == INT8) ? decode8<FMT>(w[2 * m], w[2 * m + 1]) : decode8<FMT>(w[m], 0u);
+                        if constexpr (FMT == KM4)
+                            bw[m] = decode8_km4(w[m], (uint32_t)(uintptr_t)(sl + srow * srs));
+                        else
+                            bw[m] = (FMT == INT8) ? decode8<FMT>(w[2 * m], w[2 * m + 1]) : decode8<FMT>(w[m], 0u);
+                    }
+                    if constexpr (FMT == KM4) {
+                        // no block scales: the MFMAs accumulate directly (one
+                        // accumulator per block position keeps them independent)
+#pragma unroll
+                        for (int m = 0; m < MPJ; m++)
+                            kacc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ax[m], bw[m], kacc[m], 0, 0, 0);
+                        continue;
                     }
 #pragma unroll
                     for (int m = 0; m < MPJ; m++) {
@@ -315,6 +368,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
             wave_sync_lds();   // the next step rewrites the staging buffers
             if (valid && t == steps_per_group - 1) {
                 // group done: lane (r, q) holds y[4q + v][row]
+                if constexpr (FMT == KM4) {
+#pragma unroll
+                    for (int m = 0; m < MPJ; m++) {
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[v] += kacc[m][v];
+                        kacc[m] = f4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
                 const int64_t row = grow + r;
                 if (row < N) {
 #pragma unroll
@@ -332,17 +393,20 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
     return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
 }
 
-// The batched matrix-core path takes fp16 x, 3 <= B <= 8 (below that the
-// dot2 path is as fast), whole j-steps (K % 128 == 0, int8 K % 64 == 0),
-// K <= 4096, N >= 16, a 16-byte aligned scale plane, and staging that fits
-// in 64 KiB of LDS.
+// The batched matrix-core path takes fp16 x, 3 <= B <= 8 (km4: 5 <= B; below
+// that the dot2 path is as fast), whole load steps (K % 512 == 0, int8
+// K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned scale plane, and
+// staging that fits in 64 KiB of LDS.
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
-    if (fmt == KM4 || B < 3 || B > 8 || N < 16) return false;
+    // km4 table lookups from 16 rows at once meet LDS bank conflicts; below
+    // B = 5 its dot2 path (one row's table per instruction) is faster
+    if (B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
     if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
-    // a group's scales are read as 16-byte pieces
+    // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
-                               : (fmt == FP4 ? mfma_lds_bytes<FP4>(K, B) : mfma_lds_bytes<INT8>(K, B));
+                 : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
+                 : (fmt == INT8) ? mfma_lds_bytes<INT8>(K, B) : mfma_lds_bytes<KM4>(K, B);
     return lds <= 64 * 1024;
 }
 
@@ -373,7 +437,8 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
     switch (fmt) {
     case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st);
     case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st);
-    default: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
+    case INT8: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
+    default: return launch_mfma_fmt<KM4>(codes, plane, N, (int)K, x, B, y, st);
     }
 }
 

@@ -111,7 +111,7 @@ def test_matvec_parity(fmt, N, K, B):
     assert rel_err(y, want) <= RTOL
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8"])
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K,Bs", [(1000, 2048, (3, 5, 6, 7, 8)), (16, 512, (8,)), (17, 1536, (4, 8)),
                                     (600, 4096, (3,)), (300, 3584, (8,)), (517, 640, (4,)), (260, 256, (8,))])
 def test_batched_matvec_parity(fmt, N, K, Bs):
