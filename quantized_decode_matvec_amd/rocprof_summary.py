@@ -1,9 +1,14 @@
 """Summaries of rocprofv3 output for the matvec kernels.
 
     python -m quantized_decode_matvec_amd.rocprof_summary stats KERNEL_STATS_CSV [--match SUBSTR]
+    python -m quantized_decode_matvec_amd.rocprof_summary grid KERNEL_TRACE_CSV [--match SUBSTR]
     python -m quantized_decode_matvec_amd.rocprof_summary traffic --kernel SUBSTR --key NAME \\
         --fetch FETCH_CSV --write WRITE_CSV --calib-fetch CF_CSV --calib-write CW_CSV \\
         [--calib-kernel copyBuffer] [--calib-bytes 1073741824] [--out profiles/traffic.json]
+
+`grid` groups a kernel trace by kernel and launch grid (one line per distinct
+launch shape, e.g. per token count of the MoE kernels) with the median and
+minimum duration.
 
 `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM bytes per
 dispatch: each counter is divided by what the same counter reads for a plain
@@ -58,6 +63,21 @@ def stats(path, match=None):
     return out
 
 
+def grid(path, match=None):
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"]
+        if match and match not in name:
+            continue
+        key = (name.split("(")[0], r["Grid_Size_X"], r["Grid_Size_Y"], r["Workgroup_Size_X"])
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = []
+    for key, v in sorted(groups.items()):
+        v.sort()
+        out.append(key + (len(v), v[len(v) // 2], v[0]))
+    return out
+
+
 def traffic(args):
     fetch_name, fetch_kib, nf = _pick(_per_kernel(args.fetch, "FETCH_SIZE"), args.kernel)
     write_name, write_kib, nw = _pick(_per_kernel(args.write, "WRITE_SIZE"), args.kernel)
@@ -95,6 +115,9 @@ def main():
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--match")
+    g = sub.add_parser("grid")
+    g.add_argument("csv")
+    g.add_argument("--match")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--key", required=True)
@@ -111,6 +134,11 @@ def main():
         print("|---|---|---|---|---|")
         for name, calls, avg, mn, mx in stats(a.csv, a.match):
             print("| %s | %d | %.2f | %.2f | %.2f |" % (name[:110], calls, avg / 1e3, mn / 1e3, mx / 1e3))
+    elif a.cmd == "grid":
+        print("| kernel | grid x (threads) | grid y | workgroup | calls | median us | min us |")
+        print("|---|---|---|---|---|---|---|")
+        for name, gx, gy, wg, n, med, mn in grid(a.csv, a.match):
+            print("| %s | %s | %s | %s | %d | %.2f | %.2f |" % (name[:90], gx, gy, wg, n, med, mn))
     else:
         traffic(a)
 
