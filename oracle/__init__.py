@@ -64,6 +64,8 @@ def lib():
         L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
         L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
+        L.orc_pack_int8_rows.argtypes = [P, i64, i64, P, P]
+        L.orc_embed_gather_int8.argtypes = [P, P, i64, i64, P, i64, P]
         L.orc_moe_ffn.argtypes = [ci, P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ci
@@ -187,6 +189,39 @@ def matvec(fmt: str, codes, plane, x, rows=None) -> np.ndarray:
     y = np.zeros((B, M), np.float64)
     lib().orc_matvec(FORMATS[fmt], _p(codes), _p(plane), N, K, _p(x), B, rp, nr, _p(y))
     return y
+
+
+def matvec_argmax(fmt: str, codes, plane, x):
+    """Largest entry of each batch row of matvec(...) and its row index (the
+    lowest index among equal largest values), from the fp64 products."""
+    y = matvec(fmt, codes, plane, x)
+    idx = np.argmax(y, axis=1)   # first occurrence of the maximum
+    return idx.astype(np.int64), y[np.arange(y.shape[0]), idx]
+
+
+# --- embedding table: int8 per-row scale, dequant-gather ---
+
+def pack_int8_rows(W):
+    """W [V, H] (fp16 or fp32, converted exactly to fp32) -> codes int8 [V, H],
+    scale fp16 bits uint16 [V]."""
+    W = np.ascontiguousarray(np.asarray(W).astype(np.float32))
+    V, H = W.shape
+    codes = np.zeros((V, H), np.int8)
+    scale = np.zeros(V, np.uint16)
+    lib().orc_pack_int8_rows(_p(W), V, H, _p(codes), _p(scale))
+    return codes, scale
+
+
+def embed_gather_int8(codes, scale, ids):
+    """out [T, H] fp16 bits (uint16) = fp16(codes[ids] * scale[ids])."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scale = np.ascontiguousarray(scale, dtype=np.uint16)
+    ids = np.ascontiguousarray(np.asarray(ids).reshape(-1), dtype=np.int32)
+    V, H = codes.shape
+    assert ids.min() >= 0 and ids.max() < V
+    out = np.zeros((len(ids), H), np.uint16)
+    lib().orc_embed_gather_int8(_p(codes), _p(scale), V, H, _p(ids), len(ids), _p(out))
+    return out
 
 
 # --- mixture of experts ---

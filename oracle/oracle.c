@@ -249,6 +249,53 @@ void orc_pack_int8(const float *W, int64_t N, int64_t K, int8_t *codes, uint16_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Embedding table: int8 with one fp16 scale per row, and its dequant-gather */
+/* [S3 "The LM head + embeddings": the front-end table gather is a plain     */
+/* int8 per-row dequant-gather, q[ids] as fp16 times scale[ids]].            */
+/* ------------------------------------------------------------------------ */
+
+/* Reading: the per-row scale follows the block recipe with the block being
+   the whole row and no clipping: s = fp16(fp32(amax) / 127), q = clamp(rint(
+   w / s), -127, 127) in fp32; an all-zero row has s = +0 and q = 0. */
+void orc_pack_int8_rows(const float *W, int64_t V, int64_t H, int8_t *codes, uint16_t *scale)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < V; v++) {
+        const float *w = W + v * H;
+        float amax = 0.0f;
+        for (int64_t h = 0; h < H; h++)
+            if (fabsf(w[h]) > amax)
+                amax = fabsf(w[h]);
+        uint16_t s16 = orc_f64_to_f16((double)(amax / 127.0f));
+        float s = (float)orc_f16_to_f64(s16);
+        scale[v] = s16;
+        for (int64_t h = 0; h < H; h++) {
+            float r = 0.0f;
+            if (s != 0.0f) {
+                r = rintf(w[h] / s);
+                if (r > 127.0f) r = 127.0f;
+                if (r < -127.0f) r = -127.0f;
+            }
+            codes[v * H + h] = (int8_t)r;
+        }
+    }
+}
+
+/* out[t][h] = fp16(q[ids[t]][h] * scale[ids[t]]): the product of an int8 and
+   an fp16 number is exact in fp64, so this is one rounding to fp16. */
+void orc_embed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H, const int32_t *ids,
+                           int64_t T, uint16_t *out)
+{
+    (void)V;
+    for (int64_t t = 0; t < T; t++) {
+        const int64_t v = ids[t];
+        const double s = orc_f16_to_f64(scale[v]);
+        for (int64_t h = 0; h < H; h++)
+            out[t * H + h] = orc_f64_to_f16((double)codes[v * H + h] * s);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* 4-bit k-means palettization, one 16-entry fp16 table per output row       */
 /* [S2 sections 1, 8, 8b; S3 "Palettization"].                               */
 /*                                                                          */

@@ -517,3 +517,65 @@ def test_km4_mean_on_an_fp16_midpoint_rounds_to_even(pair, kept, other):
     assert np.all(D[np.isin(row[0], np.array(pair, np.float16))] == kept_val)
     for v in ints:
         assert np.all(D[row[0] == v] == v)
+
+
+# --- embedding table (int8, one scale per row) and fused argmax ---
+
+def test_int8_rows_hand_worked():
+    """Row [1.27, -0.005, -0.635, 0, ...]: amax 1.27 gives the fp16 scale
+    0x211F (0.0100021); 1.27/s = 126.97 -> 127, -0.005/s = -0.4999 -> 0,
+    -0.635/s = -63.49 -> -63. The gathered values are fp16(q * s)."""
+    w = np.zeros((1, 64), np.float32)
+    w[0, :3] = [1.27, -0.005, -0.635]
+    q, s = oracle.pack_int8_rows(w)
+    assert s[0] == 0x211F
+    assert list(q[0, :3]) == [127, 0, -63] and not q[0, 3:].any()
+    out = oracle.embed_gather_int8(q, s, [0])
+    sv = np.array([0x211F], np.uint16).view(np.float16)[0]
+    assert out[0, 0] == (np.float16(127) * sv).view(np.uint16)
+    assert out[0, 2] == (np.float16(-63) * sv).view(np.uint16)
+    assert out[0, 1] == 0
+
+
+def test_int8_rows_equal_textbook_absmax():
+    """Per-row symmetric int8 equals the textbook recipe computed with numpy in
+    fp32 (amax, fp16 scale, rint, clamp), an all-zero row included."""
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((40, 300)) * 0.05).astype(np.float32)
+    W[5] = 0.0
+    W[6, 17] = -3.0
+    q, s = oracle.pack_int8_rows(W)
+    amax = np.abs(W).max(axis=1)
+    s_np = (amax / np.float32(127)).astype(np.float16)
+    assert np.array_equal(s, s_np.view(np.uint16))
+    sf = s_np.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q_np = np.clip(np.rint(W / sf[:, None]), -127, 127)
+    q_np[sf == 0] = 0
+    assert np.array_equal(q, q_np.astype(np.int8))
+
+
+def test_embed_gather_equals_numpy_fp16_product():
+    rng = np.random.default_rng(32)
+    W = (rng.standard_normal((70, 96)) * 0.02).astype(np.float16)
+    q, s = oracle.pack_int8_rows(W)
+    ids = np.array([0, 69, 5, 5, 33, 0], np.int32)
+    out = oracle.embed_gather_int8(q, s, ids)
+    want = q[ids].astype(np.float16) * s.view(np.float16)[ids][:, None]
+    assert np.array_equal(out, want.view(np.uint16))
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+def test_matvec_argmax_picks_the_lowest_index_among_equal_maxima(fmt):
+    """The argmax of the fp64 products equals numpy's on a numpy GEMM of the
+    dequantized matrix; two identical winning rows give the lower index."""
+    rng = np.random.default_rng(33)
+    W = (rng.standard_normal((50, 128)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((3, 128)).astype(np.float16)
+    W[41] = W[17] = np.sign(x[0]).astype(np.float16) * 0.05   # rows 17 and 41: the largest for token 0
+    codes, plane = oracle.pack(fmt, W)
+    idx, val = oracle.matvec_argmax(fmt, codes, plane, x)
+    ref = x.astype(np.float64) @ oracle.dequant(fmt, codes, plane).T
+    assert idx[0] == 17
+    assert np.array_equal(idx, np.argmax(ref, axis=1))
+    assert np.allclose(val, ref.max(axis=1), rtol=1e-12, atol=0)
