@@ -250,6 +250,29 @@ def main():
         extras["fp16_dense_torch_us"] = round(msd * 1e3, 2)
         extras["km4_speedup_vs_fp16_dense"] = round(msd / ms, 2)
         del wcp
+        # fused lm_head + argmax (no logits written) against matvec + torch.argmax
+        ws = torch.empty((qmv.qmatvec_argmax_workspace_bytes(N_ROWS, 1),), dtype=torch.uint8, device="cuda")
+        aidx = torch.empty((1,), dtype=torch.int32, device="cuda")
+        aval = torch.empty((1,), dtype=torch.float32, device="cuda")
+        msa = timed(lambda i: qmv.qmatvec_argmax("km4", copies[i % len(copies)][0], copies[i % len(copies)][1], x1,
+                                                 idx=aidx, val=aval, workspace=ws), args.steps, args.warmup)
+
+        def two_step(i):
+            qmv.qmatvec_km4(copies[i % len(copies)][0], copies[i % len(copies)][1], x1, y=y[:1])
+            torch.argmax(y[:1], dim=1)
+
+        ms2 = timed(two_step, args.steps, args.warmup)
+        extras["km4_argmax_fused_us"] = round(msa * 1e3, 2)
+        extras["km4_matvec_then_argmax_us"] = round(ms2 * 1e3, 2)
+        del ws
+        # int8 embedding dequant-gather from a table of the same shape, 8 tokens (HIP graphs)
+        tq, ts = qmv.qpack_int8_rows(W)
+        gids = torch.randint(0, N_ROWS, (8,), dtype=torch.int32, device="cuda",
+                             generator=torch.Generator(device="cuda").manual_seed(0))
+        gout = torch.empty((8, K_DIM), dtype=torch.float16, device="cuda")
+        msg = timed_graph(lambda i: qmv.qembed_gather_int8(tq, ts, gids, out=gout), args.steps, per_graph=64)
+        extras["embed_gather_int8_8tok_us"] = round(msg * 1e3, 2)
+        del tq, ts
         # attention projections of the pages' shapes (q: 2048 -> 4096, o: 4096 -> 2048)
         for name, (n, k) in {"q_proj": (4096, 2048), "o_proj": (2048, 4096)}.items():
             cc = wl.small_dense("km4", n, k, batch=1, seed=1)

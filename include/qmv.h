@@ -194,6 +194,44 @@ qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane,
                     int32_t *ids, float *weights, void *h, float *y, void *stream);
 
 /* ---------------------------------------------------------------------- */
+/* Around the lm_head matvec ["coreai-optimization reference", "The LM     */
+/* head + embeddings": the fused int8 head + argmax kernel path, and the  */
+/* front-end embedding table as a plain int8 per-row dequant-gather].     */
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of workspace qmatvec_argmax needs for N rows and batch B (0 for
+ * invalid sizes). */
+size_t qmatvec_argmax_workspace_bytes(int64_t N, int B);
+
+/* Fused matvec + argmax: for each batch row b, idx[b] = the row n with the
+ * largest y[b][n] = sum_k dequant(W)[n][k] * x[b][k] (fp32 accumulation, as
+ * qmatvec_*), the lowest n among equal largest values, and val[b] = that
+ * y[b][n]. y itself is never written; each wave of the matvec keeps its
+ * best (value, row) and a second launch reduces those. codes/plane as for
+ * qmatvec_* of `fmt`; x fp16 [B][K]; idx int32 [B]; val fp32 [B]; NaN
+ * values are not ordered. 1 <= B <= 8; the shapes of the batch-1..8 dot
+ * product path (K multiple of 32, up to 8192 for 4-bit formats and 4096
+ * for int8, and at B > 2 the register budget of that path; QMV_E_SHAPE
+ * otherwise). workspace >= qmatvec_argmax_workspace_bytes(N, B), 8-byte
+ * aligned. */
+qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
+                          const void *x, int B, int32_t *idx, float *val,
+                          void *workspace, size_t ws_bytes, void *stream);
+
+/* Embedding table packer: W [V][H] (fp16 or fp32) -> codes int8 [V][H] and
+ * one fp16 scale per row: s = fp16(amax / 127), q = clamp(rint(w / s),
+ * -127, 127) (an all-zero row has s = 0, q = 0). */
+qmv_status qpack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H,
+                           int8_t *codes, uint16_t *scale, void *stream);
+
+/* Embedding dequant-gather: out fp16 [T][H], out[t][h] = fp16(codes[ids[t]][h]
+ * * scale[ids[t]]) (exact product, one rounding to nearest even). An id
+ * outside [0, V) yields a zero row. H % 8 == 0, 0 <= T <= 65535 (T == 0 does
+ * nothing; ids and out may then be NULL); codes 8-byte, out 16-byte aligned. */
+qmv_status qembed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H,
+                              const int32_t *ids, int64_t T, void *out, void *stream);
+
+/* ---------------------------------------------------------------------- */
 /* Measurement aid: read `bytes` (a multiple of 16) from buf with 128-bit   */
 /* loads and write one checksum word per workgroup to sink[0..grid); the   */
 /* practical HBM read ceiling for the kernels above. sink must hold        */

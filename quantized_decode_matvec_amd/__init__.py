@@ -26,6 +26,7 @@ EPILOGUES = {"none": QMV_EPI_NONE, "swiglu": QMV_EPI_SWIGLU, "combine": QMV_EPI_
 EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4",
            "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qdequant",
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
+           "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read")
 
 
@@ -62,6 +63,10 @@ def lib() -> ctypes.CDLL:
             "gather_qmatvec_workspace_bytes": ([ci, ci, ci, i64, ci], sz),
             "gather_qmatvec": ([ci, P, P, ci, i64, i64, P, ci, ci, ci, ci, P, P, ci, P, P, sz, P], ci),
             "qmoe_ffn": ([ci, P, P, P, P, ci, i64, i64, P, P, ci, ci, P, P, P, P, P], ci),
+            "qmatvec_argmax_workspace_bytes": ([i64, ci], sz),
+            "qmatvec_argmax": ([ci, P, P, i64, i64, P, ci, P, P, P, sz, P], ci),
+            "qpack_int8_rows": ([P, ci, i64, i64, P, P, P], ci),
+            "qembed_gather_int8": ([P, P, i64, i64, P, i64, P, P], ci),
             "qmv_stream_read_sink_words": ([sz], sz),
             "qmv_stream_read": ([P, sz, P, P], ci),
         }
@@ -264,6 +269,51 @@ def moe_ffn(gu_codes, gu_scale, dn_codes, dn_scale, x, logits, topk, fmt="int4",
     h = gather_qmatvec(fmt, gu_codes, gu_scale, x, ids, epi="swiglu", stream=stream)
     return gather_qmatvec(fmt, dn_codes, dn_scale, h, ids, weights=w, epi="combine", x_per_slot=True,
                           stream=stream), ids, w
+
+
+# ---------------------------------------------------------------- around the lm_head
+
+def qmatvec_argmax_workspace_bytes(N, B):
+    return int(lib().qmatvec_argmax_workspace_bytes(N, B))
+
+
+def qmatvec_argmax(fmt, codes, plane, x, idx=None, val=None, workspace=None, stream=None):
+    """Fused matvec + argmax: (idx int32 [B], val fp32 [B]) of the largest y per batch row."""
+    torch = _torch()
+    N, K = codes.shape[0], _kdim(fmt, codes)
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    B = x2.shape[0]
+    idx = _empty((B,), torch.int32, codes) if idx is None else idx
+    val = _empty((B,), torch.float32, codes) if val is None else val
+    if workspace is None:
+        workspace = _empty((qmatvec_argmax_workspace_bytes(N, B),), torch.uint8, codes)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("qmatvec_argmax", lib().qmatvec_argmax(
+        FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(x2), B, _ptr(idx), _ptr(val),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return idx, val
+
+
+def qpack_int8_rows(W, codes=None, scale=None, stream=None):
+    """Embedding table W [V, H] -> (codes int8 [V, H], scale fp16 bits uint16 [V])."""
+    torch = _torch()
+    V, H = W.shape
+    codes = _empty((V, H), torch.int8, W) if codes is None else codes
+    scale = _empty((V,), torch.uint16, W) if scale is None else scale
+    _check("qpack_int8_rows", lib().qpack_int8_rows(_ptr(W), _dt(W), V, H, _ptr(codes), _ptr(scale),
+                                                    _stream(stream)))
+    return codes, scale
+
+
+def qembed_gather_int8(codes, scale, ids, out=None, stream=None):
+    """out fp16 [T, H] = fp16(codes[ids] * scale[ids])."""
+    torch = _torch()
+    V, H = codes.shape
+    T = ids.numel()
+    out = _empty((T, H), torch.float16, codes) if out is None else out
+    _check("qembed_gather_int8", lib().qembed_gather_int8(_ptr(codes), _ptr(scale), V, H, _ptr(ids), T,
+                                                          _ptr(out), _stream(stream)))
+    return out
 
 
 # ---------------------------------------------------------------- measurement aid

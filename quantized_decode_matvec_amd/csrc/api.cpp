@@ -209,6 +209,44 @@ qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane, 
                                              topk, ids, weights, h, y, as_stream(stream)));
 }
 
+size_t qmatvec_argmax_workspace_bytes(int64_t N, int B) {
+    if (N < 1 || B < 1 || B > 8) return 0;
+    return qmv::argmax_workspace_bytes(N, B);
+}
+
+qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                          int B, int32_t *idx, float *val, void *workspace, size_t ws_bytes, void *stream) {
+    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (!codes || !plane || !x || !idx || !val) return QMV_E_NULL;
+    if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || B < 1 || B > 8) return QMV_E_SHAPE;
+    if (N > (int64_t(1) << 40) / K || !qmv::argmax_supported(fmt, K, B)) return QMV_E_SHAPE;
+    if (!workspace || ws_bytes < qmv::argmax_workspace_bytes(N, B)) return QMV_E_WORKSPACE;
+    if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(idx, 4) ||
+        !aligned(val, 4) || !aligned(workspace, 8))
+        return QMV_E_ALIGN;
+    return launch_status(qmv::launch_matvec_argmax(fmt, codes, plane, N, K, x, B, idx, val, workspace,
+                                                   as_stream(stream)));
+}
+
+qmv_status qpack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, int8_t *codes, uint16_t *scale,
+                           void *stream) {
+    if (!W || !codes || !scale) return QMV_E_NULL;
+    if (wdt != QMV_F16 && wdt != QMV_F32) return QMV_E_DTYPE;
+    if (V < 1 || V > INT32_MAX || H < 1 || V > (int64_t(1) << 40) / H) return QMV_E_SHAPE;
+    if (!aligned(W, wdt == QMV_F16 ? 2 : 4) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_int8_rows(W, wdt, V, H, codes, scale, as_stream(stream)));
+}
+
+qmv_status qembed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H, const int32_t *ids,
+                              int64_t T, void *out, void *stream) {
+    if (!codes || !scale) return QMV_E_NULL;
+    if (V < 1 || H < 8 || H % 8 != 0 || T < 0 || T > 65535 || V > (int64_t(1) << 40) / H) return QMV_E_SHAPE;
+    if (T == 0) return QMV_OK;   // nothing to gather; ids and out may be NULL
+    if (!ids || !out) return QMV_E_NULL;
+    if (!aligned(codes, 8) || !aligned(scale, 2) || !aligned(ids, 4) || !aligned(out, 16)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_embed_gather_int8(codes, scale, V, H, ids, T, out, as_stream(stream)));
+}
+
 size_t qmv_stream_read_sink_words(size_t bytes) { return qmv::stream_read_grid(bytes); }
 
 qmv_status qmv_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {

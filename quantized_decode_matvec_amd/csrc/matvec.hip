@@ -27,11 +27,33 @@ namespace qmv {
 // stretch of the code plane. The x slices are loaded once per wave, so ITERS
 // grows with the batch width to amortize them.
 // ---------------------------------------------------------------------------
-template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK>
+// Argmax keys: the fp32 value in order-preserving form above the complement
+// of the row index, so the largest key is the largest value and, among equal
+// values, the lowest row. Every finite value gives a key above 0.
+__device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, m), hi = __shfl_xor((uint32_t)(k >> 32), m);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
+// ARGMAX: instead of storing y, each wave keeps the largest key per batch row
+// over its rows and writes it to part[wave][b] (the fused lm_head + argmax);
+// waves past the last row write 0.
+template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK, bool ARGMAX = false>
 __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict__ codes,
                                                       const void *__restrict__ plane, int64_t N, int K,
                                                       const _Float16 *__restrict__ x, int B,
-                                                      float *__restrict__ y) {
+                                                      float *__restrict__ y, uint64_t *__restrict__ part = nullptr) {
     constexpr int RPW = kWave / LPR;            // rows per row group
     constexpr int XW = ChunkTraits<FMT>::kXWords;
     constexpr int ROWS_IT = R * RPW;            // rows per iteration
@@ -51,7 +73,15 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     const int nb = K / 32;                                                   // blocks per row
     const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
     const int64_t wrow0 = ((int64_t)blockIdx.x * WAVES + wave) * ROWS_IT * ITERS;
-    if (wrow0 >= N) return;
+    if (wrow0 >= N) {
+        if constexpr (ARGMAX) {
+            if (lane < B) part[((int64_t)blockIdx.x * WAVES + wave) * B + lane] = 0;
+        }
+        return;
+    }
+    uint64_t kbest[ARGMAX ? BT : 1];
+#pragma unroll
+    for (int b = 0; b < (ARGMAX ? BT : 1); b++) kbest[b] = 0;
 
     // Loads of one iteration. Wave-uniform bases, 32-bit per-lane offsets.
     // Loads are unconditional: a row past the end reads row N-1 and a chunk
@@ -172,9 +202,54 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             for (int j = 0; j < Red::live; j++) {
                 int idx = base + j, g = idx / BT, b = idx % BT;
                 int64_t row = row0 + g * RPW + rsub;
-                if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
+                if constexpr (ARGMAX) {
+                    if (row < N) {
+                        const uint64_t key = argmax_key(acc[j], row);
+#pragma unroll
+                        for (int bb = 0; bb < BT; bb++)
+                            if (bb == b && key > kbest[bb]) kbest[bb] = key;
+                    }
+                } else {
+                    if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
+                }
             }
         }
+    }
+    if constexpr (ARGMAX) {
+#pragma unroll
+        for (int bb = 0; bb < BT; bb++) {
+            const uint64_t k = wave_max_u64(kbest[bb]);
+            if (lane == 0 && bb < B) part[((int64_t)blockIdx.x * WAVES + wave) * B + bb] = k;
+        }
+    }
+}
+
+// Largest key over the partials of each batch row -> (index, value). Four
+// independent loads per thread and step keep the reads in flight.
+__global__ __launch_bounds__(1024) void argmax_reduce_kernel(const uint64_t *__restrict__ part, int64_t nparts, int B,
+                                                             int32_t *__restrict__ idx, float *__restrict__ val) {
+    const int b = blockIdx.x;
+    uint64_t k = 0;
+    for (int64_t i0 = threadIdx.x; i0 < nparts; i0 += 4 * 1024) {
+        uint64_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t i = i0 + u * 1024;
+            v[u] = i < nparts ? part[(i < nparts ? i : 0) * B + b] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) k = v[u] > k ? v[u] : k;
+    }
+    k = wave_max_u64(k);
+    __shared__ uint64_t red[16];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < 16; w++) k = red[w] > k ? red[w] : k;
+        const uint32_t hi = (uint32_t)(k >> 32);
+        const uint32_t bits = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
+        idx[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+        val[b] = __builtin_bit_cast(float, bits);
     }
 }
 
@@ -309,35 +384,52 @@ template <int FMT, int BT> struct LaunchShape {
     static constexpr int WAVES = (FMT == KM4) ? 1 : 4;
 };
 
-template <int FMT, int BT, int LPR, int CPL>
+// The argmax epilogue writes one key per wave: waves cover 4x more rows (at
+// least 16) so the reduction that follows reads few keys.
+template <int FMT, int BT, bool ARGMAX> struct ShapeFor : LaunchShape<FMT, BT> {
+    static constexpr int ITERS = ARGMAX ? 4 * LaunchShape<FMT, BT>::ITERS : LaunchShape<FMT, BT>::ITERS;
+};
+
+template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false>
 static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                              float *y, hipStream_t st) {
-    using S = LaunchShape<FMT, BT>;
+                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr) {
+    using S = ShapeFor<FMT, BT, ARGMAX>;
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
+    if (nparts) *nparts = grid * S::WAVES;
     const int cpr = (FMT == INT8) ? K / 16 : K / 32;
     if (cpr == LPR * CPL)
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true>), dim3((unsigned)grid),
-                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, ARGMAX>), dim3((unsigned)grid),
+                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
+                           part);
     else
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false>), dim3((unsigned)grid),
-                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false, ARGMAX>), dim3((unsigned)grid),
+                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
+                           part);
     return hipGetLastError();
 }
 
-template <int FMT, int LPR, int CPL>
+// Register budget for the x slices held per lane (CPL * BT * XW words): the
+// batch widths each (LPR, CPL) shape takes on the dot2 path.
+template <int FMT, int CPL>
+constexpr bool dot2_takes(int B) {
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    return B <= 2 || (B <= 4 && CPL * 4 * XW <= 128) || (B <= 8 && CPL * 8 * XW <= 128);
+}
+
+template <int FMT, int LPR, int CPL, bool ARGMAX = false>
 static hipError_t dispatch_b(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                             float *y, hipStream_t st, bool *handled) {
+                             float *y, hipStream_t st, bool *handled, uint64_t *part = nullptr,
+                             int64_t *nparts = nullptr) {
     *handled = true;
     constexpr int XW = ChunkTraits<FMT>::kXWords;
-    // register budget for x: CPL * BT * XW words
-    if (B == 1) return launch_fast<FMT, 1, LPR, CPL>(codes, plane, N, K, x, B, y, st);
-    if (B == 2) return launch_fast<FMT, 2, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+    if (B == 1) return launch_fast<FMT, 1, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
+    if (B == 2) return launch_fast<FMT, 2, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
     if constexpr (CPL * 4 * XW <= 128) {
-        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
     }
     if constexpr (CPL * 8 * XW <= 128) {
-        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL>(codes, plane, N, K, x, B, y, st);
+        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
     }
     *handled = false;
     return hipSuccess;
@@ -369,6 +461,75 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
         hipLaunchKernelGGL((mv_generic<FMT, float>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
                            reinterpret_cast<const float *>(x), B, y);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fused matvec + argmax: the dot2 kernel with the ARGMAX epilogue writes one
+// key per wave and batch row, then one workgroup per batch row reduces them.
+// ---------------------------------------------------------------------------
+template <int FMT>
+static bool argmax_shape(int K, int B, int *lpr, int *cpl) {
+    const int cpr = K / ChunkTraits<FMT>::kElems;
+    int l, c;
+    if (cpr <= 16) l = 16, c = 1;
+    else if (cpr <= 32) l = 32, c = 1;
+    else if (cpr <= 64) l = 64, c = 1;
+    else if (cpr <= 128) l = 64, c = 2;
+    else if (cpr <= 192) l = 64, c = 3;
+    else if (cpr <= 256) l = 64, c = 4;
+    else return false;
+    const bool ok = c == 1 ? dot2_takes<FMT, 1>(B) : c == 2 ? dot2_takes<FMT, 2>(B)
+                  : c == 3 ? dot2_takes<FMT, 3>(B) : dot2_takes<FMT, 4>(B);
+    if (lpr) *lpr = l;
+    if (cpl) *cpl = c;
+    return ok;
+}
+
+bool argmax_supported(int fmt, int64_t K, int B) {
+    switch (fmt) {
+    case INT4: return argmax_shape<INT4>((int)K, B, nullptr, nullptr);
+    case FP4: return argmax_shape<FP4>((int)K, B, nullptr, nullptr);
+    case INT8: return argmax_shape<INT8>((int)K, B, nullptr, nullptr);
+    default: return argmax_shape<KM4>((int)K, B, nullptr, nullptr);
+    }
+}
+
+// every argmax launch shape covers at least 16 rows per wave; the last
+// workgroup may hold up to 4 waves past the end
+size_t argmax_workspace_bytes(int64_t N, int B) {
+    return (size_t)((N + 15) / 16 + 4) * (size_t)B * sizeof(uint64_t);
+}
+
+template <int FMT>
+static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                             int32_t *idx, float *val, uint64_t *part, hipStream_t st) {
+    int lpr = 0, cpl = 0;
+    if (!argmax_shape<FMT>(K, B, &lpr, &cpl)) return hipErrorInvalidValue;
+    bool handled = false;
+    int64_t nparts = 0;
+    hipError_t err;
+    if (lpr == 16) err = dispatch_b<FMT, 16, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    else if (lpr == 32) err = dispatch_b<FMT, 32, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    else if (cpl == 1) err = dispatch_b<FMT, 64, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    else if (cpl == 2) err = dispatch_b<FMT, 64, 2, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    else if (cpl == 3) err = dispatch_b<FMT, 64, 3, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    else err = dispatch_b<FMT, 64, 4, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    if (err != hipSuccess) return err;
+    if (!handled) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(B), dim3(1024), 0, st, part, nparts, B, idx, val);
+    return hipGetLastError();
+}
+
+hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                                int B, int32_t *idx, float *val, void *workspace, hipStream_t st) {
+    const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
+    uint64_t *part = reinterpret_cast<uint64_t *>(workspace);
+    switch (fmt) {
+    case INT4: return argmax_fmt<INT4>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    case FP4: return argmax_fmt<FP4>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    case INT8: return argmax_fmt<INT8>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    default: return argmax_fmt<KM4>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    }
 }
 
 hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,

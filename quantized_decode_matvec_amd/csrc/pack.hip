@@ -398,6 +398,42 @@ hipError_t launch_pack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Embedding table: int8 with one fp16 scale per row ("coreai-optimization
+// reference", "The LM head + embeddings": plain int8 per-row dequant-gather).
+// One workgroup per row: amax over the row, s = fp16(amax / 127), q =
+// clamp(rint(w / s), -127, 127), each step one IEEE operation.
+// ---------------------------------------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(256) void pack_int8_rows_kernel(const WT *__restrict__ W, int64_t H,
+                                                             int8_t *__restrict__ codes, uint16_t *__restrict__ scale) {
+    const int64_t v = blockIdx.x;
+    const WT *w = W + v * H;
+    float amax = 0.0f;
+    for (int64_t h = threadIdx.x; h < H; h += 256) amax = __builtin_fmaxf(amax, __builtin_fabsf((float)w[h]));
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m));
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+    const float s = f16_bits_to_f32(s16);
+    if (threadIdx.x == 0) scale[v] = s16;
+    for (int64_t h = threadIdx.x; h < H; h += 256) codes[v * H + h] = (int8_t)quant_q<127>((float)w[h], s);
+}
+
+hipError_t launch_pack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, int8_t *codes, uint16_t *scale,
+                                 hipStream_t st) {
+    if (wdt == QMV_F16)
+        hipLaunchKernelGGL(pack_int8_rows_kernel<_Float16>, dim3((unsigned)V), dim3(256), 0, st,
+                           reinterpret_cast<const _Float16 *>(W), H, codes, scale);
+    else
+        hipLaunchKernelGGL(pack_int8_rows_kernel<float>, dim3((unsigned)V), dim3(256), 0, st,
+                           reinterpret_cast<const float *>(W), H, codes, scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint8_t *scale,
                            hipStream_t st) {
     if (wdt == QMV_F16)

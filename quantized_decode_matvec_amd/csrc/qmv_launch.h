@@ -18,6 +18,14 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
 // batched matrix-core path; *handled is false when the shape is not one it takes
 hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
                               int B, float *y, hipStream_t st, bool *handled);
+bool argmax_supported(int fmt, int64_t K, int B);
+size_t argmax_workspace_bytes(int64_t N, int B);
+hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                                int B, int32_t *idx, float *val, void *workspace, hipStream_t st);
+hipError_t launch_pack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, int8_t *codes, uint16_t *scale,
+                                 hipStream_t st);
+hipError_t launch_embed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H,
+                                    const int32_t *ids, int64_t T, void *out, hipStream_t st);
 hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *out,
                           hipStream_t st);
 size_t stream_read_grid(size_t bytes);

@@ -108,3 +108,27 @@ def test_dequant_and_moe_validation(L):
     assert call(a0=2, a7=8192) == E_SHAPE
     assert call(a14=ODD) == E_ALIGN
     assert L.qmv_stream_read(FAKE, 24, FAKE, S) == E_SHAPE
+
+
+def test_argmax_and_embedding_validation(L):
+    A = L.qmatvec_argmax
+    ws = L.qmatvec_argmax_workspace_bytes(1000, 2)
+    assert ws >= (1000 // 16) * 2 * 8
+    assert L.qmatvec_argmax_workspace_bytes(1000, 9) == 0
+    # B > 8, K = 8192 int4 at B = 8 (beyond the dot-path register budget), missing workspace, misaligned x
+    assert A(0, FAKE, FAKE, 1000, 2048, FAKE, 9, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
+    assert A(0, FAKE, FAKE, 1000, 8192, FAKE, 8, FAKE, FAKE, FAKE, 1 << 30, S) == E_SHAPE
+    assert A(3, FAKE, FAKE, 1000, 2048, FAKE, 2, FAKE, FAKE, NUL, 0, S) == E_WORKSPACE
+    assert A(3, FAKE, FAKE, 1000, 2048, FAKE, 2, FAKE, FAKE, FAKE, ws - 8, S) == E_WORKSPACE
+    assert A(3, FAKE, FAKE, 1000, 2048, ODD, 2, FAKE, FAKE, FAKE, ws, S) == E_ALIGN
+    assert A(3, FAKE, FAKE, 1000, 2048, NUL, 2, FAKE, FAKE, FAKE, ws, S) == E_NULL
+    # embedding: H not a multiple of 8, negative T, misaligned out, null scale
+    G = L.qembed_gather_int8
+    assert G(FAKE, FAKE, 100, 12, FAKE, 3, FAKE, S) == E_SHAPE
+    assert G(FAKE, FAKE, 100, 16, FAKE, -1, FAKE, S) == E_SHAPE
+    assert G(FAKE, FAKE, 100, 16, FAKE, 3, ODD, S) == E_ALIGN
+    assert G(FAKE, NUL, 100, 16, FAKE, 3, FAKE, S) == E_NULL
+    assert G(FAKE, FAKE, 100, 16, NUL, 3, FAKE, S) == E_NULL
+    assert G(FAKE, FAKE, 100, 16, NUL, 0, NUL, S) == 0          # T = 0: nothing to do
+    assert L.qpack_int8_rows(FAKE, 5, 10, 16, FAKE, FAKE, S) == E_DTYPE
+    assert L.qpack_int8_rows(FAKE, 0, 0, 16, FAKE, FAKE, S) == E_SHAPE
