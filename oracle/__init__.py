@@ -27,8 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT_INT4, FMT_FP4, FMT_INT8, FMT_KM4 = 0, 1, 2, 3
-FORMATS = {"int4": FMT_INT4, "fp4": FMT_FP4, "int8": FMT_INT8, "km4": FMT_KM4}
+FMT_INT4, FMT_FP4, FMT_INT8, FMT_KM4, FMT_INT4AFF = 0, 1, 2, 3, 4
+FORMATS = {"int4": FMT_INT4, "fp4": FMT_FP4, "int8": FMT_INT8, "km4": FMT_KM4, "int4aff": FMT_INT4AFF}
 
 _lib = None
 
@@ -60,6 +60,7 @@ def lib():
         L.orc_pack_fp4.argtypes = [P, i64, i64, P, P]
         L.orc_pack_int4.argtypes = [P, i64, i64, ci, P, P]
         L.orc_pack_int8.argtypes = [P, i64, i64, P, P]
+        L.orc_pack_int4aff.argtypes = [P, i64, i64, P, P]
         L.orc_pack_km4.argtypes = [P, i64, i64, ci, P, P, P]
         L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
@@ -137,6 +138,17 @@ def pack_int8(W):
     return codes, scale
 
 
+def pack_int4aff(W):
+    """codes [N, K/2] uint8 (u in 0..15, element 2j low nibble), plane [N, K/32]
+    uint32 (fp16 scale low half, fp16 bias high half)."""
+    W = _as_f32(W)
+    N, K = _check_shape(W)
+    codes = np.zeros((N, K // 2), np.uint8)
+    plane = np.zeros((N, K // 32), np.uint32)
+    lib().orc_pack_int4aff(_p(W), N, K, _p(codes), _p(plane))
+    return codes, plane
+
+
 def pack_km4(W_f16, max_iter: int = 20, return_iters: bool = False):
     W = np.ascontiguousarray(np.asarray(W_f16, dtype=np.float16)).view(np.uint16)
     N, K = _check_shape(W)
@@ -150,7 +162,8 @@ def pack_km4(W_f16, max_iter: int = 20, return_iters: bool = False):
 
 
 def pack(fmt: str, W, **kw):
-    return {"int4": pack_int4, "fp4": pack_fp4, "int8": pack_int8, "km4": pack_km4}[fmt](W, **kw)
+    return {"int4": pack_int4, "fp4": pack_fp4, "int8": pack_int8, "km4": pack_km4,
+            "int4aff": pack_int4aff}[fmt](W, **kw)
 
 
 # --- dequant and matvec ---

@@ -249,6 +249,49 @@ void orc_pack_int8(const float *W, int64_t N, int64_t K, int8_t *codes, uint16_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Affine int4 per block of 32 [S1 section 1: the production MoE gather      */
+/* formats include affine int4 with a scale and a bias per 32-block; S2      */
+/* section 8: fp4 is that affine structure without the bias].               */
+/* ------------------------------------------------------------------------ */
+
+/* Reading: min-max affine, every step one fp32 operation:
+     b = fp16(min), s = fp16((max - min) / 15),
+     u = clamp(rint((w - b) / s), 0, 15)   (s == 0: u = 0),
+   dequant w' = s * u + b. Plane: one 32-bit word per block with the fp16
+   scale in the low half and the fp16 bias in the high half. Codes as int4:
+   element 2j in the low nibble of byte j. */
+void orc_pack_int4aff(const float *W, int64_t N, int64_t K, uint8_t *codes, uint32_t *plane)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t blk = 0; blk < K / 32; blk++) {
+            const float *w = W + n * K + blk * 32;
+            float mn = w[0], mx = w[0];
+            for (int k = 1; k < 32; k++) {
+                if (w[k] < mn) mn = w[k];
+                if (w[k] > mx) mx = w[k];
+            }
+            uint16_t s16 = orc_f64_to_f16((double)((mx - mn) / 15.0f));
+            uint16_t b16 = orc_f64_to_f16((double)mn);
+            float s = (float)orc_f16_to_f64(s16), b = (float)orc_f16_to_f64(b16);
+            plane[n * (K / 32) + blk] = (uint32_t)s16 | ((uint32_t)b16 << 16);
+            int u[32];
+            for (int k = 0; k < 32; k++) {
+                float r = 0.0f;
+                if (s != 0.0f) {
+                    r = rintf((w[k] - b) / s);
+                    if (r < 0.0f) r = 0.0f;
+                    if (r > 15.0f) r = 15.0f;
+                }
+                u[k] = (int)r;
+            }
+            for (int j = 0; j < 16; j++)
+                codes[n * (K / 2) + blk * 16 + j] = (uint8_t)(u[2 * j] | (u[2 * j + 1] << 4));
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Embedding table: int8 with one fp16 scale per row, and its dequant-gather */
 /* [S3 "The LM head + embeddings": the front-end table gather is a plain     */
 /* int8 per-row dequant-gather, q[ids] as fp16 times scale[ids]].            */
@@ -450,6 +493,10 @@ static double dequant_one(int fmt, const void *codes, const void *plane, int64_t
         double v = ldexp(mag, (int)e[n * (K / 32) + k / 32] - 127);
         return (c & 8) ? -v : v;
     }
+    if (fmt == 4) {
+        const uint32_t word = ((const uint32_t *)plane)[n * (K / 32) + k / 32];
+        return orc_f16_to_f64((uint16_t)(word & 0xFFFF)) * (double)c + orc_f16_to_f64((uint16_t)(word >> 16));
+    }
     /* km4 */
     const uint16_t *lut = (const uint16_t *)plane;
     return orc_f16_to_f64(lut[n * 16 + c]);
@@ -515,12 +562,13 @@ void orc_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, do
 }
 
 /* Bytes of one row of codes, and of one row of the scale / table plane,
-   for a K-long row in format fmt (0 int4, 1 fp4, 2 int8, 3 km4). */
+   for a K-long row in format fmt (0 int4, 1 fp4, 2 int8, 3 km4, 4 int4aff). */
 static int64_t code_row_bytes(int fmt, int64_t K) { return fmt == 2 ? K : K / 2; }
 static int64_t plane_row_bytes(int fmt, int64_t K)
 {
     if (fmt == 1) return K / 32;      /* one e8m0 byte per block */
     if (fmt == 3) return 32;          /* sixteen fp16 table entries */
+    if (fmt == 4) return 4 * (K / 32);   /* fp16 scale + fp16 bias per block */
     return 2 * (K / 32);              /* one fp16 scale per block */
 }
 

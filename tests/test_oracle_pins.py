@@ -399,7 +399,7 @@ def test_km4_gaussian_reaches_lloyd_max_levels():
 # matvec
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff"])
 def test_matvec_equals_dense_fp64_matmul(fmt):
     rng = np.random.default_rng(8)
     W = (rng.standard_normal((37, 96)) * 0.02).astype(np.float16)
@@ -458,7 +458,7 @@ def _small_moe(seed=12, E=6, H=64, I=32, fmt="int4"):
             dnc.reshape(E, H, -1), dns.reshape(E, H, -1), rng)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff"])
 def test_moe_top1_reduces_to_one_expert_ffn(fmt):
     """One slot of weight 1 is that expert's SwiGLU FFN (numpy GEMVs over the
     dequantized slabs); the last expert catches a wrong per-expert stride, and
@@ -565,7 +565,7 @@ def test_embed_gather_equals_numpy_fp16_product():
     assert np.array_equal(out, want.view(np.uint16))
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4"])
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff"])
 def test_matvec_argmax_picks_the_lowest_index_among_equal_maxima(fmt):
     """The argmax of the fp64 products equals numpy's on a numpy GEMM of the
     dequantized matrix; two identical winning rows give the lower index."""
@@ -579,3 +579,65 @@ def test_matvec_argmax_picks_the_lowest_index_among_equal_maxima(fmt):
     assert idx[0] == 17
     assert np.array_equal(idx, np.argmax(ref, axis=1))
     assert np.allclose(val, ref.max(axis=1), rtol=1e-12, atol=0)
+
+
+# --- affine int4 (scale and bias per 32-block) ---
+
+def test_int4aff_golden_blocks():
+    seen = 0
+    for name, nz, word, bytes_hex in _records("int4aff_blocks.txt"):
+        w = np.zeros((1, 32), np.float32)
+        for item in nz.split(","):
+            i, h = item.split("=")
+            v = np.array(int(h, 16), np.uint32).view(np.float32)
+            if i == "all":
+                w[0, :] = v
+            else:
+                w[0, int(i)] = v
+        codes, plane = oracle.pack_int4aff(w)
+        assert plane[0, 0] == int(word, 16), name
+        want = bytes.fromhex(bytes_hex)
+        assert codes[0, :len(want)].tobytes() == want, name
+        seen += 1
+    assert seen == 2
+    w = np.zeros((1, 32), np.float32)
+    w[0, :3] = [-0.5, 0.25, 1.0]
+    d = oracle.dequant("int4aff", *oracle.pack_int4aff(w))[0]
+    s = np.float64(np.array(0x2E66, np.uint16).view(np.float16))
+    assert d[0] == -0.5 and d[1] == 8 * s - 0.5 and d[2] == 15 * s - 0.5 and d[3] == 5 * s - 0.5
+
+
+def test_int4aff_equals_numpy_minmax():
+    """The packer equals the min-max affine recipe computed with numpy's fp32
+    operations and fp16 casts, over random blocks, a constant block and
+    blocks with a large outlier."""
+    rng = np.random.default_rng(41)
+    W = (rng.standard_normal((30, 256)) * 0.03).astype(np.float32)
+    W[2, :32] = 0.125
+    W[3, 40] = 5.0
+    B = W.reshape(30, -1, 32)
+    mn, mx = B.min(-1, keepdims=True), B.max(-1, keepdims=True)
+    s = ((mx - mn) / np.float32(15)).astype(np.float16)
+    b = mn.astype(np.float16)
+    sf, bf = s.astype(np.float32), b.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(sf == 0, 0, np.clip(np.rint((B - bf) / sf), 0, 15)).astype(np.int64).reshape(30, 256)
+    codes, plane = oracle.pack_int4aff(W)
+    assert np.array_equal(_unpack_nibbles(codes), u)
+    word = s[..., 0].view(np.uint16).astype(np.uint32) | (b[..., 0].view(np.uint16).astype(np.uint32) << 16)
+    assert np.array_equal(plane, word)
+
+
+def test_int4aff_reconstruction_error_is_half_a_step():
+    """Every reconstructed value lies within half a step (plus the fp16
+    rounding of the bias) of its input."""
+    rng = np.random.default_rng(42)
+    W = (rng.standard_normal((20, 512)) * 0.05).astype(np.float32)
+    codes, plane = oracle.pack_int4aff(W)
+    D = oracle.dequant("int4aff", codes, plane)
+    s = (plane & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    b = (plane >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    mn = W.reshape(20, -1, 32).min(-1).astype(np.float64)
+    bound = 0.5 * s + np.abs(b - mn) + 1e-6 * s
+    err = np.abs(D - W).reshape(20, -1, 32).max(-1)
+    assert np.all(err <= bound)
