@@ -36,7 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 def algo_bytes(fmt, N, K):
     """Bytes a call must read from HBM: code plane plus scale/table plane."""
     codes = N * K if fmt == "int8" else N * K // 2
-    plane = {"int4": N * (K // 32) * 2, "int8": N * (K // 32) * 2, "fp4": N * (K // 32), "km4": N * 16 * 2}[fmt]
+    plane = {"int4": N * (K // 32) * 2, "int8": N * (K // 32) * 2, "fp4": N * (K // 32), "km4": N * 16 * 2,
+             "int4aff": N * (K // 32) * 4}[fmt]
     return codes + plane
 
 
@@ -229,7 +230,7 @@ def main():
         extras["km4_B8_us"] = round(ms8 * 1e3, 2)
         extras["km4_B8_GBps"] = round(nbytes / (ms8 * 1e-3) / 1e9, 1)
 
-        for fmt in ("fp4", "int4"):
+        for fmt in ("fp4", "int4", "int4aff"):
             pk = [qmv.qpack(fmt, W)]
             pk += [(a.clone(), b.clone()) for a, b in [pk[0]] * (len(copies) - 1)]
             msf = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x1, y=y[:1]),

@@ -62,7 +62,7 @@ typedef enum {
 } qmv_status;
 
 typedef enum { QMV_F32 = 0, QMV_F16 = 1 } qmv_dtype;
-typedef enum { QMV_INT4 = 0, QMV_FP4 = 1, QMV_INT8 = 2, QMV_KM4 = 3 } qmv_format;
+typedef enum { QMV_INT4 = 0, QMV_FP4 = 1, QMV_INT8 = 2, QMV_KM4 = 3, QMV_INT4AFF = 4 } qmv_format;
 typedef enum { QMV_EPI_NONE = 0, QMV_EPI_SWIGLU = 1, QMV_EPI_COMBINE = 2 } qmv_epilogue;
 
 /* Static string naming a status (never NULL). */
@@ -112,6 +112,16 @@ qmv_status qpack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
 qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
                      uint8_t *codes, uint16_t *lut, void *stream);
 
+/* Affine int4 per block of 32 with an fp16 scale and an fp16 bias [S1 sec. 1:
+ * affine int4, block 32, among the production MoE gather formats; S2 sec. 8:
+ * fp4 is that affine structure without the bias]. Min-max, fp32 steps:
+ * b = fp16(min), s = fp16((max - min) / 15), u = clamp(rint((w - b)/s), 0, 15)
+ * (s == 0: u = 0). Outputs: codes [N][K/2] of u (element 2j in the low
+ * nibble); plane [N][K/32] 32-bit words, fp16 scale in the low half and fp16
+ * bias in the high half. Dequant: s * u + b. */
+qmv_status qpack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
+                         uint8_t *codes, uint32_t *plane, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Fused dequantize-matvec [S2 secs. 1 and 8: the fused 4-bit decode       */
 /* matvec; the same kernel structure for every format, only the dequant    */
@@ -128,9 +138,12 @@ qmv_status qmatvec_int8(const int8_t *codes, const uint16_t *scale, int64_t N, i
                         const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K,
+                           const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 
 /* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
- * weight is exact in fp32) [S3 "Theoretical size" for the plane shapes]. */
+ * weight is exact in fp32, except affine int4, where s * u + b is rounded
+ * once to the nearest fp32) [S3 "Theoretical size" for the plane shapes]. */
 qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
                     float *W_hat, void *stream);
 

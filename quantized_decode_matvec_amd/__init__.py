@@ -17,14 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqmv.so")
 
 QMV_F32, QMV_F16 = 0, 1
-QMV_INT4, QMV_FP4, QMV_INT8, QMV_KM4 = 0, 1, 2, 3
+QMV_INT4, QMV_FP4, QMV_INT8, QMV_KM4, QMV_INT4AFF = 0, 1, 2, 3, 4
 QMV_EPI_NONE, QMV_EPI_SWIGLU, QMV_EPI_COMBINE = 0, 1, 2
-FORMATS = {"int4": QMV_INT4, "fp4": QMV_FP4, "int8": QMV_INT8, "km4": QMV_KM4}
+FORMATS = {"int4": QMV_INT4, "fp4": QMV_FP4, "int8": QMV_INT8, "km4": QMV_KM4, "int4aff": QMV_INT4AFF}
 EPILOGUES = {"none": QMV_EPI_NONE, "swiglu": QMV_EPI_SWIGLU, "combine": QMV_EPI_COMBINE}
 
 # every symbol include/qmv.h declares
-EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4",
-           "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qdequant",
+EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4", "qpack_int4aff",
+           "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff", "qdequant",
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read")
@@ -54,10 +54,12 @@ def lib() -> ctypes.CDLL:
             "qpack_fp4": ([P, ci, i64, i64, P, P, P], ci),
             "qpack_int8": ([P, ci, i64, i64, P, P, P], ci),
             "qpack_km4": ([P, i64, i64, ci, P, P, P], ci),
+            "qpack_int4aff": ([P, ci, i64, i64, P, P, P], ci),
             "qmatvec_int4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_fp4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_int8": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_km4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
+            "qmatvec_int4aff": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qdequant": ([ci, P, P, i64, i64, P, P], ci),
             "qmoe_route": ([P, ci, ci, ci, P, P, P], ci),
             "gather_qmatvec_workspace_bytes": ([ci, ci, ci, i64, ci], sz),
@@ -152,8 +154,19 @@ def qpack_km4(W, max_iter=20, codes=None, lut=None, stream=None):
     return codes, lut
 
 
+def qpack_int4aff(W, codes=None, plane=None, stream=None):
+    """W [N, K] -> (codes uint8 [N, K/2], plane uint32-as-int32 [N, K/32]: fp16 scale | fp16 bias << 16)."""
+    torch = _torch()
+    N, K = W.shape
+    codes = _empty((N, K // 2), torch.uint8, W) if codes is None else codes
+    plane = _empty((N, K // 32), torch.int32, W) if plane is None else plane
+    _check("qpack_int4aff", lib().qpack_int4aff(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(plane), _stream(stream)))
+    return codes, plane
+
+
 def qpack(fmt, W, **kw):
-    return {"int4": qpack_int4, "fp4": qpack_fp4, "int8": qpack_int8, "km4": qpack_km4}[fmt](W, **kw)
+    return {"int4": qpack_int4, "fp4": qpack_fp4, "int8": qpack_int8, "km4": qpack_km4,
+            "int4aff": qpack_int4aff}[fmt](W, **kw)
 
 
 # ---------------------------------------------------------------- matvec
@@ -187,6 +200,10 @@ def qmatvec_int8(codes, scale, x, y=None, stream=None):
 
 def qmatvec_km4(codes, lut, x, y=None, stream=None):
     return _matvec("qmatvec_km4", "km4", codes, lut, x, y, stream)
+
+
+def qmatvec_int4aff(codes, plane, x, y=None, stream=None):
+    return _matvec("qmatvec_int4aff", "int4aff", codes, plane, x, y, stream)
 
 
 def qmatvec(fmt, codes, plane, x, y=None, stream=None):

@@ -59,7 +59,8 @@ int64_t gather_max_k(qmv_format f) { return f == QMV_INT8 ? 4096 : 8192; }
 size_t plane_alignment(qmv_format f) {
     switch (f) {
     case QMV_FP4: return 1;
-    case QMV_KM4: return 4;   // tables are read as 32-bit words
+    case QMV_KM4: return 4;       // tables are read as 32-bit words
+    case QMV_INT4AFF: return 4;   // one 32-bit scale + bias word per block
     default: return 2;
     }
 }
@@ -108,6 +109,15 @@ qmv_status qpack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, int8_t
     return launch_status(qmv::launch_pack_int8(W, wdt, N, K, codes, scale, as_stream(stream)));
 }
 
+qmv_status qpack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint32_t *plane,
+                         void *stream) {
+    qmv_status s = check_wk(W, wdt, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !plane) return QMV_E_NULL;
+    if (!aligned(codes, 16) || !aligned(plane, 4)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_int4aff(W, wdt, N, K, codes, plane, as_stream(stream)));
+}
+
 qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
                      void *stream) {
     qmv_status s = check_wk(W_f16, QMV_F16, N, K);
@@ -146,9 +156,16 @@ qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int
     return launch_status(qmv::launch_matvec(QMV_KM4, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
+qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K, const void *x,
+                           qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, plane, 4, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    return launch_status(qmv::launch_matvec(QMV_INT4AFF, codes, plane, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
 qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *W_hat,
                     void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
     if (!codes || !plane || !W_hat) return QMV_E_NULL;
     if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(W_hat, 16)) return QMV_E_ALIGN;
@@ -171,7 +188,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
                           const void *x, qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids,
                           const float *weights, qmv_epilogue epi, void *y, void *workspace, size_t ws_bytes,
                           void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
     if (epi != QMV_EPI_NONE && epi != QMV_EPI_SWIGLU && epi != QMV_EPI_COMBINE) return QMV_E_DTYPE;
     if (xdt != QMV_F16) return QMV_E_DTYPE;
     if (!codes || !plane || !x || !ids || !y) return QMV_E_NULL;
@@ -194,7 +211,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
 qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane, const void *dn_codes,
                     const void *dn_plane, int E, int64_t H, int64_t I, const float *logits, const void *x, int T,
                     int topk, int32_t *ids, float *weights, void *h, float *y, void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
     if (!gu_codes || !gu_plane || !dn_codes || !dn_plane || !logits || !x || !ids || !weights || !h || !y)
         return QMV_E_NULL;
     if (E < 1 || E > 4096 || T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
@@ -216,7 +233,7 @@ size_t qmatvec_argmax_workspace_bytes(int64_t N, int B) {
 
 qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                           int B, int32_t *idx, float *val, void *workspace, size_t ws_bytes, void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_KM4) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
     if (!codes || !plane || !x || !idx || !val) return QMV_E_NULL;
     if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || B < 1 || B > 8) return QMV_E_SHAPE;
     if (N > (int64_t(1) << 40) / K || !qmv::argmax_supported(fmt, K, B)) return QMV_E_SHAPE;

@@ -87,8 +87,10 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     // Loads are unconditional: a row past the end reads row N-1 and a chunk
     // past the end of the row reads chunk 0; their x slices are zero and their
     // rows are never stored, so they contribute nothing.
+    constexpr bool AFF = (FMT == INT4AFF);
     uint4 cw[R][CPL];
     float sc[R][CPL];
+    float bi[AFF ? R : 1][AFF ? CPL : 1];   // affine bias per block
     uint32_t lutv[LUT_PER_LANE];
     auto issue_loads = [&](int64_t row0) {
         const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);   // last valid row offset
@@ -109,6 +111,11 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 } else if constexpr (FMT == FP4) {
                     const uint8_t *s = reinterpret_cast<const uint8_t *>(plane) + row0 * nb;
                     sc[g][j] = e8m0_to_f32(s[(uint32_t)rr * (uint32_t)nb + (uint32_t)cc]);
+                } else if constexpr (AFF) {
+                    const uint32_t *s = reinterpret_cast<const uint32_t *>(plane) + row0 * nb;
+                    const uint32_t wd = s[(uint32_t)rr * (uint32_t)nb + (uint32_t)cc];
+                    sc[g][j] = f16_bits_to_f32((uint16_t)(wd & 0xFFFFu));
+                    bi[g][j] = f16_bits_to_f32((uint16_t)(wd >> 16));
                 } else {
                     sc[g][j] = 1.f;
                 }
@@ -137,6 +144,14 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             load_x_slice<FMT>(x + (size_t)(b < B ? b : 0) * K, c, (FULLK || c < cpr) && (BT == 1 || b < B),
                               xr[j][b]);
     }
+    // affine blocks add bias * (sum of the block's x)
+    float xsum[AFF ? CPL : 1][AFF ? BT : 1];
+    if constexpr (AFF) {
+#pragma unroll
+        for (int j = 0; j < CPL; j++)
+#pragma unroll
+            for (int b = 0; b < BT; b++) xsum[j][b] = x_slice_sum<XW>(xr[j][b]);
+    }
 
     issue_loads(wrow0);
 #pragma unroll 1
@@ -147,12 +162,14 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
         // they are in flight while this one computes
         uint4 cwc[R][CPL];
         float scc[R][CPL];
+        float bic[AFF ? R : 1][AFF ? CPL : 1];
 #pragma unroll
         for (int g = 0; g < R; g++)
 #pragma unroll
             for (int j = 0; j < CPL; j++) {
                 cwc[g][j] = cw[g][j];
                 scc[g][j] = sc[g][j];
+                if constexpr (AFF) bic[g][j] = bi[g][j];
             }
         _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
         if constexpr (FMT == KM4) {
@@ -178,12 +195,14 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 for (int j = 0; j < CPL; j++) {
                     float d;
                     if constexpr (FMT == INT4) d = chunk_dot_int4(cwc[g][j], xr[j][b]);
+                    else if constexpr (AFF) d = chunk_dot_int4<true>(cwc[g][j], xr[j][b]);
                     else if constexpr (FMT == FP4) d = chunk_dot_fp4(cwc[g][j], xr[j][b]);
                     else if constexpr (FMT == INT8) d = chunk_dot_int8(cwc[g][j], xr[j][b]);
                     else if constexpr (KM4_IMM)
                         d = chunk_dot_km4_imm(cwc[g][j], reinterpret_cast<const char *>(lut_lds) + g * 32, xr[j][b]);
                     else d = chunk_dot_km4(cwc[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
                     a = (FMT == KM4) ? a + d : __builtin_fmaf(d, scc[g][j], a);
+                    if constexpr (AFF) a = __builtin_fmaf(xsum[j][b], bic[g][j], a);
                 }
                 acc[g * BT + b] = a;
             }
@@ -289,6 +308,14 @@ __device__ __forceinline__ void decode_chunk_f32(const uint8_t *__restrict__ cod
             for (int d = 0; d < 4; d++)
 #pragma unroll
                 for (int i = 0; i < 8; i++) w[8 * d + i] = s * (float)((int)((wd[d] >> (4 * i)) & 15u) - 8);
+        } else if constexpr (FMT == INT4AFF) {
+            // s * u + b with one rounding (the fp32 value nearest the exact one)
+            const uint32_t sb = reinterpret_cast<const uint32_t *>(plane)[row * nb + c];
+            const float s = f16_bits_to_f32((uint16_t)(sb & 0xFFFFu)), b = f16_bits_to_f32((uint16_t)(sb >> 16));
+#pragma unroll
+            for (int d = 0; d < 4; d++)
+#pragma unroll
+                for (int i = 0; i < 8; i++) w[8 * d + i] = __builtin_fmaf(s, (float)((wd[d] >> (4 * i)) & 15u), b);
         } else {
             const uint16_t *lut = reinterpret_cast<const uint16_t *>(plane) + row * 16;
 #pragma unroll
@@ -488,6 +515,7 @@ static bool argmax_shape(int K, int B, int *lpr, int *cpl) {
 bool argmax_supported(int fmt, int64_t K, int B) {
     switch (fmt) {
     case INT4: return argmax_shape<INT4>((int)K, B, nullptr, nullptr);
+    case INT4AFF: return argmax_shape<INT4AFF>((int)K, B, nullptr, nullptr);
     case FP4: return argmax_shape<FP4>((int)K, B, nullptr, nullptr);
     case INT8: return argmax_shape<INT8>((int)K, B, nullptr, nullptr);
     default: return argmax_shape<KM4>((int)K, B, nullptr, nullptr);
@@ -526,6 +554,7 @@ hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, i
     uint64_t *part = reinterpret_cast<uint64_t *>(workspace);
     switch (fmt) {
     case INT4: return argmax_fmt<INT4>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    case INT4AFF: return argmax_fmt<INT4AFF>(c, plane, N, (int)K, x, B, idx, val, part, st);
     case FP4: return argmax_fmt<FP4>(c, plane, N, (int)K, x, B, idx, val, part, st);
     case INT8: return argmax_fmt<INT8>(c, plane, N, (int)K, x, B, idx, val, part, st);
     default: return argmax_fmt<KM4>(c, plane, N, (int)K, x, B, idx, val, part, st);
@@ -537,6 +566,7 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
     const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
     switch (fmt) {
     case INT4: return matvec_fmt<INT4>(c, plane, N, (int)K, x, xdt, B, y, st);
+    case INT4AFF: return matvec_fmt<INT4AFF>(c, plane, N, (int)K, x, xdt, B, y, st);
     case FP4: return matvec_fmt<FP4>(c, plane, N, (int)K, x, xdt, B, y, st);
     case INT8: return matvec_fmt<INT8>(c, plane, N, (int)K, x, xdt, B, y, st);
     default: return matvec_fmt<KM4>(c, plane, N, (int)K, x, xdt, B, y, st);
@@ -550,6 +580,9 @@ hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t
     int grid = (int)((blocks + 255) / 256);
     switch (fmt) {
     case INT4: hipLaunchKernelGGL(dequant_kernel<INT4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
+    case INT4AFF:
+        hipLaunchKernelGGL(dequant_kernel<INT4AFF>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out);
+        break;
     case FP4: hipLaunchKernelGGL(dequant_kernel<FP4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
     case INT8: hipLaunchKernelGGL(dequant_kernel<INT8>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
     default: hipLaunchKernelGGL(dequant_kernel<KM4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;

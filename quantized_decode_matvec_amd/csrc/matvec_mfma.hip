@@ -393,14 +393,15 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
     return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
 }
 
-// The batched matrix-core path takes fp16 x, 3 <= B <= 8 (km4: 5 <= B; below
-// that the dot2 path is as fast), whole load steps (K % 512 == 0, int8
+// The batched matrix-core path takes int4, fp4, int8 and km4 (not affine
+// int4), fp16 x, 3 <= B <= 8 (km4: 5 <= B; below that the dot2 path is as
+// fast), whole load steps (K % 512 == 0, int8
 // K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned scale plane, and
 // staging that fits in 64 KiB of LDS.
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
     // km4 table lookups from 16 rows at once meet LDS bank conflicts; below
     // B = 5 its dot2 path (one row's table per instruction) is faster
-    if (B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
+    if (fmt == INT4AFF || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
     if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;

@@ -142,9 +142,20 @@ __device__ __forceinline__ float plane_scale(const void *plane, int64_t row, int
         return f16_bits_to_f32(reinterpret_cast<const uint16_t *>(plane)[row * nb + blk]);
     } else if constexpr (FMT == FP4) {
         return e8m0_to_f32(reinterpret_cast<const uint8_t *>(plane)[row * nb + c]);
+    } else if constexpr (FMT == INT4AFF) {
+        return f16_bits_to_f32((uint16_t)(reinterpret_cast<const uint32_t *>(plane)[row * nb + c] & 0xFFFFu));
     } else {
         return 1.f;
     }
+}
+
+// affine int4: the block's bias (it multiplies the block's x sum)
+template <int FMT>
+__device__ __forceinline__ float plane_bias(const void *plane, int64_t row, int nb, int c) {
+    if constexpr (FMT == INT4AFF)
+        return f16_bits_to_f32((uint16_t)(reinterpret_cast<const uint32_t *>(plane)[row * nb + c] >> 16));
+    else
+        return 0.f;
 }
 
 template <int FMT>
@@ -159,6 +170,8 @@ __device__ __forceinline__ void expert_slabs(const uint8_t *codes, const void *p
         plane_e = reinterpret_cast<const uint8_t *>(plane) + e * N * (K / 32);
     else if constexpr (FMT == KM4)
         plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * 16;
+    else if constexpr (FMT == INT4AFF)
+        plane_e = reinterpret_cast<const uint32_t *>(plane) + e * N * (K / 32);
     else
         plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * (K / 32);
 }
@@ -167,6 +180,7 @@ template <int FMT>
 __device__ __forceinline__ float chunk_dot(uint4 cw, const uint32_t (&xw)[ChunkTraits<FMT>::kXWords],
                                            const _Float16 *lut) {
     if constexpr (FMT == INT4) return chunk_dot_int4(cw, xw);
+    else if constexpr (FMT == INT4AFF) return chunk_dot_int4<true>(cw, xw);
     else if constexpr (FMT == FP4) return chunk_dot_fp4(cw, xw);
     else if constexpr (FMT == INT8) return chunk_dot_int8(cw, xw);
     else return chunk_dot_km4(cw, lut, xw);
@@ -225,7 +239,9 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
     const int nb = K / 32;
     const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
 
+    constexpr bool AFF = (FMT == INT4AFF);
     uint32_t xr[CPL][PB][XW];
+    float xsum[AFF ? CPL : 1][AFF ? PB : 1];
 #pragma unroll
     for (int p = 0; p < PB; p++) {
         int pr = pairs[p];
@@ -234,6 +250,7 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
         for (int j = 0; j < CPL; j++) {
             int c = sub + LPR * j;
             load_x_slice<FMT>(xp, c, c < cpr, xr[j][p]);
+            if constexpr (AFF) xsum[j][p] = x_slice_sum<XW>(xr[j][p]);
         }
     }
     const int64_t tile0 = (int64_t)blockIdx.x * a.tile_rows;
@@ -242,6 +259,7 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
     for (int64_t l0 = tile0 + (int64_t)wave * LROWS; l0 < tile1; l0 += 4 * LROWS) {
         uint4 cw[R][CPL];
         float sc[R][CPL];
+        float bi[AFF ? R : 1][AFF ? CPL : 1];
 #pragma unroll
         for (int g = 0; g < R; g++) {
             int gl = (EPI == EPI_SWIGLU) ? (g % G) : g;
@@ -255,6 +273,7 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
                 int cc = c < cpr ? c : 0;
                 cw[g][j] = load_stream16(rp + (uint32_t)cc * 16u);
                 sc[g][j] = plane_scale<FMT>(plane_e, prow, nb, cc);
+                if constexpr (AFF) bi[g][j] = plane_bias<FMT>(plane_e, prow, nb, cc);
             }
         }
         if constexpr (FMT == KM4) {
@@ -280,6 +299,7 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
                 for (int j = 0; j < CPL; j++) {
                     float d = chunk_dot<FMT>(cw[g][j], xr[j][p], lut_w + (g * RPW + rsub) * 16);
                     s = (FMT == KM4) ? s + d : __builtin_fmaf(d, sc[g][j], s);
+                    if constexpr (AFF) s = __builtin_fmaf(xsum[j][p], bi[g][j], s);
                 }
                 acc[g * PB + p] = s;
             }
@@ -441,8 +461,11 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
 #pragma unroll
     for (int g = 0; g < R; g++) acc[g] = 0.f;
     for (int s0 = 0; s0 < a.topk; s0 += SB) {
+        constexpr bool AFF = (FMT == INT4AFF);
         uint4 cw[SB][R][CPL];
         float sc[SB][R][CPL];
+        float bi[AFF ? SB : 1][AFF ? R : 1][AFF ? CPL : 1];
+        float xs[AFF ? SB : 1][AFF ? CPL : 1];
         uint32_t xr[SB][CPL][XW];
         float ws[SB];
         uint32_t lutv[SB];
@@ -466,6 +489,7 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
                     int cc = c < cpr ? c : 0;
                     cw[b][g][j] = load_stream16(codes_e + row * (int64_t)row_bytes + (uint32_t)cc * 16u);
                     sc[b][g][j] = plane_scale<FMT>(plane_e, row, nb, cc);
+                    if constexpr (AFF) bi[b][g][j] = plane_bias<FMT>(plane_e, row, nb, cc);
                 }
             }
             const _Float16 *xp = a.x + (int64_t)(a.x_per_slot ? t * a.topk + s : t) * K;
@@ -473,6 +497,7 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
             for (int j = 0; j < CPL; j++) {
                 int c = sub + LPR * j;
                 load_x_slice<FMT>(xp, c, c < cpr, xr[b][j]);
+                if constexpr (AFF) xs[b][j] = x_slice_sum<XW>(xr[b][j]);
             }
             if constexpr (FMT == KM4) {
                 int rr = (lane / 8) % ROWS;
@@ -494,6 +519,7 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
                 for (int j = 0; j < CPL; j++) {
                     float d = chunk_dot<FMT>(cw[b][g][j], xr[b][j], lut_lds + (b * ROWS + g * RPW + rsub) * 16);
                     acc[g] = __builtin_fmaf(d, ws[b] * sc[b][g][j], acc[g]);
+                    if constexpr (AFF) acc[g] = __builtin_fmaf(xs[b][j], ws[b] * bi[b][g][j], acc[g]);
                 }
         if constexpr (FMT == KM4) wave_fence();   // the next batch rewrites the tables
     }
@@ -601,7 +627,8 @@ static hipError_t launch_any(int fmt, GatherArgs a, int epi, bool fused, int uma
     case INT4: err = launch_fmt<INT4>(a, epi, fused, umax, &handled, st); break;
     case FP4: err = launch_fmt<FP4>(a, epi, fused, umax, &handled, st); break;
     case INT8: err = launch_fmt<INT8>(a, epi, fused, umax, &handled, st); break;
-    default: err = launch_fmt<KM4>(a, epi, fused, umax, &handled, st); break;
+    case KM4: err = launch_fmt<KM4>(a, epi, fused, umax, &handled, st); break;
+    default: err = launch_fmt<INT4AFF>(a, epi, fused, umax, &handled, st); break;
     }
     if (err != hipSuccess) return err;
     return handled ? hipSuccess : hipErrorInvalidValue;

@@ -399,6 +399,61 @@ hipError_t launch_pack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, 
 }
 
 // ---------------------------------------------------------------------------
+// Affine int4 blocks ("Stream D - Quantization", section 1: affine int4 with
+// block 32 among the MoE gather formats). Min-max: b = fp16(min),
+// s = fp16((max - min) / 15), u = clamp(rint((w - b) / s), 0, 15); plane
+// word = scale | bias << 16. One thread per block, one IEEE op per step.
+// ---------------------------------------------------------------------------
+template <typename WT>
+__global__ __launch_bounds__(256) void pack_int4aff_kernel(const WT *__restrict__ W, int64_t N, int K,
+                                                           uint8_t *__restrict__ codes, uint32_t *__restrict__ plane) {
+    const int nb = K / 32;
+    int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= N * nb) return;
+    int64_t row = gid / nb;
+    int blk = (int)(gid % nb);
+    float w[32];
+    load_block_f32<WT>(W, row * K + (int64_t)blk * 32, w);
+    float mn = w[0], mx = w[0];
+#pragma unroll
+    for (int k = 1; k < 32; k++) {
+        mn = w[k] < mn ? w[k] : mn;
+        mx = w[k] > mx ? w[k] : mx;
+    }
+    const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(__fsub_rn(mx, mn), 15.0f));
+    const uint16_t b16 = f32_to_f16_bits(mn);
+    const float s = f16_bits_to_f32(s16), b = f16_bits_to_f32(b16);
+    plane[row * nb + blk] = (uint32_t)s16 | ((uint32_t)b16 << 16);
+    uint32_t out[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float u = 0.0f;
+            if (s != 0.0f)
+                u = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(__fsub_rn(w[8 * d + i], b), s)), 0.0f),
+                                    15.0f);
+            v |= (uint32_t)u << (4 * i);
+        }
+        out[d] = v;
+    }
+    *reinterpret_cast<uint4 *>(codes + row * (int64_t)(K / 2) + (int64_t)blk * 16) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+hipError_t launch_pack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint32_t *plane,
+                               hipStream_t st) {
+    if (wdt == QMV_F16)
+        hipLaunchKernelGGL((pack_int4aff_kernel<_Float16>), dim3(blocks_grid(N, K)), dim3(256), 0, st,
+                           reinterpret_cast<const _Float16 *>(W), N, (int)K, codes, plane);
+    else
+        hipLaunchKernelGGL((pack_int4aff_kernel<float>), dim3(blocks_grid(N, K)), dim3(256), 0, st,
+                           reinterpret_cast<const float *>(W), N, (int)K, codes, plane);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Embedding table: int8 with one fp16 scale per row ("coreai-optimization
 // reference", "The LM head + embeddings": plain int8 per-row dequant-gather).
 // One workgroup per row: amax over the row, s = fp16(amax / 127), q =

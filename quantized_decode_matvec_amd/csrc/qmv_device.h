@@ -8,6 +8,8 @@
 //   FP4 : 32 E2M1 codes per chunk = one block; w = grid[c] * 2^(e8m0 - 127)
 //   INT8: 16 int8 codes per chunk = half a block; w = s * q
 //   KM4 : 32 indices per chunk; w = lut[row][c]
+//   INT4AFF: 32 codes u per chunk = one block; w = s * u + b (scale and bias
+//        per block [S1 sec. 1: affine int4 among the MoE gather formats])
 // Every decoded value below is exact in fp16 before scaling (the scale is
 // applied to the fp32 block sum), so the only rounding is fp32 accumulation.
 #pragma once
@@ -19,7 +21,7 @@ namespace qmv {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-enum Fmt { INT4 = 0, FP4 = 1, INT8 = 2, KM4 = 3 };
+enum Fmt { INT4 = 0, FP4 = 1, INT8 = 2, KM4 = 3, INT4AFF = 4 };
 
 constexpr int kWave = 64;
 
@@ -38,7 +40,7 @@ template <int FMT> struct ChunkTraits {
 
 // x slice for one chunk and one batch row, packed as half2 words in the
 // order the decoder consumes them.
-//  INT4: word 4d+0 = (x[8d], x[8d+4]), 4d+1 = (x[8d+2], x[8d+6]),
+//  INT4, INT4AFF: word 4d+0 = (x[8d], x[8d+4]), 4d+1 = (x[8d+2], x[8d+6]),
 //        4d+2 = (x[8d+1], x[8d+5]), 4d+3 = (x[8d+3], x[8d+7])
 //  others: natural pairs (x[2i], x[2i+1]).
 template <int FMT>
@@ -57,7 +59,7 @@ __device__ __forceinline__ void load_x_slice(const _Float16 *__restrict__ xrow, 
         nat[4 * i + 2] = valid ? v.z : 0u;
         nat[4 * i + 3] = valid ? v.w : 0u;
     }
-    if constexpr (FMT == INT4) {
+    if constexpr (FMT == INT4 || FMT == INT4AFF) {
         // nat[4d + m] = (x[8d+2m], x[8d+2m+1])
 #pragma unroll
         for (int d = 0; d < 4; d++) {
@@ -88,9 +90,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask, uint32_t m
     return r;
 }
 
+// AFF: the codes are used as u (bias 1024 and 16 * 64 + 1024), not u - 8.
+template <bool AFF = false>
 __device__ __forceinline__ float chunk_dot_int4(uint4 cw, const uint32_t (&xw)[16]) {
-    const h2 b0 = as_h2(0x64086408u);   // (1032, 1032)
-    const h2 b1 = as_h2(0x64806480u);   // (1152, 1152)
+    const h2 b0 = as_h2(AFF ? 0x64006400u : 0x64086408u);   // (1024, 1024) or (1032, 1032)
+    const h2 b1 = as_h2(AFF ? 0x64006400u : 0x64806480u);   // (1024, 1024) or (1152, 1152)
     const uint32_t magic = 0x64006400u;
     float lo = 0.f, hi = 0.f;
     uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
@@ -107,6 +111,16 @@ __device__ __forceinline__ float chunk_dot_int4(uint4 cw, const uint32_t (&xw)[1
         hi = dot2(a37, as_h2(xw[4 * d + 3]), hi);
     }
     return __builtin_fmaf(hi, 0.0625f, lo);
+}
+
+// Sum of the chunk's x values in fp32 (the affine bias multiplies it).
+template <int XW>
+__device__ __forceinline__ float x_slice_sum(const uint32_t (&xw)[XW]) {
+    const h2 one = as_h2(0x3C003C00u);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < XW; i++) s = dot2(as_h2(xw[i]), one, s);
+    return s;
 }
 
 // FP4: the gfx950 scaled conversion turns one byte (two E2M1 codes, low

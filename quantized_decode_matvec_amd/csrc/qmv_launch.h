@@ -37,6 +37,8 @@ hipError_t launch_pack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, 
                             hipStream_t st);
 hipError_t launch_pack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint8_t *scale,
                            hipStream_t st);
+hipError_t launch_pack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint32_t *plane,
+                               hipStream_t st);
 hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
                            hipStream_t st);
 

@@ -18,6 +18,8 @@ def dev(a: np.ndarray):
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return t.from_numpy(a.view(np.int16)).cuda().view(t.uint16)
+    if a.dtype == np.uint32:   # 32-bit plane words travel as int32 (the binding allocates them so)
+        return t.from_numpy(a.view(np.int32)).cuda()
     return t.from_numpy(a).cuda()
 
 
@@ -26,6 +28,13 @@ def host(x) -> np.ndarray:
     if x.dtype == t.uint16:
         return x.view(t.int16).cpu().numpy().view(np.uint16)
     return x.cpu().numpy()
+
+
+def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
+    """Same shape and the same bytes (uint32 plane words against their int32 view)."""
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and a.dtype.itemsize == b.dtype.itemsize and np.array_equal(a.view(np.uint8),
+                                                                                         b.view(np.uint8))
 
 
 def rel_err(y, ref):

@@ -61,9 +61,14 @@ def test_pack_validation(L):
     assert L.qpack_int8(FAKE, 0, 4, 64, ODD, FAKE, S) == E_ALIGN
     assert L.qpack_km4(FAKE, 4, 8192, 20, FAKE, FAKE, S) == E_SHAPE    # K too large for the row sort
     assert L.qpack_km4(FAKE, 4, 64, 0, FAKE, FAKE, S) == E_SHAPE       # max_iter < 1
+    half = ctypes.c_void_p(0x10002)   # 2-byte aligned: too little for the 32-bit scale + bias words
+    assert L.qpack_int4aff(FAKE, 1, 4, 48, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_int4aff(FAKE, 1, 4, 64, FAKE, half, S) == E_ALIGN
+    assert L.qmatvec_int4aff(FAKE, half, 8, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
+    assert L.qdequant(5, FAKE, FAKE, 4, 64, FAKE, S) == E_DTYPE        # one past the last format
 
 
-@pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4"])
+@pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff"])
 def test_matvec_validation(L, name):
     f = getattr(L, name)
     assert f(NUL, FAKE, 8, 64, FAKE, 1, 1, FAKE, S) == E_NULL

@@ -17,7 +17,7 @@ from tests.gpu_helpers import RTOL, dev, host
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["int4", "fp4", "int8", "km4"]
+FMTS = ["int4", "fp4", "int8", "km4", "int4aff"]
 
 
 def _check_argmax(idx, val, ref):

@@ -8,11 +8,11 @@ import pytest
 import oracle
 import quantized_decode_matvec_amd as qmv
 from quantized_decode_matvec_amd import workloads as wl
-from tests.gpu_helpers import RTOL, dev, host, rel_err
+from tests.gpu_helpers import RTOL, bits_equal, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ["int4", "fp4", "int8", "km4"]
+FMTS = ["int4", "fp4", "int8", "km4", "int4aff"]
 # (N, K): short K (16 lanes per row), 32 lanes, one chunk per lane at 64 lanes,
 # two/three/four chunks per lane, a K beyond the register fast path, ragged N
 SHAPES = [(37, 96), (50, 512), (65, 1024), (129, 2048), (33, 2560), (47, 4096), (21, 6144), (8, 8192)]
@@ -50,10 +50,10 @@ def test_pack_bit_exact(fmt, N, K):
     want = oracle.pack(fmt, W)
     got = qmv.qpack(fmt, dev(W))
     for a, b in zip(want, got):
-        assert np.array_equal(a, host(b)), fmt
+        assert bits_equal(a, host(b)), fmt
 
 
-@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8"])
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "int4aff"])
 def test_pack_fp32_input_bit_exact(fmt):
     c = wl.tiny_int4()
     W = c.W.copy()
@@ -63,7 +63,7 @@ def test_pack_fp32_input_bit_exact(fmt):
     want = oracle.pack(fmt, W)
     got = qmv.qpack(fmt, dev(W))
     for a, b in zip(want, got):
-        assert np.array_equal(a, host(b))
+        assert bits_equal(a, host(b))
 
 
 @pytest.mark.parametrize("max_iter", [1, 3, 20])
@@ -94,7 +94,11 @@ def test_dequant_exact(fmt):
     W, _ = _case(fmt, 41, 2560 if fmt != "km4" else 2048)
     codes, plane = oracle.pack(fmt, W)
     D = host(qmv.qdequant(fmt, dev(codes), dev(plane)))
-    assert np.array_equal(D.astype(np.float64), oracle.dequant(fmt, codes, plane))
+    want = oracle.dequant(fmt, codes, plane)
+    if fmt == "int4aff":
+        # s * u + b is exact in fp64 and rounded once to fp32 on the device
+        want = want.astype(np.float32).astype(np.float64)
+    assert np.array_equal(D.astype(np.float64), want)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -165,6 +169,8 @@ def test_matvec_unit_vectors_pick_columns_exactly(fmt):
     W, _ = _case(fmt, 64, 2048, seed=5)
     codes, plane = oracle.pack(fmt, W)
     D = oracle.dequant(fmt, codes, plane)
+    if fmt == "int4aff":
+        D = D.astype(np.float32).astype(np.float64)   # s * u + b rounded once to fp32
     ks = [0, 1, 31, 32, 1000, 2047]
     x = np.zeros((len(ks), 2048), np.float16)
     for i, k in enumerate(ks):
