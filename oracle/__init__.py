@@ -14,6 +14,8 @@ Formats (codes and planes as numpy arrays; W is N x K row-major, K % 32 == 0):
 * fp4:  codes uint8 [N, K/2] (E2M1, sign in bit 3), scale uint8 [N, K/32] (e8m0).
 * int8: codes int8 [N, K], scale uint16 [N, K/32].
 * km4:  codes uint8 [N, K/2] (4-bit indices), lut uint16 [N, 16] (fp16 bits).
+* int4aff: codes uint8 [N, K/2] (u in 0..15), plane uint32 [N, K/32] (fp16 scale | fp16 bias << 16).
+* int8km: codes uint8 [N, K] (8-bit indices), lut uint16 [N/32, 256] (fp16 bits), N % 32 == 0.
 """
 from __future__ import annotations
 
@@ -27,8 +29,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT_INT4, FMT_FP4, FMT_INT8, FMT_KM4, FMT_INT4AFF = 0, 1, 2, 3, 4
-FORMATS = {"int4": FMT_INT4, "fp4": FMT_FP4, "int8": FMT_INT8, "km4": FMT_KM4, "int4aff": FMT_INT4AFF}
+FMT_INT4, FMT_FP4, FMT_INT8, FMT_KM4, FMT_INT4AFF, FMT_INT8KM = 0, 1, 2, 3, 4, 5
+FORMATS = {"int4": FMT_INT4, "fp4": FMT_FP4, "int8": FMT_INT8, "km4": FMT_KM4, "int4aff": FMT_INT4AFF,
+           "int8km": FMT_INT8KM}
 
 _lib = None
 
@@ -62,6 +65,7 @@ def lib():
         L.orc_pack_int8.argtypes = [P, i64, i64, P, P]
         L.orc_pack_int4aff.argtypes = [P, i64, i64, P, P]
         L.orc_pack_km4.argtypes = [P, i64, i64, ci, P, P, P]
+        L.orc_pack_int8km.argtypes = [P, i64, i64, ci, P, P, P]
         L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
         L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
@@ -161,15 +165,30 @@ def pack_km4(W_f16, max_iter: int = 20, return_iters: bool = False):
     return codes, lut
 
 
+def pack_int8km(W_f16, max_iter: int = 20, return_iters: bool = False):
+    """W [N, K] fp16 (N % 32 == 0) -> codes uint8 [N, K] (indices), lut uint16
+    [N/32, 256] (fp16 bits): one 256-entry table per group of 32 rows."""
+    W = np.ascontiguousarray(np.asarray(W_f16, dtype=np.float16)).view(np.uint16)
+    N, K = _check_shape(W)
+    assert N % 32 == 0, "int8km groups 32 rows"
+    codes = np.zeros((N, K), np.uint8)
+    lut = np.zeros((N // 32, 256), np.uint16)
+    iters = np.zeros((N // 32,), np.int32)
+    lib().orc_pack_int8km(_p(W), N, K, int(max_iter), _p(codes), _p(lut), _p(iters))
+    if return_iters:
+        return codes, lut, iters
+    return codes, lut
+
+
 def pack(fmt: str, W, **kw):
     return {"int4": pack_int4, "fp4": pack_fp4, "int8": pack_int8, "km4": pack_km4,
-            "int4aff": pack_int4aff}[fmt](W, **kw)
+            "int4aff": pack_int4aff, "int8km": pack_int8km}[fmt](W, **kw)
 
 
 # --- dequant and matvec ---
 
 def _kdim(fmt: str, codes: np.ndarray) -> int:
-    return codes.shape[1] if fmt == "int8" else codes.shape[1] * 2
+    return codes.shape[1] if fmt in ("int8", "int8km") else codes.shape[1] * 2
 
 
 def dequant(fmt: str, codes, plane) -> np.ndarray:

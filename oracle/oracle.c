@@ -469,12 +469,118 @@ void orc_pack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 8-bit k-means palettization, one 256-entry fp16 table per group of 32     */
+/* consecutive output rows [S3 "Palettization": 2^n_bits centroids, 1-D     */
+/* k-means, per-grouped-channel granularity; S3 "The LM head + embeddings"  */
+/* and S5 "int8 k-means > whole-model int4": int8 k-means with group 32].    */
+/*                                                                          */
+/* Reading: the same procedure as the 4-bit tables above, over the 32*K      */
+/* values of a group taken together (row-major), with 256 centroids:        */
+/*   1. at most 256 distinct numbers: they are the table (ascending, padded  */
+/*      with the largest);                                                   */
+/*   2. otherwise start from the order statistics at ranks (2j+1)M/512 of    */
+/*      the M = 32K sorted values;                                           */
+/*   3. Lloyd steps, at most max_iter: a value v goes to the index equal to  */
+/*      the number of adjacent centroid pairs (C[i], C[i+1]) whose midpoint  */
+/*      lies strictly below v (the nearest centroid, a tie to the lower      */
+/*      index; the centroids stay in ascending order); every non-empty       */
+/*      centroid moves to its members' mean rounded to the nearest fp16      */
+/*      number (ties to even), empty ones stay; stop when none moves;        */
+/*   4. assign once more with the final centroids.                           */
+/* A row count that is not a multiple of 32 is not a group layout.           */
+/* ------------------------------------------------------------------------ */
+
+#define KM8_L 256
+
+static int nearest_centroid_l(const int64_t *C, int L, int64_t x)
+{
+    int a = 0;
+    for (int i = 0; i + 1 < L; i++)
+        if (C[i] + C[i + 1] < 2 * x)
+            a++;
+    return a;
+}
+
+/* w: M fp16 values of one group; idx: M indices; lut: 256 fp16 entries.
+   Returns the number of Lloyd updates taken. max_iter 0 keeps the starting
+   centroids (used by tests). */
+static int km8_group(const uint16_t *w, int64_t M, int max_iter, uint8_t *idx, uint16_t *lut)
+{
+    int64_t *X = malloc(sizeof(int64_t) * M);
+    int64_t *S = malloc(sizeof(int64_t) * M);
+    for (int64_t k = 0; k < M; k++)
+        X[k] = S[k] = f16_to_units(w[k]);
+    qsort(S, M, sizeof(int64_t), cmp_i64);
+
+    int64_t C[KM8_L];
+    int64_t D = 1;
+    for (int64_t k = 1; k < M; k++)
+        if (S[k] != S[k - 1])
+            D++;
+    int iters = 0;
+    if (D <= KM8_L) {
+        int j = 0;
+        for (int64_t k = 0; k < M; k++)
+            if (k == 0 || S[k] != S[k - 1])
+                C[j++] = S[k];
+        for (; j < KM8_L; j++)
+            C[j] = S[M - 1];
+    } else {
+        for (int j = 0; j < KM8_L; j++)
+            C[j] = S[(2 * (int64_t)j + 1) * M / (2 * KM8_L)];
+        for (int it = 0; it < max_iter; it++) {
+            int64_t sum[KM8_L] = {0}, cnt[KM8_L] = {0}, Cn[KM8_L];
+            for (int64_t k = 0; k < M; k++) {
+                int j = nearest_centroid_l(C, KM8_L, X[k]);
+                sum[j] += X[k];
+                cnt[j] += 1;
+            }
+            int moved = 0;
+            for (int j = 0; j < KM8_L; j++) {
+                Cn[j] = cnt[j] ? round_mean_to_f16_units(sum[j], cnt[j]) : C[j];
+                if (Cn[j] != C[j])
+                    moved = 1;
+            }
+            iters++;
+            if (!moved)
+                break;
+            memcpy(C, Cn, sizeof(C));
+        }
+    }
+    for (int64_t k = 0; k < M; k++)
+        idx[k] = (uint8_t)nearest_centroid_l(C, KM8_L, X[k]);
+    for (int j = 0; j < KM8_L; j++)
+        lut[j] = units_to_f16(C[j]);
+    free(X);
+    free(S);
+    return iters;
+}
+
+/* W_f16: N x K fp16 bits, N % 32 == 0; codes N x K (indices); lut
+   (N/32) x 256 fp16 bits; iters (may be NULL): Lloyd updates per group. */
+void orc_pack_int8km(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
+                     uint8_t *codes, uint16_t *lut, int32_t *iters)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t g = 0; g < N / 32; g++) {
+        int it = km8_group(W_f16 + g * 32 * K, 32 * K, max_iter, codes + g * 32 * K, lut + g * KM8_L);
+        if (iters)
+            iters[g] = it;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Dequantization: every reconstructed weight is exact in fp64 (and fp32).   */
-/* fmt: 0 int4, 1 fp4, 2 int8, 3 km4.                                        */
+/* fmt: 0 int4, 1 fp4, 2 int8, 3 km4, 4 int4aff, 5 int8km.                  */
 /* ------------------------------------------------------------------------ */
 
 static double dequant_one(int fmt, const void *codes, const void *plane, int64_t K, int64_t n, int64_t k)
 {
+    if (fmt == 5) {   /* int8km: the group's table at the byte's index */
+        const uint8_t *c = (const uint8_t *)codes;
+        const uint16_t *lut = (const uint16_t *)plane;
+        return orc_f16_to_f64(lut[(n / 32) * KM8_L + c[n * K + k]]);
+    }
     if (fmt == 2) {
         const int8_t *c = (const int8_t *)codes;
         const uint16_t *s = (const uint16_t *)plane;
@@ -562,10 +668,12 @@ void orc_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, do
 }
 
 /* Bytes of one row of codes, and of one row of the scale / table plane,
-   for a K-long row in format fmt (0 int4, 1 fp4, 2 int8, 3 km4, 4 int4aff). */
-static int64_t code_row_bytes(int fmt, int64_t K) { return fmt == 2 ? K : K / 2; }
+   for a K-long row in format fmt (0 int4, 1 fp4, 2 int8, 3 km4, 4 int4aff,
+   5 int8km; int8km rows come in groups of 32, so 16 bytes of table per row). */
+static int64_t code_row_bytes(int fmt, int64_t K) { return (fmt == 2 || fmt == 5) ? K : K / 2; }
 static int64_t plane_row_bytes(int fmt, int64_t K)
 {
+    if (fmt == 5) return 16;          /* a 512-byte table per 32 rows */
     if (fmt == 1) return K / 32;      /* one e8m0 byte per block */
     if (fmt == 3) return 32;          /* sixteen fp16 table entries */
     if (fmt == 4) return 4 * (K / 32);   /* fp16 scale + fp16 bias per block */

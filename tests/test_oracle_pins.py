@@ -641,3 +641,141 @@ def test_int4aff_reconstruction_error_is_half_a_step():
     bound = 0.5 * s + np.abs(b - mn) + 1e-6 * s
     err = np.abs(D - W).reshape(20, -1, 32).max(-1)
     assert np.all(err <= bound)
+
+
+# --- int8 k-means: one 256-entry table per group of 32 rows ---
+
+def test_int8km_few_distinct_values_are_exact():
+    """At most 256 distinct numbers in a group: they are the table (ascending,
+    padded with the largest), so dequant reproduces the weights exactly."""
+    rng = np.random.default_rng(40)
+    for d in (1, 3, 200, 256):
+        vals = np.unique(rng.standard_normal(4 * d).astype(np.float16))[:d]
+        assert len(vals) == d
+        W = rng.choice(vals, size=(64, 96)).astype(np.float16)
+        W[32:] = (W[:32][::-1] * np.float16(-3)).astype(np.float16)   # second group: its own values
+        codes, lut = oracle.pack_int8km(W)
+        assert codes.shape == (64, 96) and lut.shape == (2, 256)
+        assert np.array_equal(oracle.dequant("int8km", codes, lut), W.astype(np.float64))
+        Lf = lut.view(np.float16).astype(np.float64)
+        for g in range(2):
+            used = np.unique(W[32 * g:32 * g + 32].astype(np.float64))
+            assert np.array_equal(Lf[g, :len(used)], used)
+            assert np.all(Lf[g, len(used):] == used[-1])
+
+
+def test_int8km_starting_table_is_order_statistics():
+    """With no Lloyd step the table is the group's order statistics at ranks
+    (2j+1)M/512 (numpy sort), and every weight takes its nearest entry."""
+    rng = np.random.default_rng(41)
+    W = (rng.standard_normal((64, 128)) * 0.02).astype(np.float16)
+    codes, lut, iters = oracle.pack_int8km(W, max_iter=0, return_iters=True)
+    assert np.all(iters == 0)
+    M = 32 * 128
+    ranks = (2 * np.arange(256) + 1) * M // 512
+    for g in range(2):
+        S = np.sort(W[32 * g:32 * g + 32].reshape(-1).astype(np.float64))
+        assert np.array_equal(lut[g].view(np.float16).astype(np.float64), S[ranks])
+    _int8km_check_nearest(W, codes, lut)
+
+
+def test_int8km_hand_worked_fixed_point():
+    """Even integers 0..1022, four copies each, in one group: the starting
+    entries are 4j+2; one Lloyd step moves entry 0 to 2 (members 0, 2, 4),
+    entry j to 4j+3 (members 4j+2, 4j+4) and keeps 1022 in the last; the next
+    step moves nothing. Worked by hand from the midpoint rule."""
+    vals = np.repeat(np.arange(0, 1024, 2), 4)
+    rng = np.random.default_rng(42)
+    W = vals[rng.permutation(vals.size)].reshape(32, 64).astype(np.float16)
+    codes, lut, iters = oracle.pack_int8km(W, return_iters=True)
+    want = np.array([2] + [4 * j + 3 for j in range(1, 255)] + [1022], np.float64)
+    assert np.array_equal(lut[0].view(np.float16).astype(np.float64), want)
+    assert iters[0] == 2
+    v = W.astype(np.int64)
+    want_codes = np.where(v <= 4, 0, (v - 2) // 4)
+    assert np.array_equal(codes.astype(np.int64), want_codes)
+
+
+def _int8km_check_nearest(W, codes, lut):
+    Lf = lut.view(np.float16).astype(np.float64)
+    for g in range(W.shape[0] // 32):
+        w = W[32 * g:32 * g + 32].reshape(-1).astype(np.float64)
+        c = codes[32 * g:32 * g + 32].reshape(-1).astype(np.int64)
+        assert np.all(np.diff(Lf[g]) >= 0), "table ascending"
+        dist = np.abs(w[:, None] - Lf[g][None, :])
+        assert np.array_equal(dist[np.arange(w.size), c], dist.min(1)), "nearest entry"
+        # among distinct entries at equal distance the lower one is taken
+        best = dist.min(1)
+        first = np.argmax(dist == best[:, None], axis=1)
+        assert np.all((Lf[g][first] == Lf[g][c]) | (first == c))
+        tie = np.isclose(dist[np.arange(w.size), first], dist[np.arange(w.size), c]) & (Lf[g][first] != Lf[g][c])
+        assert not np.any(tie & (Lf[g][c] > Lf[g][first]))
+
+
+def test_int8km_lloyd_invariants():
+    """Converged groups: every weight takes its nearest entry and every used
+    entry is its members' exact mean rounded to the nearest fp16 number."""
+    rng = np.random.default_rng(43)
+    W = (rng.standard_normal((64, 64)) * 0.02).astype(np.float16)
+    W[40, ::5] *= 25                                 # outliers in the second group
+    codes, lut, iters = oracle.pack_int8km(W, max_iter=2000, return_iters=True)
+    assert np.all(iters < 2000)
+    _int8km_check_nearest(W, codes, lut)
+    Lf = lut.view(np.float16).astype(np.float64)
+    for g in range(2):
+        w = W[32 * g:32 * g + 32].reshape(-1)
+        c = codes[32 * g:32 * g + 32].reshape(-1)
+        for j in np.unique(c):
+            mem = w[c == j].astype(np.float64)
+            mean = sum(Fraction(float(v)) for v in mem) / len(mem)
+            e = np.float16(Lf[g, j])
+            lo = Fraction(float(np.nextafter(e, np.float16(-np.inf))))
+            hi = Fraction(float(np.nextafter(e, np.float16(np.inf))))
+            assert abs(mean - Fraction(float(e))) <= min(abs(mean - lo), abs(mean - hi))
+    # the default 20 steps keep the nearest-entry property
+    codes, lut = oracle.pack_int8km(W)
+    _int8km_check_nearest(W, codes, lut)
+
+
+def test_int8km_uniform_group_reaches_the_uniform_quantizer():
+    """256-level k-means of a uniform group: the optimal quantizer has equal
+    cells, with squared error (2/L)^2/12 for U(-1, 1), i.e. var/L^2; the
+    entries sit at the cell centres (2j+1)/L - 1."""
+    rng = np.random.default_rng(44)
+    W = rng.uniform(-1, 1, (32, 1024)).astype(np.float16)
+    codes, lut = oracle.pack_int8km(W)
+    D = oracle.dequant("int8km", codes, lut)
+    w = W.astype(np.float64)
+    mse = np.mean((D - w) ** 2)
+    want = (2 / 256) ** 2 / 12
+    assert abs(mse / want - 1) < 0.05, (mse, want)
+    centres = (2 * np.arange(256) + 1) / 256 - 1
+    # sampling noise moves the cell edges by a fraction of a cell, never by one
+    assert np.max(np.abs(lut[0].view(np.float16).astype(np.float64) - centres)) < 2 / 256
+
+
+def test_int8km_matvec_moe_and_argmax():
+    """Matvec equals a numpy GEMM of the dequantized rows (groups of 32 rows
+    sharing a table), the one-expert MoE reduces to numpy GEMVs, and equal
+    winning rows of one group give the lower index."""
+    rng = np.random.default_rng(45)
+    W = (rng.standard_normal((64, 96)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((3, 96)).astype(np.float16)
+    W[20] = W[17] = np.sign(x[0]).astype(np.float16) * 0.05
+    codes, lut = oracle.pack_int8km(W)
+    D = oracle.dequant("int8km", codes, lut)
+    assert np.array_equal(D[33], lut[1].view(np.float16).astype(np.float64)[codes[33]])
+    y = oracle.matvec("int8km", codes, lut, x)
+    assert np.allclose(y, x.astype(np.float64) @ D.T, rtol=1e-13, atol=1e-15)
+    idx, val = oracle.matvec_argmax("int8km", codes, lut, x)
+    assert idx[0] == 17
+    E, H, I = 6, 64, 32
+    guc, gus, dnc, dns, rng = _small_moe(E=E, H=H, I=I, fmt="int8km")
+    xt = rng.standard_normal((1, H)).astype(np.float16)
+    e = E - 1
+    y = oracle.moe_ffn(guc, gus, dnc, dns, xt, np.array([[e]]), np.array([[1.0]]), fmt="int8km")
+    Wg = oracle.dequant("int8km", guc[e], gus[e])
+    Wd = oracle.dequant("int8km", dnc[e], dns[e])
+    g = Wg @ xt[0].astype(np.float64)
+    h = (g[:I] / (1 + np.exp(-g[:I])) * g[I:]).astype(np.float16).astype(np.float64)
+    assert np.allclose(y[0], Wd @ h, rtol=1e-12, atol=1e-12)
