@@ -35,9 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 def algo_bytes(fmt, N, K):
     """Bytes a call must read from HBM: code plane plus scale/table plane."""
-    codes = N * K if fmt == "int8" else N * K // 2
+    codes = N * K if fmt in ("int8", "int8km") else N * K // 2
     plane = {"int4": N * (K // 32) * 2, "int8": N * (K // 32) * 2, "fp4": N * (K // 32), "km4": N * 16 * 2,
-             "int4aff": N * (K // 32) * 4}[fmt]
+             "int4aff": N * (K // 32) * 4, "int8km": (N // 32) * 512}[fmt]
     return codes + plane
 
 
@@ -230,7 +230,13 @@ def main():
         extras["km4_B8_us"] = round(ms8 * 1e3, 2)
         extras["km4_B8_GBps"] = round(nbytes / (ms8 * 1e-3) / 1e9, 1)
 
-        for fmt in ("fp4", "int4", "int4aff"):
+        e0.record()
+        pk8 = qmv.qpack_int8km(W)
+        e1.record()
+        torch.cuda.synchronize()
+        extras["int8km_pack_ms"] = round(e0.elapsed_time(e1), 3)
+        del pk8
+        for fmt in ("fp4", "int4", "int4aff", "int8km"):
             pk = [qmv.qpack(fmt, W)]
             pk += [(a.clone(), b.clone()) for a, b in [pk[0]] * (len(copies) - 1)]
             msf = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x1, y=y[:1]),

@@ -62,7 +62,7 @@ typedef enum {
 } qmv_status;
 
 typedef enum { QMV_F32 = 0, QMV_F16 = 1 } qmv_dtype;
-typedef enum { QMV_INT4 = 0, QMV_FP4 = 1, QMV_INT8 = 2, QMV_KM4 = 3, QMV_INT4AFF = 4 } qmv_format;
+typedef enum { QMV_INT4 = 0, QMV_FP4 = 1, QMV_INT8 = 2, QMV_KM4 = 3, QMV_INT4AFF = 4, QMV_INT8KM = 5 } qmv_format;
 typedef enum { QMV_EPI_NONE = 0, QMV_EPI_SWIGLU = 1, QMV_EPI_COMBINE = 2 } qmv_epilogue;
 
 /* Static string naming a status (never NULL). */
@@ -122,6 +122,24 @@ qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
 qmv_status qpack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K,
                          uint8_t *codes, uint32_t *plane, void *stream);
 
+/* 8-bit k-means palettization with one 256-entry fp16 table per group of 32
+ * consecutive rows [S3 "Palettization": 2^n_bits centroids, 1-D k-means,
+ * per-grouped-channel granularity; S5 "int8 k-means > whole-model int4":
+ * int8 k-means, group 32]. The 4-bit table procedure above on the 32 * K
+ * values of each group: exact integer arithmetic on units of 2^-24; at most
+ * 256 distinct values form the table (ascending, padded with the largest);
+ * otherwise start from the order statistics at ranks (2j+1)M/512 (M = 32K)
+ * and take at most max_iter Lloyd steps (a value goes to the index equal to
+ * the number of adjacent entry pairs whose midpoint lies strictly below it;
+ * non-empty entries move to their members' mean rounded to the nearest fp16,
+ * ties to even; stop when none moves). Outputs: codes [N][K] byte indices,
+ * lut [N/32][256] fp16 bits ascending. N % 32 == 0 (a row count that is not
+ * a multiple of the group is refused rather than left unpacked, [S3]
+ * "Pitfalls"); K <= 2048 (a group's sorted values are held on chip);
+ * max_iter >= 1; W, codes 16-byte aligned, lut 4-byte aligned. */
+qmv_status qpack_int8km(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
+                        uint8_t *codes, uint16_t *lut, void *stream);
+
 /* ---------------------------------------------------------------------- */
 /* Fused dequantize-matvec [S2 secs. 1 and 8: the fused 4-bit decode       */
 /* matvec; the same kernel structure for every format, only the dequant    */
@@ -140,6 +158,9 @@ qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int
                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K,
                            const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+/* int8km: N % 32 == 0; lut as qpack_int8km writes it (4-byte aligned). */
+qmv_status qmatvec_int8km(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                          const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 
 /* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
  * weight is exact in fp32, except affine int4, where s * u + b is rounded

@@ -17,14 +17,16 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqmv.so")
 
 QMV_F32, QMV_F16 = 0, 1
-QMV_INT4, QMV_FP4, QMV_INT8, QMV_KM4, QMV_INT4AFF = 0, 1, 2, 3, 4
+QMV_INT4, QMV_FP4, QMV_INT8, QMV_KM4, QMV_INT4AFF, QMV_INT8KM = 0, 1, 2, 3, 4, 5
 QMV_EPI_NONE, QMV_EPI_SWIGLU, QMV_EPI_COMBINE = 0, 1, 2
-FORMATS = {"int4": QMV_INT4, "fp4": QMV_FP4, "int8": QMV_INT8, "km4": QMV_KM4, "int4aff": QMV_INT4AFF}
+FORMATS = {"int4": QMV_INT4, "fp4": QMV_FP4, "int8": QMV_INT8, "km4": QMV_KM4, "int4aff": QMV_INT4AFF,
+           "int8km": QMV_INT8KM}
 EPILOGUES = {"none": QMV_EPI_NONE, "swiglu": QMV_EPI_SWIGLU, "combine": QMV_EPI_COMBINE}
 
 # every symbol include/qmv.h declares
 EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4", "qpack_int4aff",
-           "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff", "qdequant",
+           "qpack_int8km", "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
+           "qmatvec_int8km", "qdequant",
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read")
@@ -55,11 +57,13 @@ def lib() -> ctypes.CDLL:
             "qpack_int8": ([P, ci, i64, i64, P, P, P], ci),
             "qpack_km4": ([P, i64, i64, ci, P, P, P], ci),
             "qpack_int4aff": ([P, ci, i64, i64, P, P, P], ci),
+            "qpack_int8km": ([P, i64, i64, ci, P, P, P], ci),
             "qmatvec_int4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_fp4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_int8": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_km4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_int4aff": ([P, P, i64, i64, P, ci, ci, P, P], ci),
+            "qmatvec_int8km": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qdequant": ([ci, P, P, i64, i64, P, P], ci),
             "qmoe_route": ([P, ci, ci, ci, P, P, P], ci),
             "gather_qmatvec_workspace_bytes": ([ci, ci, ci, i64, ci], sz),
@@ -164,15 +168,27 @@ def qpack_int4aff(W, codes=None, plane=None, stream=None):
     return codes, plane
 
 
+def qpack_int8km(W, max_iter=20, codes=None, lut=None, stream=None):
+    """W fp16 [N, K], N % 32 == 0 -> (codes uint8 [N, K], lut uint16 [N/32, 256])."""
+    torch = _torch()
+    if W.dtype != torch.float16:
+        raise TypeError("qpack_int8km takes fp16 weights")
+    N, K = W.shape
+    codes = _empty((N, K), torch.uint8, W) if codes is None else codes
+    lut = _empty((N // 32, 256), torch.uint16, W) if lut is None else lut
+    _check("qpack_int8km", lib().qpack_int8km(_ptr(W), N, K, int(max_iter), _ptr(codes), _ptr(lut), _stream(stream)))
+    return codes, lut
+
+
 def qpack(fmt, W, **kw):
     return {"int4": qpack_int4, "fp4": qpack_fp4, "int8": qpack_int8, "km4": qpack_km4,
-            "int4aff": qpack_int4aff}[fmt](W, **kw)
+            "int4aff": qpack_int4aff, "int8km": qpack_int8km}[fmt](W, **kw)
 
 
 # ---------------------------------------------------------------- matvec
 
 def _kdim(fmt, codes):
-    return codes.shape[-1] if fmt == "int8" else codes.shape[-1] * 2
+    return codes.shape[-1] if fmt in ("int8", "int8km") else codes.shape[-1] * 2
 
 
 def _matvec(name, fmt, codes, plane, x, y, stream):
@@ -204,6 +220,10 @@ def qmatvec_km4(codes, lut, x, y=None, stream=None):
 
 def qmatvec_int4aff(codes, plane, x, y=None, stream=None):
     return _matvec("qmatvec_int4aff", "int4aff", codes, plane, x, y, stream)
+
+
+def qmatvec_int8km(codes, lut, x, y=None, stream=None):
+    return _matvec("qmatvec_int8km", "int8km", codes, lut, x, y, stream)
 
 
 def qmatvec(fmt, codes, plane, x, y=None, stream=None):

@@ -53,6 +53,9 @@ qmv_status check_mv(const void *codes, const void *plane, size_t plane_align, in
     return QMV_OK;
 }
 
+// int8km tables cover groups of 32 rows: other row counts are refused
+inline bool rows_fit(qmv_format f, int64_t N) { return f != QMV_INT8KM || N % 32 == 0; }
+
 // largest K the expert gather handles: 256 chunks per row of codes
 int64_t gather_max_k(qmv_format f) { return f == QMV_INT8 ? 4096 : 8192; }
 
@@ -61,6 +64,7 @@ size_t plane_alignment(qmv_format f) {
     case QMV_FP4: return 1;
     case QMV_KM4: return 4;       // tables are read as 32-bit words
     case QMV_INT4AFF: return 4;   // one 32-bit scale + bias word per block
+    case QMV_INT8KM: return 4;    // tables are read as 32-bit words
     default: return 2;
     }
 }
@@ -163,11 +167,28 @@ qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t 
     return launch_status(qmv::launch_matvec(QMV_INT4AFF, codes, plane, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
+qmv_status qpack_int8km(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
+                        void *stream) {
+    if (!W_f16 || !codes || !lut) return QMV_E_NULL;
+    if (N < 32 || N % 32 != 0 || K < 32 || K % 32 != 0 || K > 2048 || max_iter < 1) return QMV_E_SHAPE;
+    if (N / 32 > INT32_MAX) return QMV_E_SHAPE;
+    if (!aligned(W_f16, 16) || !aligned(codes, 16) || !aligned(lut, 4)) return QMV_E_ALIGN;
+    return launch_status(qmv::launch_pack_int8km(W_f16, N, K, max_iter, codes, lut, as_stream(stream)));
+}
+
+qmv_status qmatvec_int8km(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const void *x,
+                          qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(codes, lut, 4, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    if (N % 32 != 0) return QMV_E_SHAPE;
+    return launch_status(qmv::launch_matvec(QMV_INT8KM, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
+}
+
 qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *W_hat,
                     void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;
     if (!codes || !plane || !W_hat) return QMV_E_NULL;
-    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K || !rows_fit(fmt, N)) return QMV_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(W_hat, 16)) return QMV_E_ALIGN;
     return launch_status(qmv::launch_dequant(fmt, codes, plane, N, K, W_hat, as_stream(stream)));
 }
@@ -233,9 +254,9 @@ size_t qmatvec_argmax_workspace_bytes(int64_t N, int B) {
 
 qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                           int B, int32_t *idx, float *val, void *workspace, size_t ws_bytes, void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;
     if (!codes || !plane || !x || !idx || !val) return QMV_E_NULL;
-    if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || B < 1 || B > 8) return QMV_E_SHAPE;
+    if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || B < 1 || B > 8 || !rows_fit(fmt, N)) return QMV_E_SHAPE;
     if (N > (int64_t(1) << 40) / K || !qmv::argmax_supported(fmt, K, B)) return QMV_E_SHAPE;
     if (!workspace || ws_bytes < qmv::argmax_workspace_bytes(N, B)) return QMV_E_WORKSPACE;
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(idx, 4) ||

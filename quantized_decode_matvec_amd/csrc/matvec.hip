@@ -60,18 +60,23 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     // with one wave per workgroup and one row per row group the km4 tables sit
     // at compile-time LDS offsets
     constexpr bool KM4_IMM = (FMT == KM4) && WAVES == 1 && RPW == 1;
-    constexpr int LUT_WORDS = ROWS_IT * 8;      // km4 table dwords per iteration
+    // int8 k-means: an iteration's rows share one 256-entry table (rows come in
+    // groups of 32 and an iteration's rows never straddle two groups); one wave
+    // per workgroup keeps the table at a compile-time LDS address
+    constexpr bool KM8 = (FMT == INT8KM);
+    static_assert(!KM8 || (WAVES == 1 && 32 % ROWS_IT == 0), "int8km: one wave, rows within a group");
+    constexpr int LUT_WORDS = KM8 ? 128 : ROWS_IT * 8;   // table dwords per iteration
     constexpr int LUT_PER_LANE = (LUT_WORDS + kWave - 1) / kWave;
-    __shared__ __align__(16) _Float16 lut_lds[(FMT == KM4) ? WAVES * ROWS_IT * 16 : 1];
+    __shared__ __align__(16) _Float16 lut_lds[(FMT == KM4) ? WAVES * ROWS_IT * 16 : (KM8 ? 256 : 1)];
 
     const int lane = threadIdx.x & 63;
     const int wave = (WAVES == 1) ? 0 : (threadIdx.x >> 6);
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
     // FULLK: K fills the lanes exactly (chunks per row == LPR * CPL)
-    const int cpr = FULLK ? LPR * CPL : ((FMT == INT8) ? K / 16 : K / 32);   // chunks per row
-    const int nb = K / 32;                                                   // blocks per row
-    const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
+    const int cpr = FULLK ? LPR * CPL : ((FMT == INT8 || KM8) ? K / 16 : K / 32);   // chunks per row
+    const int nb = K / 32;                                                          // blocks per row
+    const uint32_t row_bytes = (FMT == INT8 || KM8) ? (uint32_t)K : (uint32_t)K / 2;
     const int64_t wrow0 = ((int64_t)blockIdx.x * WAVES + wave) * ROWS_IT * ITERS;
     if (wrow0 >= N) {
         if constexpr (ARGMAX) {
@@ -131,6 +136,10 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 rr = rr <= last ? rr : last;
                 lutv[q] = lsrc[rr * 8 + (i % 8)];
             }
+        } else if constexpr (KM8) {
+            const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane) + (row0 / 32) * 128;
+#pragma unroll
+            for (int q = 0; q < LUT_PER_LANE; q++) lutv[q] = lsrc[q * kWave + lane];
         }
     };
 
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 if constexpr (AFF) bic[g][j] = bi[g][j];
             }
         _Float16 *lut_w = lut_lds + wave * ROWS_IT * 16;
-        if constexpr (FMT == KM4) {
+        if constexpr (FMT == KM4 || KM8) {
             uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
 #pragma unroll
             for (int q = 0; q < LUT_PER_LANE; q++) {
@@ -198,16 +207,18 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                     else if constexpr (AFF) d = chunk_dot_int4<true>(cwc[g][j], xr[j][b]);
                     else if constexpr (FMT == FP4) d = chunk_dot_fp4(cwc[g][j], xr[j][b]);
                     else if constexpr (FMT == INT8) d = chunk_dot_int8(cwc[g][j], xr[j][b]);
+                    else if constexpr (KM8)
+                        d = chunk_dot_int8km_imm(cwc[g][j], reinterpret_cast<const char *>(lut_lds), xr[j][b]);
                     else if constexpr (KM4_IMM)
                         d = chunk_dot_km4_imm(cwc[g][j], reinterpret_cast<const char *>(lut_lds) + g * 32, xr[j][b]);
                     else d = chunk_dot_km4(cwc[g][j], lut_w + (g * RPW + rsub) * 16, xr[j][b]);
-                    a = (FMT == KM4) ? a + d : __builtin_fmaf(d, scc[g][j], a);
+                    a = (FMT == KM4 || KM8) ? a + d : __builtin_fmaf(d, scc[g][j], a);
                     if constexpr (AFF) a = __builtin_fmaf(xsum[j][b], bic[g][j], a);
                 }
                 acc[g * BT + b] = a;
             }
         }
-        if constexpr (FMT == KM4 && ITERS > 1) {
+        if constexpr ((FMT == KM4 || KM8) && ITERS > 1) {
             // the next iteration rewrites the tables: keep this iteration's reads above it
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -280,7 +291,12 @@ template <int FMT>
 __device__ __forceinline__ void decode_chunk_f32(const uint8_t *__restrict__ codes, const void *__restrict__ plane,
                                                  int64_t row, int K, int c, float (&w)[32]) {
     const int nb = K / 32;
-    if constexpr (FMT == INT8) {
+    if constexpr (FMT == INT8KM) {
+        const uint8_t *p = codes + row * (int64_t)K + (int64_t)c * 16;
+        const uint16_t *lut = reinterpret_cast<const uint16_t *>(plane) + (row / 32) * 256;
+#pragma unroll
+        for (int i = 0; i < 16; i++) w[i] = f16_bits_to_f32(lut[p[i]]);
+    } else if constexpr (FMT == INT8) {
         const int8_t *p = reinterpret_cast<const int8_t *>(codes) + row * (int64_t)K + (int64_t)c * 16;
         float s = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(plane)[row * nb + c / 2]);
 #pragma unroll
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     int64_t row = gid / nb;
     int blk = (int)(gid % nb);
     float w[32];
-    if constexpr (FMT == INT8) {
+    if constexpr (FMT == INT8 || FMT == INT8KM) {
         decode_chunk_f32<FMT>(codes, plane, row, K, 2 * blk, w);
         float w2[32];
         decode_chunk_f32<FMT>(codes, plane, row, K, 2 * blk + 1, w2);
@@ -406,9 +422,9 @@ static int grid_for_waves(int64_t waves_needed) {
 // amortize the x slices held in registers.
 template <int FMT, int BT> struct LaunchShape {
     static constexpr int R = (BT == 1) ? ((FMT == INT4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
-    static constexpr int ITERS = (FMT == KM4) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
+    static constexpr int ITERS = (FMT == KM4 || FMT == INT8KM) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
                                               : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
-    static constexpr int WAVES = (FMT == KM4) ? 1 : 4;
+    static constexpr int WAVES = (FMT == KM4 || FMT == INT8KM) ? 1 : 4;
 };
 
 // The argmax epilogue writes one key per wave: waves cover 4x more rows (at
@@ -424,7 +440,7 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
     if (nparts) *nparts = grid * S::WAVES;
-    const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+    const int cpr = (FMT == INT8 || FMT == INT8KM) ? K / 16 : K / 32;
     if (cpr == LPR * CPL)
         hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, ARGMAX>), dim3((unsigned)grid),
                            dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
@@ -516,6 +532,7 @@ bool argmax_supported(int fmt, int64_t K, int B) {
     switch (fmt) {
     case INT4: return argmax_shape<INT4>((int)K, B, nullptr, nullptr);
     case INT4AFF: return argmax_shape<INT4AFF>((int)K, B, nullptr, nullptr);
+    case INT8KM: return argmax_shape<INT8KM>((int)K, B, nullptr, nullptr);
     case FP4: return argmax_shape<FP4>((int)K, B, nullptr, nullptr);
     case INT8: return argmax_shape<INT8>((int)K, B, nullptr, nullptr);
     default: return argmax_shape<KM4>((int)K, B, nullptr, nullptr);
@@ -555,6 +572,7 @@ hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, i
     switch (fmt) {
     case INT4: return argmax_fmt<INT4>(c, plane, N, (int)K, x, B, idx, val, part, st);
     case INT4AFF: return argmax_fmt<INT4AFF>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    case INT8KM: return argmax_fmt<INT8KM>(c, plane, N, (int)K, x, B, idx, val, part, st);
     case FP4: return argmax_fmt<FP4>(c, plane, N, (int)K, x, B, idx, val, part, st);
     case INT8: return argmax_fmt<INT8>(c, plane, N, (int)K, x, B, idx, val, part, st);
     default: return argmax_fmt<KM4>(c, plane, N, (int)K, x, B, idx, val, part, st);
@@ -567,6 +585,7 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
     switch (fmt) {
     case INT4: return matvec_fmt<INT4>(c, plane, N, (int)K, x, xdt, B, y, st);
     case INT4AFF: return matvec_fmt<INT4AFF>(c, plane, N, (int)K, x, xdt, B, y, st);
+    case INT8KM: return matvec_fmt<INT8KM>(c, plane, N, (int)K, x, xdt, B, y, st);
     case FP4: return matvec_fmt<FP4>(c, plane, N, (int)K, x, xdt, B, y, st);
     case INT8: return matvec_fmt<INT8>(c, plane, N, (int)K, x, xdt, B, y, st);
     default: return matvec_fmt<KM4>(c, plane, N, (int)K, x, xdt, B, y, st);
@@ -582,6 +601,9 @@ hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t
     case INT4: hipLaunchKernelGGL(dequant_kernel<INT4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
     case INT4AFF:
         hipLaunchKernelGGL(dequant_kernel<INT4AFF>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out);
+        break;
+    case INT8KM:
+        hipLaunchKernelGGL(dequant_kernel<INT8KM>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out);
         break;
     case FP4: hipLaunchKernelGGL(dequant_kernel<FP4>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;
     case INT8: hipLaunchKernelGGL(dequant_kernel<INT8>, dim3(grid), dim3(256), 0, st, c, plane, N, (int)K, out); break;

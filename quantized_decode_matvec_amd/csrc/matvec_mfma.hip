@@ -401,7 +401,7 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
     // km4 table lookups from 16 rows at once meet LDS bank conflicts; below
     // B = 5 its dot2 path (one row's table per instruction) is faster
-    if (fmt == INT4AFF || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
+    if (fmt == INT4AFF || fmt == INT8KM || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
     if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;

@@ -371,6 +371,174 @@ __global__ __launch_bounds__(kKmThreads) void pack_km4_kernel(const uint16_t *__
 }
 
 // ---------------------------------------------------------------------------
+// int8km: one 256-entry table per group of 32 rows ("coreai-optimization
+// reference", Palettization: 2^n_bits centroids, per-grouped-channel; the
+// "Compression" page's recipe: int8 k-means, group 32). The km4 procedure on
+// the group's M = 32 K values, one 1024-thread workgroup per group:
+//   the keys are sorted in LDS (bitonic over P = M rounded up to a power of
+//   two); the sorted values' prefix sums are kept every 64 keys (a full prefix
+//   array would not fit next to the keys), so the prefix at any position is
+//   one of them plus at most 63 keys; in each Lloyd step thread j < 256 owns
+//   entry j, finds its cluster's upper edge by binary search and takes the
+//   exact mean from two prefixes.
+// ---------------------------------------------------------------------------
+constexpr int kKm8Threads = 1024;
+constexpr int kKm8MaxKeys = 65536;   // M <= 65536: K <= 2048
+
+// inclusive prefix sum over the 1024 threads of the workgroup
+__device__ __forceinline__ int64_t block_scan_1024(int64_t v, int64_t *wtot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    if (lane == 63) wtot[w] = v;
+    __syncthreads();
+    int64_t add = 0;
+    for (int i = 0; i < w; i++) add += wtot[i];
+    __syncthreads();
+    return v + add;
+}
+
+__global__ __launch_bounds__(kKm8Threads) void pack_int8km_kernel(const uint16_t *__restrict__ W, int K, int P,
+                                                                  int max_iter, uint8_t *__restrict__ codes,
+                                                                  uint16_t *__restrict__ lut) {
+    __shared__ uint16_t keys[kKm8MaxKeys];
+    __shared__ int64_t ps64[kKm8MaxKeys / 64 + 1];   // sum of the sorted values before key 64 c
+    __shared__ int64_t cent[256];
+    __shared__ int64_t pre[256];                      // prefix at each cluster's upper edge; then thresholds
+    __shared__ int bnd[256];
+    __shared__ int64_t wtot[16];
+    __shared__ int ndistinct;
+
+    const int tid = threadIdx.x;
+    const int M = 32 * K;
+    const int NC = M / 64;
+    const int64_t g = blockIdx.x;
+    const uint16_t *wg = W + g * (int64_t)M;
+
+    for (int v = tid; v < M / 8; v += kKm8Threads) {
+        const uint4 raw = reinterpret_cast<const uint4 *>(wg)[v];
+        const uint32_t d[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; e++) keys[8 * v + e] = sort_key((uint16_t)(d[e / 2] >> (16 * (e & 1))));
+    }
+    for (int i = M + tid; i < P; i += kKm8Threads) keys[i] = 0xFFFFu;
+    __syncthreads();
+    // bitonic sort, ascending; every thread takes compare-exchange pairs
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int p = tid; p < P / 2; p += kKm8Threads) {
+                const int i = 2 * p - (p & (j - 1));
+                const int ixj = i + j;
+                const uint16_t a = keys[i], b = keys[ixj];
+                if ((a > b) == ((i & k) == 0)) {
+                    keys[i] = b;
+                    keys[ixj] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // 64-key chunks: sums and distinct-value starts, then their prefix sums
+    int64_t csum = 0;
+    int ccnt = 0;
+    if (tid < NC) {
+        int64_t prev = tid ? units_of_f16(unsort_key(keys[64 * tid - 1])) : 0;
+        for (int i = 64 * tid; i < 64 * tid + 64; i++) {
+            const int64_t xv = units_of_f16(unsort_key(keys[i]));
+            csum += xv;
+            ccnt += (i == 0) || xv != prev;
+            prev = xv;
+        }
+    }
+    const int64_t sincl = block_scan_1024(csum, wtot);
+    const int64_t cincl = block_scan_1024(ccnt, wtot);
+    if (tid < NC) ps64[tid] = sincl - csum;
+    if (tid == NC - 1) {
+        ps64[NC] = sincl;
+        ndistinct = (int)cincl;
+    }
+    __syncthreads();
+    const bool few = ndistinct <= 256;
+    if (few) {
+        if (tid < NC) {
+            int rank = (int)(cincl - ccnt);
+            int64_t prev = tid ? units_of_f16(unsort_key(keys[64 * tid - 1])) : 0;
+            for (int i = 64 * tid; i < 64 * tid + 64; i++) {
+                const int64_t xv = units_of_f16(unsort_key(keys[i]));
+                if (i == 0 || xv != prev) cent[rank++] = xv;
+                prev = xv;
+            }
+        }
+        __syncthreads();
+        if (tid >= ndistinct && tid < 256) cent[tid] = units_of_f16(unsort_key(keys[M - 1]));
+    } else if (tid < 256) {
+        cent[tid] = units_of_f16(unsort_key(keys[(2 * tid + 1) * (M / 512)]));
+    }
+    __syncthreads();
+    if (!few) {
+        for (int it = 0; it < max_iter; it++) {
+            if (tid < 256) {
+                int b = M;
+                if (tid < 255) {
+                    // first sorted index whose doubled value exceeds c_j + c_{j+1}
+                    const int64_t t = cent[tid] + cent[tid + 1];
+                    int l = 0, h = M;
+                    while (l < h) {
+                        const int mid = (l + h) >> 1;
+                        if (2 * units_of_f16(unsort_key(keys[mid])) > t) h = mid;
+                        else l = mid + 1;
+                    }
+                    b = l;
+                }
+                int64_t pb = ps64[b >> 6];
+                for (int i = b & ~63; i < b; i++) pb += units_of_f16(unsort_key(keys[i]));
+                bnd[tid] = b;
+                pre[tid] = pb;
+            }
+            __syncthreads();
+            int64_t cn = 0;
+            bool moved = false;
+            if (tid < 256) {
+                const int lo = tid ? bnd[tid - 1] : 0;
+                const int64_t plo = tid ? pre[tid - 1] : 0;
+                const int64_t n = bnd[tid] - lo;
+                cn = n > 0 ? mean_to_f16_units(pre[tid] - plo, n) : cent[tid];
+                moved = cn != cent[tid];
+            }
+            __syncthreads();
+            if (tid < 256) cent[tid] = cn;
+            if (!__syncthreads_or(moved)) break;
+        }
+    }
+    // thresholds c_j + c_{j+1}; a value's index is how many lie below twice it
+    if (tid < 255) pre[tid] = cent[tid] + cent[tid + 1];
+    __syncthreads();
+    uint8_t *cg = codes + g * (int64_t)M;
+    for (int u = tid; u < M / 16; u += kKm8Threads) {
+        const uint4 r0 = reinterpret_cast<const uint4 *>(wg)[2 * u];
+        const uint4 r1 = reinterpret_cast<const uint4 *>(wg)[2 * u + 1];
+        const uint32_t d[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+        uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const int64_t x2 = 2 * units_of_f16((d[e / 2] >> (16 * (e & 1))) & 0xFFFFu);
+            int l = 0, h = 255;
+            while (l < h) {
+                const int mid = (l + h) >> 1;
+                if (pre[mid] < x2) l = mid + 1;
+                else h = mid;
+            }
+            out[e / 4] |= (uint32_t)l << (8 * (e & 3));
+        }
+        reinterpret_cast<uint4 *>(cg)[u] = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    if (tid < 256) lut[g * 256 + tid] = f16_of_units(cent[tid]);
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 static int blocks_grid(int64_t N, int64_t K) { return (int)((N * (K / 32) + 255) / 256); }
@@ -515,6 +683,15 @@ hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_pack_int8km(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
+                              hipStream_t st) {
+    int P = 1024;
+    while (P < 32 * K) P <<= 1;
+    hipLaunchKernelGGL(pack_int8km_kernel, dim3((unsigned)(N / 32)), dim3(kKm8Threads), 0, st, W, (int)K, P, max_iter,
+                       codes, lut);
+    return hipGetLastError();
 }
 
 }  // namespace qmv

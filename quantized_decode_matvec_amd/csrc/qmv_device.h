@@ -10,6 +10,8 @@
 //   KM4 : 32 indices per chunk; w = lut[row][c]
 //   INT4AFF: 32 codes u per chunk = one block; w = s * u + b (scale and bias
 //        per block [S1 sec. 1: affine int4 among the MoE gather formats])
+//   INT8KM: 16 byte indices per chunk; w = lut[row / 32][c], one 256-entry
+//        table per 32 rows [S3 "Palettization"; S5: int8 k-means, group 32]
 // Every decoded value below is exact in fp16 before scaling (the scale is
 // applied to the fp32 block sum), so the only rounding is fp32 accumulation.
 #pragma once
@@ -21,7 +23,7 @@ namespace qmv {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-enum Fmt { INT4 = 0, FP4 = 1, INT8 = 2, KM4 = 3, INT4AFF = 4 };
+enum Fmt { INT4 = 0, FP4 = 1, INT8 = 2, KM4 = 3, INT4AFF = 4, INT8KM = 5 };
 
 constexpr int kWave = 64;
 
@@ -34,7 +36,7 @@ __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
 
 // Bytes of codes per chunk is always 16; elements per chunk:
 template <int FMT> struct ChunkTraits {
-    static constexpr int kElems = (FMT == INT8) ? 16 : 32;
+    static constexpr int kElems = (FMT == INT8 || FMT == INT8KM) ? 16 : 32;
     static constexpr int kXWords = kElems / 2;   // half2 words of x per chunk
 };
 
@@ -209,6 +211,61 @@ __device__ __forceinline__ float chunk_dot_km4_imm(uint4 cw, const char *L, cons
             v.x = *reinterpret_cast<const _Float16 *>(L + a[2 * i]);
             v.y = *reinterpret_cast<const _Float16 *>(L + a[2 * i + 1]);
             acc = dot2(v, as_h2(xw[4 * d + i]), acc);
+        }
+    }
+    return acc;
+}
+
+// (byte S of w) << 1: the byte offset of a 2-byte table entry, one SDWA shift.
+template <int S>
+__device__ __forceinline__ uint32_t byte_shl1(uint32_t w) {
+    uint32_t r;
+    if constexpr (S == 0)
+        asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (S == 1)
+        asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (S == 2)
+        asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 1, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+
+// INT8KM: 16 byte indices into a 256-entry fp16 table at the compile-time LDS
+// address L (a static __shared__ array of a one-wave workgroup); each byte's
+// table offset is one SDWA shift and the table base folds into the LDS
+// instruction's immediate offset.
+__device__ __forceinline__ float chunk_dot_int8km_imm(uint4 cw, const char *L, const uint32_t (&xw)[8]) {
+    float acc = 0.f;
+    uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+        const uint32_t a0 = byte_shl1<0>(w[d]), a1 = byte_shl1<1>(w[d]);
+        const uint32_t a2 = byte_shl1<2>(w[d]), a3 = byte_shl1<3>(w[d]);
+        h2 v, u;
+        v.x = *reinterpret_cast<const _Float16 *>(L + a0);
+        v.y = *reinterpret_cast<const _Float16 *>(L + a1);
+        u.x = *reinterpret_cast<const _Float16 *>(L + a2);
+        u.y = *reinterpret_cast<const _Float16 *>(L + a3);
+        acc = dot2(v, as_h2(xw[2 * d + 0]), acc);
+        acc = dot2(u, as_h2(xw[2 * d + 1]), acc);
+    }
+    return acc;
+}
+
+// INT8KM with a table at any LDS address.
+__device__ __forceinline__ float chunk_dot_int8km(uint4 cw, const _Float16 *__restrict__ lut,
+                                                  const uint32_t (&xw)[8]) {
+    float acc = 0.f;
+    uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            h2 v;
+            v.x = lut[(w[d] >> (16 * i)) & 255u];
+            v.y = lut[(w[d] >> (16 * i + 8)) & 255u];
+            acc = dot2(v, as_h2(xw[2 * d + i]), acc);
         }
     }
     return acc;

@@ -41,6 +41,8 @@ hipError_t launch_pack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t 
                                hipStream_t st);
 hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
                            hipStream_t st);
+hipError_t launch_pack_int8km(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
+                              hipStream_t st);
 
 hipError_t launch_moe_route(const float *logits, int T, int E, int topk, int32_t *ids, float *weights,
                             hipStream_t st);

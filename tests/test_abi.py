@@ -65,10 +65,20 @@ def test_pack_validation(L):
     assert L.qpack_int4aff(FAKE, 1, 4, 48, FAKE, FAKE, S) == E_SHAPE
     assert L.qpack_int4aff(FAKE, 1, 4, 64, FAKE, half, S) == E_ALIGN
     assert L.qmatvec_int4aff(FAKE, half, 8, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
-    assert L.qdequant(5, FAKE, FAKE, 4, 64, FAKE, S) == E_DTYPE        # one past the last format
+    assert L.qdequant(6, FAKE, FAKE, 4, 64, FAKE, S) == E_DTYPE        # one past the last format
+    # int8km: rows in groups of 32, K <= 2048 for the packer, max_iter >= 1, 4-byte tables
+    assert L.qpack_int8km(FAKE, 48, 64, 20, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_int8km(FAKE, 64, 4096, 20, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_int8km(FAKE, 64, 64, 0, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_int8km(FAKE, 64, 64, 20, FAKE, half, S) == E_ALIGN
+    assert L.qpack_int8km(NUL, 64, 64, 20, FAKE, FAKE, S) == E_NULL
+    assert L.qmatvec_int8km(FAKE, FAKE, 40, 64, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_int8km(FAKE, half, 64, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
+    assert L.qdequant(5, FAKE, FAKE, 40, 64, FAKE, S) == E_SHAPE
 
 
-@pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff"])
+@pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
+                                  "qmatvec_int8km"])
 def test_matvec_validation(L, name):
     f = getattr(L, name)
     assert f(NUL, FAKE, 8, 64, FAKE, 1, 1, FAKE, S) == E_NULL
