@@ -341,41 +341,45 @@ def bench_int8_head(args):
 
 
 def bench_moe(args):
+    """The MoE layer (E = 256, top-8, H = 2048, I = 512) in the pages' gather
+    formats, at T = 1, 4, 8 tokens, fused entry point and three-call path."""
     import torch
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
     c = wl.moe()
     E, I2, H = c.W_gate_up.shape
     I = I2 // 2
-    guc, gus = qmv.qpack_int4(torch.from_numpy(c.W_gate_up.reshape(E * I2, H)).cuda())
-    dnc, dns = qmv.qpack_int4(torch.from_numpy(c.W_down.reshape(E * H, I)).cuda())
-    guc, gus = guc.view(E, I2, H // 2), gus.view(E, I2, H // 32)
-    dnc, dns = dnc.view(E, H, I // 2), dns.view(E, H, I // 32)
     out = {}
-    per_expert = algo_bytes("int4", I2, H) + algo_bytes("int4", H, I)
-    for T in (1, 4, 8):
-        x = torch.from_numpy(c.x[:T]).cuda()
-        lg = torch.from_numpy(c.logits[:T]).cuda()
-        ids = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
-        w = torch.empty((T, c.topk), dtype=torch.float32, device="cuda")
-        h = torch.empty((T, c.topk, I), dtype=torch.float16, device="cuda")
-        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    for fmt in ("int4", "int4aff", "int8km"):
+        guc, gus = qmv.qpack(fmt, torch.from_numpy(c.W_gate_up.reshape(E * I2, H)).cuda())
+        dnc, dns = qmv.qpack(fmt, torch.from_numpy(c.W_down.reshape(E * H, I)).cuda())
+        guc, gus = guc.view(E, I2, -1), gus.view(E, -1)
+        dnc, dns = dnc.view(E, H, -1), dns.view(E, -1)
+        per_expert = algo_bytes(fmt, I2, H) + algo_bytes(fmt, H, I)
+        for T in (1, 4, 8):
+            x = torch.from_numpy(c.x[:T]).cuda()
+            lg = torch.from_numpy(c.logits[:T]).cuda()
+            ids = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
+            w = torch.empty((T, c.topk), dtype=torch.float32, device="cuda")
+            h = torch.empty((T, c.topk, I), dtype=torch.float16, device="cuda")
+            y = torch.empty((T, H), dtype=torch.float32, device="cuda")
 
-        def layer(i):
-            qmv.qmoe_ffn("int4", guc, gus, dnc, dns, x, lg, c.topk, ids=ids, weights=w, h=h, y=y)
+            def layer(i):
+                qmv.qmoe_ffn(fmt, guc, gus, dnc, dns, x, lg, c.topk, ids=ids, weights=w, h=h, y=y)
 
-        def layer3(i):
-            qmv.qmoe_route(lg, c.topk, ids=ids, weights=w)
-            qmv.gather_qmatvec("int4", guc, gus, x, ids, epi="swiglu", y=h)
-            qmv.gather_qmatvec("int4", dnc, dns, h, ids, weights=w, epi="combine", x_per_slot=True, y=y)
+            def layer3(i):
+                qmv.qmoe_route(lg, c.topk, ids=ids, weights=w)
+                qmv.gather_qmatvec(fmt, guc, gus, x, ids, epi="swiglu", y=h)
+                qmv.gather_qmatvec(fmt, dnc, dns, h, ids, weights=w, epi="combine", x_per_slot=True, y=y)
 
-        ms = timed_graph(layer, args.steps, per_graph=16)
-        ms3 = timed_graph(layer3, args.steps, per_graph=16)
-        uniq = len(np.unique(ids.cpu().numpy()))
-        out["moe_T%d_us" % T] = round(ms * 1e3, 2)
-        out["moe_T%d_GBps" % T] = round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)
-        out["moe_T%d_3call_us" % T] = round(ms3 * 1e3, 2)
-        out["moe_T%d_experts" % T] = uniq
+            ms = timed_graph(layer, args.steps, per_graph=16)
+            ms3 = timed_graph(layer3, args.steps, per_graph=16)
+            uniq = len(np.unique(ids.cpu().numpy()))
+            out["moe_%s_T%d_us" % (fmt, T)] = round(ms * 1e3, 2)
+            out["moe_%s_T%d_GBps" % (fmt, T)] = round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)
+            out["moe_%s_T%d_3call_us" % (fmt, T)] = round(ms3 * 1e3, 2)
+            out["moe_T%d_experts" % T] = uniq
+        del guc, gus, dnc, dns
     return out
 
 

@@ -197,7 +197,9 @@ size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epi
  *  epi == QMV_EPI_COMBINE: y fp32 [T][N] = sum over slots of
  *                          weights[t][slot] * (W[ids[t][slot]] x)[n].
  * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096; 32 <= K <= 8192 (4096
- * for INT8), K % 32 == 0. COMBINE sums the slots of a token in slot order,
+ * for INT8 and INT8KM), K % 32 == 0. INT8KM: N % 32 == 0 (each expert's
+ * tables cover groups of 32 rows; with SWIGLU, N % 64 == 0 so the gate and up
+ * halves are whole groups). COMBINE sums the slots of a token in slot order,
  * so the result does not depend on scheduling. The workspace, if
  * gather_qmatvec_workspace_bytes(...) is nonzero, must hold that many
  * bytes, 256-byte aligned; otherwise it may be NULL. */

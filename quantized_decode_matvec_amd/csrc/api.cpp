@@ -57,7 +57,7 @@ qmv_status check_mv(const void *codes, const void *plane, size_t plane_align, in
 inline bool rows_fit(qmv_format f, int64_t N) { return f != QMV_INT8KM || N % 32 == 0; }
 
 // largest K the expert gather handles: 256 chunks per row of codes
-int64_t gather_max_k(qmv_format f) { return f == QMV_INT8 ? 4096 : 8192; }
+int64_t gather_max_k(qmv_format f) { return (f == QMV_INT8 || f == QMV_INT8KM) ? 4096 : 8192; }
 
 size_t plane_alignment(qmv_format f) {
     switch (f) {
@@ -209,7 +209,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
                           const void *x, qmv_dtype xdt, int x_per_slot, int T, int topk, const int32_t *ids,
                           const float *weights, qmv_epilogue epi, void *y, void *workspace, size_t ws_bytes,
                           void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;
     if (epi != QMV_EPI_NONE && epi != QMV_EPI_SWIGLU && epi != QMV_EPI_COMBINE) return QMV_E_DTYPE;
     if (xdt != QMV_F16) return QMV_E_DTYPE;
     if (!codes || !plane || !x || !ids || !y) return QMV_E_NULL;
@@ -218,6 +218,8 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
     if (T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
     if (x_per_slot != 0 && x_per_slot != 1) return QMV_E_SHAPE;
     if (epi == QMV_EPI_SWIGLU && N % 2 != 0) return QMV_E_SHAPE;
+    // int8km tables cover 32 rows: whole groups, and gate and up halves of whole groups
+    if (!rows_fit(fmt, N) || (fmt == QMV_INT8KM && epi == QMV_EPI_SWIGLU && (N / 2) % 32 != 0)) return QMV_E_SHAPE;
     if (N > (int64_t(1) << 40) / K / E) return QMV_E_SHAPE;
     size_t need = qmv::gather_workspace_bytes(T, topk, E, N, epi);
     if (need > 0 && (!workspace || ws_bytes < need)) return QMV_E_WORKSPACE;
@@ -232,7 +234,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
 qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane, const void *dn_codes,
                     const void *dn_plane, int E, int64_t H, int64_t I, const float *logits, const void *x, int T,
                     int topk, int32_t *ids, float *weights, void *h, float *y, void *stream) {
-    if (fmt < QMV_INT4 || fmt > QMV_INT4AFF) return QMV_E_DTYPE;
+    if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;
     if (!gu_codes || !gu_plane || !dn_codes || !dn_plane || !logits || !x || !ids || !weights || !h || !y)
         return QMV_E_NULL;
     if (E < 1 || E > 4096 || T < 1 || T > 8 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;

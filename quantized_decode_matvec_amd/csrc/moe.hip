@@ -159,7 +159,7 @@ __device__ __forceinline__ float plane_bias(const void *plane, int64_t row, int 
 }
 
 template <int FMT>
-__device__ __forceinline__ int64_t code_row_bytes(int K) { return (FMT == INT8) ? K : K / 2; }
+__device__ __forceinline__ int64_t code_row_bytes(int K) { return (FMT == INT8 || FMT == INT8KM) ? K : K / 2; }
 
 // expert e's code and plane slabs
 template <int FMT>
@@ -172,6 +172,8 @@ __device__ __forceinline__ void expert_slabs(const uint8_t *codes, const void *p
         plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * 16;
     else if constexpr (FMT == INT4AFF)
         plane_e = reinterpret_cast<const uint32_t *>(plane) + e * N * (K / 32);
+    else if constexpr (FMT == INT8KM)
+        plane_e = reinterpret_cast<const uint16_t *>(plane) + e * (N / 32) * 256;   // N % 32 == 0
     else
         plane_e = reinterpret_cast<const uint16_t *>(plane) + e * N * (K / 32);
 }
@@ -183,6 +185,7 @@ __device__ __forceinline__ float chunk_dot(uint4 cw, const uint32_t (&xw)[ChunkT
     else if constexpr (FMT == INT4AFF) return chunk_dot_int4<true>(cw, xw);
     else if constexpr (FMT == FP4) return chunk_dot_fp4(cw, xw);
     else if constexpr (FMT == INT8) return chunk_dot_int8(cw, xw);
+    else if constexpr (FMT == INT8KM) return chunk_dot_int8km(cw, lut, xw);
     else return chunk_dot_km4(cw, lut, xw);
 }
 
@@ -235,11 +238,12 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
     const int K = a.K;
-    const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+    const int cpr = (FMT == INT8 || FMT == INT8KM) ? K / 16 : K / 32;
     const int nb = K / 32;
     const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
 
     constexpr bool AFF = (FMT == INT4AFF);
+    constexpr bool KM8 = (FMT == INT8KM);
     uint32_t xr[CPL][PB][XW];
     float xsum[AFF ? CPL : 1][AFF ? PB : 1];
 #pragma unroll
@@ -288,6 +292,26 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
                 ldst[i] = lsrc[pr * 8 + (i % 8)];
             }
             wave_fence();
+        } else if constexpr (KM8) {
+            // one 256-entry table per row group: its RPW rows are aligned and
+            // lie in one group of 32 (the first row, clamped, names it)
+            const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane_e);
+            uint32_t *ldst = reinterpret_cast<uint32_t *>(lut_w);
+            uint32_t tv[R][2];
+#pragma unroll
+            for (int g = 0; g < R; g++) {
+                int gl = (EPI == EPI_SWIGLU) ? (g % G) : g;
+                int64_t lrow = l0 + gl * RPW;
+                lrow = lrow < tile1 ? lrow : tile1 - 1;
+                int64_t pr = (EPI == EPI_SWIGLU && g >= G) ? lrow + a.out_rows : lrow;
+#pragma unroll
+                for (int q = 0; q < 2; q++) tv[g][q] = lsrc[(pr / 32) * 128 + q * kWave + lane];
+            }
+#pragma unroll
+            for (int g = 0; g < R; g++)
+#pragma unroll
+                for (int q = 0; q < 2; q++) ldst[g * 128 + q * kWave + lane] = tv[g][q];
+            wave_fence();
         }
         float acc[R * PB];
 #pragma unroll
@@ -297,13 +321,13 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
                 float s = 0.f;
 #pragma unroll
                 for (int j = 0; j < CPL; j++) {
-                    float d = chunk_dot<FMT>(cw[g][j], xr[j][p], lut_w + (g * RPW + rsub) * 16);
-                    s = (FMT == KM4) ? s + d : __builtin_fmaf(d, sc[g][j], s);
+                    float d = chunk_dot<FMT>(cw[g][j], xr[j][p], KM8 ? lut_w + g * 256 : lut_w + (g * RPW + rsub) * 16);
+                    s = (FMT == KM4 || KM8) ? s + d : __builtin_fmaf(d, sc[g][j], s);
                     if constexpr (AFF) s = __builtin_fmaf(xsum[j][p], bi[g][j], s);
                 }
                 acc[g * PB + p] = s;
             }
-        if constexpr (FMT == KM4) wave_fence();   // the next iteration rewrites the tables
+        if constexpr (FMT == KM4 || KM8) wave_fence();   // the next iteration rewrites the tables
         if constexpr (EPI == EPI_SWIGLU) {
             // full reduction: every lane gets every row sum, so each gate sum
             // meets its up sum (group g + G) in the same lane
@@ -351,7 +375,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     __shared__ int s_pairs[8];
     __shared__ int s_np;
     __shared__ int s_expert;
-    __shared__ _Float16 lut_lds[(FMT == KM4) ? 4 * R * RPW * 16 : 1];
+    constexpr int LUT_HALVES = (FMT == KM4) ? R * RPW * 16 : (FMT == INT8KM ? R * 256 : 1);   // per wave
+    __shared__ _Float16 lut_lds[4 * LUT_HALVES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int npairs = a.T * a.topk;
@@ -417,7 +442,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     const uint8_t *codes_e;
     const void *plane_e;
     expert_slabs<FMT>(a.codes, a.plane, e, a.N, a.K, codes_e, plane_e);
-    _Float16 *lut_w = lut_lds + (tid >> 6) * R * RPW * 16;
+    _Float16 *lut_w = lut_lds + (tid >> 6) * LUT_HALVES;
     int p0 = 0;
     for (; p0 + 2 <= np; p0 += 2)
         gather_pass<FMT, 2, LPR, CPL, R, EPI>(a, codes_e, plane_e, s_pairs + p0, lut_w);
@@ -434,7 +459,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 // ---------------------------------------------------------------------------
 template <int FMT, int R, int CPL>
 constexpr int combine_slot_batch() {
-    constexpr int per_slot = 5 * R * CPL + ChunkTraits<FMT>::kXWords * CPL + (FMT == KM4 ? 1 : 0);
+    constexpr int per_slot = 5 * R * CPL + ChunkTraits<FMT>::kXWords * CPL + (FMT == KM4 ? 1 : (FMT == INT8KM ? 2 : 0));
     constexpr int sb = 192 / per_slot;
     return sb < 1 ? 1 : (sb > 8 ? 8 : sb);
 }
@@ -444,13 +469,17 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
     constexpr int RPW = kWave / LPR;
     constexpr int XW = ChunkTraits<FMT>::kXWords;
     constexpr int ROWS = R * RPW;
-    __shared__ _Float16 lut_lds[(FMT == KM4) ? SB * ROWS * 16 : 1];
+    // int8km: ROWS divides 32 and row0 is a multiple of ROWS, so the wave's
+    // rows share one table per slot
+    constexpr bool KM8 = (FMT == INT8KM);
+    static_assert(!KM8 || 32 % ROWS == 0, "int8km: a wave's rows within one group");
+    __shared__ _Float16 lut_lds[(FMT == KM4) ? SB * ROWS * 16 : (KM8 ? SB * 256 : 1)];
     const int lane = threadIdx.x;
     const int sub = lane % LPR;
     const int rsub = lane / LPR;
     const int t = blockIdx.y;
     const int K = a.K;
-    const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+    const int cpr = (FMT == INT8 || KM8) ? K / 16 : K / 32;
     const int nb = K / 32;
     const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
     const int64_t row0 = (int64_t)blockIdx.x * ROWS;
@@ -468,7 +497,7 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
         float xs[AFF ? SB : 1][AFF ? CPL : 1];
         uint32_t xr[SB][CPL][XW];
         float ws[SB];
-        uint32_t lutv[SB];
+        uint32_t lutv[SB][KM8 ? 2 : 1];
 #pragma unroll
         for (int b = 0; b < SB; b++) {
             // slots past topk repeat the last one with weight 0
@@ -502,13 +531,23 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
             if constexpr (FMT == KM4) {
                 int rr = (lane / 8) % ROWS;
                 rr = rr <= last ? rr : last;
-                lutv[b] = reinterpret_cast<const uint32_t *>(plane_e)[(row0 + rr) * 8 + (lane % 8)];
+                lutv[b][0] = reinterpret_cast<const uint32_t *>(plane_e)[(row0 + rr) * 8 + (lane % 8)];
+            } else if constexpr (KM8) {
+#pragma unroll
+                for (int q = 0; q < 2; q++)
+                    lutv[b][q] = reinterpret_cast<const uint32_t *>(plane_e)[(row0 / 32) * 128 + q * kWave + lane];
             }
         }
         if constexpr (FMT == KM4) {
 #pragma unroll
             for (int b = 0; b < SB; b++)
-                if (lane < ROWS * 8) reinterpret_cast<uint32_t *>(lut_lds)[b * ROWS * 8 + lane] = lutv[b];
+                if (lane < ROWS * 8) reinterpret_cast<uint32_t *>(lut_lds)[b * ROWS * 8 + lane] = lutv[b][0];
+            wave_fence();
+        } else if constexpr (KM8) {
+#pragma unroll
+            for (int b = 0; b < SB; b++)
+#pragma unroll
+                for (int q = 0; q < 2; q++) reinterpret_cast<uint32_t *>(lut_lds)[b * 128 + q * kWave + lane] = lutv[b][q];
             wave_fence();
         }
 #pragma unroll
@@ -517,11 +556,12 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
             for (int g = 0; g < R; g++)
 #pragma unroll
                 for (int j = 0; j < CPL; j++) {
-                    float d = chunk_dot<FMT>(cw[b][g][j], xr[b][j], lut_lds + (b * ROWS + g * RPW + rsub) * 16);
+                    float d = chunk_dot<FMT>(cw[b][g][j], xr[b][j],
+                                             KM8 ? lut_lds + b * 256 : lut_lds + (b * ROWS + g * RPW + rsub) * 16);
                     acc[g] = __builtin_fmaf(d, ws[b] * sc[b][g][j], acc[g]);
                     if constexpr (AFF) acc[g] = __builtin_fmaf(xs[b][j], ws[b] * bi[b][g][j], acc[g]);
                 }
-        if constexpr (FMT == KM4) wave_fence();   // the next batch rewrites the tables
+        if constexpr (FMT == KM4 || KM8) wave_fence();   // the next batch rewrites the tables
     }
     using Red = GroupReduce<R, LPR>;
     Red::run(acc, lane);
@@ -545,7 +585,7 @@ static hipError_t launch_expert_major(GatherArgs a, int umax, hipStream_t st) {
     // gate and up rows in pairs; fewer rows per iteration on long rows (and
     // for table lookups, which hold more registers) to stay within the
     // register file
-    constexpr int heavy = (FMT == KM4) ? CPL + 1 : CPL;
+    constexpr int heavy = (FMT == KM4 || FMT == INT8KM) ? CPL + 1 : CPL;
     constexpr int R = (EPI == EPI_SWIGLU) ? (heavy >= 3 ? 2 : 4) : (heavy >= 3 ? 1 : 2);
     constexpr int RPW = kWave / LPR;
     constexpr int G = (EPI == EPI_SWIGLU) ? R / 2 : R;
@@ -628,6 +668,7 @@ static hipError_t launch_any(int fmt, GatherArgs a, int epi, bool fused, int uma
     case FP4: err = launch_fmt<FP4>(a, epi, fused, umax, &handled, st); break;
     case INT8: err = launch_fmt<INT8>(a, epi, fused, umax, &handled, st); break;
     case KM4: err = launch_fmt<KM4>(a, epi, fused, umax, &handled, st); break;
+    case INT8KM: err = launch_fmt<INT8KM>(a, epi, fused, umax, &handled, st); break;
     default: err = launch_fmt<INT4AFF>(a, epi, fused, umax, &handled, st); break;
     }
     if (err != hipSuccess) return err;

@@ -16,7 +16,7 @@ from tests.gpu_helpers import RTOL, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = ["int4", "fp4", "int8", "km4", "int4aff"]
+FORMATS = ["int4", "fp4", "int8", "km4", "int4aff", "int8km"]
 # E, H, I, T, topk
 CASES = [
     (16, 256, 128, 1, 3),
