@@ -16,6 +16,8 @@ Formats (codes and planes as numpy arrays; W is N x K row-major, K % 32 == 0):
 * km4:  codes uint8 [N, K/2] (4-bit indices), lut uint16 [N, 16] (fp16 bits).
 * int4aff: codes uint8 [N, K/2] (u in 0..15), plane uint32 [N, K/32] (fp16 scale | fp16 bias << 16).
 * int8km: codes uint8 [N, K] (8-bit indices), lut uint16 [N/32, 256] (fp16 bits), N % 32 == 0.
+* km4 + int8 outliers: km4 codes and tables of the row with its P largest-magnitude
+  entries zeroed, plus ocol uint16 [N, P] (increasing), oval int8 [N, P], oscale uint16 [N].
 """
 from __future__ import annotations
 
@@ -66,6 +68,8 @@ def lib():
         L.orc_pack_int4aff.argtypes = [P, i64, i64, P, P]
         L.orc_pack_km4.argtypes = [P, i64, i64, ci, P, P, P]
         L.orc_pack_int8km.argtypes = [P, i64, i64, ci, P, P, P]
+        L.orc_pack_km4o.argtypes = [P, i64, i64, ci, ci, P, P, P, P, P]
+        L.orc_matvec_km4o.argtypes = [P, P, P, P, P, i64, i64, ci, P, ci, P]
         L.orc_dequant.argtypes = [ci, P, P, i64, i64, P]
         L.orc_matvec.argtypes = [ci, P, P, i64, i64, P, ci, P, i64, P]
         L.orc_moe_route.argtypes = [P, ci, ci, ci, P, P]
@@ -178,6 +182,38 @@ def pack_int8km(W_f16, max_iter: int = 20, return_iters: bool = False):
     if return_iters:
         return codes, lut, iters
     return codes, lut
+
+
+def pack_km4o(W_f16, P: int, max_iter: int = 20):
+    """4-bit k-means rows plus P int8 outliers per row. Returns (codes uint8
+    [N, K/2], lut uint16 [N, 16], ocol uint16 [N, P], oval int8 [N, P],
+    oscale uint16 [N] fp16 bits)."""
+    W = np.ascontiguousarray(np.asarray(W_f16, dtype=np.float16)).view(np.uint16)
+    N, K = _check_shape(W)
+    assert 0 <= P <= K
+    codes = np.zeros((N, K // 2), np.uint8)
+    lut = np.zeros((N, 16), np.uint16)
+    ocol = np.zeros((N, P), np.uint16)
+    oval = np.zeros((N, P), np.int8)
+    oscale = np.zeros((N,), np.uint16)
+    lib().orc_pack_km4o(_p(W), N, K, int(P), int(max_iter), _p(codes), _p(lut), _p(ocol), _p(oval), _p(oscale))
+    return codes, lut, ocol, oval, oscale
+
+
+def matvec_km4o(codes, lut, ocol, oval, oscale, x) -> np.ndarray:
+    """y [B, N] = W_hat x in fp64, W_hat = table value + outlier (if any)."""
+    codes, lut = np.ascontiguousarray(codes), np.ascontiguousarray(lut, dtype=np.uint16)
+    ocol = np.ascontiguousarray(ocol, dtype=np.uint16)
+    oval = np.ascontiguousarray(oval, dtype=np.int8)
+    oscale = np.ascontiguousarray(oscale, dtype=np.uint16)
+    N, K = codes.shape[0], codes.shape[1] * 2
+    P = ocol.shape[1]
+    x = np.ascontiguousarray(np.atleast_2d(np.asarray(x)).astype(np.float64))
+    assert x.shape[1] == K and ocol.shape == (N, P) and oval.shape == (N, P)
+    B = x.shape[0]
+    y = np.zeros((B, N), np.float64)
+    lib().orc_matvec_km4o(_p(codes), _p(lut), _p(ocol), _p(oval), _p(oscale), N, K, int(P), _p(x), B, _p(y))
+    return y
 
 
 def pack(fmt: str, W, **kw):

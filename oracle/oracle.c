@@ -469,6 +469,92 @@ void orc_pack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 4-bit k-means rows plus int8 outliers [S4 "NEXT per lever", Stream D:     */
+/* a mixed int4 + int8-outlier matvec built on the int4 k-means linear, to   */
+/* bridge the int4 quality cliff at about int4 bandwidth].                   */
+/*                                                                          */
+/* Reading (the page names the idea only): per row, the P entries of largest */
+/* magnitude (ties to the lower column) are outliers, listed by increasing   */
+/* column. They are stored as int8 with one fp16 scale per row, the int8    */
+/* per-row recipe: s = fp16(fp32(max |w|) / 127), q = clamp(rint(w / s),     */
+/* -127, 127) in fp32 (s = 0 gives q = 0). The row with its outliers set to  */
+/* +0 is palettized by the 4-bit k-means above. The weight is the sum of the */
+/* two parts: W_hat[n][k] = lut[n][code] + (k an outlier ? s * q : 0).       */
+/* ------------------------------------------------------------------------ */
+
+/* W_f16: N x K fp16 bits; codes N x K/2; lut N x 16; ocol N x P (uint16);
+   oval N x P (int8); oscale N (fp16 bits). 0 <= P <= K. */
+void orc_pack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int P, int max_iter,
+                   uint8_t *codes, uint16_t *lut, uint16_t *ocol, int8_t *oval, uint16_t *oscale)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t n = 0; n < N; n++) {
+        const uint16_t *w = W_f16 + n * K;
+        uint16_t *res = malloc(sizeof(uint16_t) * K);
+        char *taken = calloc(K, 1);
+        memcpy(res, w, sizeof(uint16_t) * K);
+        /* the P largest magnitudes, ties to the lower column */
+        for (int o = 0; o < P; o++) {
+            int64_t best = -1;
+            for (int64_t k = 0; k < K; k++)
+                if (!taken[k] && (best < 0 || fabs(orc_f16_to_f64(w[k])) > fabs(orc_f16_to_f64(w[best]))))
+                    best = k;
+            taken[best] = 1;
+        }
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; k++)
+            if (taken[k] && fabsf((float)orc_f16_to_f64(w[k])) > amax)
+                amax = fabsf((float)orc_f16_to_f64(w[k]));
+        uint16_t s16 = orc_f64_to_f16((double)(amax / 127.0f));
+        float s = (float)orc_f16_to_f64(s16);
+        oscale[n] = s16;
+        int o = 0;
+        for (int64_t k = 0; k < K; k++) {
+            if (!taken[k])
+                continue;
+            float q = 0.0f;
+            if (s != 0.0f) {
+                q = rintf((float)orc_f16_to_f64(w[k]) / s);
+                if (q > 127.0f) q = 127.0f;
+                if (q < -127.0f) q = -127.0f;
+            }
+            ocol[n * P + o] = (uint16_t)k;
+            oval[n * P + o] = (int8_t)q;
+            o++;
+            res[k] = 0x0000;
+        }
+        km4_row(res, K, max_iter, codes + n * (K / 2), lut + n * 16);
+        free(res);
+        free(taken);
+    }
+}
+
+/* y[b][n] = sum over k ascending of W_hat[n][k] * x[b][k] in fp64, W_hat as
+   above (the dense part and the outlier part of a weight summed first). */
+void orc_matvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
+                     const uint16_t *oscale, int64_t N, int64_t K, int P, const double *x, int B, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; n++) {
+        double *wh = malloc(sizeof(double) * K);
+        for (int64_t k = 0; k < K; k++) {
+            uint8_t byte = codes[n * (K / 2) + k / 2];
+            int c = (k % 2 == 0) ? (byte & 0xf) : (byte >> 4);
+            wh[k] = orc_f16_to_f64(lut[n * 16 + c]);
+        }
+        for (int o = 0; o < P; o++)
+            wh[ocol[n * P + o]] += orc_f16_to_f64(oscale[n]) * (double)oval[n * P + o];
+        for (int b = 0; b < B; b++) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; k++)
+                acc += wh[k] * x[b * K + k];
+            y[b * N + n] = acc;
+        }
+        free(wh);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* 8-bit k-means palettization, one 256-entry fp16 table per group of 32     */
 /* consecutive output rows [S3 "Palettization": 2^n_bits centroids, 1-D     */
 /* k-means, per-grouped-channel granularity; S3 "The LM head + embeddings"  */

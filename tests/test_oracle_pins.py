@@ -779,3 +779,75 @@ def test_int8km_matvec_moe_and_argmax():
     g = Wg @ xt[0].astype(np.float64)
     h = (g[:I] / (1 + np.exp(-g[:I])) * g[I:]).astype(np.float16).astype(np.float64)
     assert np.allclose(y[0], Wd @ h, rtol=1e-12, atol=1e-12)
+
+
+# --- 4-bit k-means rows plus int8 outliers ---
+
+def _km4o_dense_numpy(codes, lut, ocol, oval, oscale):
+    """W_hat assembled with numpy from the packed pieces: table lookups plus the
+    scattered int8 outliers times the row scale."""
+    idx = _unpack_nibbles(codes)
+    L = lut.view(np.float16).astype(np.float64)
+    W = np.take_along_axis(L, idx.astype(np.int64), axis=1)
+    s = oscale.view(np.float16).astype(np.float64)
+    for n in range(W.shape[0]):
+        W[n, ocol[n].astype(np.int64)] += s[n] * oval[n].astype(np.float64)
+    return W
+
+
+def test_km4o_without_outliers_is_km4():
+    rng = np.random.default_rng(50)
+    W = (rng.standard_normal((9, 256)) * 0.02).astype(np.float16)
+    codes, lut, ocol, oval, oscale = oracle.pack_km4o(W, 0)
+    c4, l4 = oracle.pack_km4(W)
+    assert np.array_equal(codes, c4) and np.array_equal(lut, l4)
+    assert ocol.shape == (9, 0) and np.all(oscale == 0)
+
+
+def test_km4o_outliers_are_the_largest_magnitudes_as_textbook_int8():
+    """Selection equals a numpy lexsort on (-|w|, column); the values are the
+    absmax int8 recipe on them (numpy); the 4-bit part is the k-means of the
+    row with the outliers zeroed."""
+    rng = np.random.default_rng(51)
+    W = (rng.standard_normal((12, 512)) * 0.02).astype(np.float16)
+    W[:, ::37] *= 8
+    W[3, [10, 20, 30]] = np.float16(0.5)          # equal magnitudes: lower columns first
+    W[3, [15, 25]] = np.float16(-0.5)
+    W[5] = 0                                       # all-zero row: scale 0, q 0
+    P = 6
+    codes, lut, ocol, oval, oscale = oracle.pack_km4o(W, P)
+    for n in range(W.shape[0]):
+        a = np.abs(W[n].astype(np.float64))
+        order = np.lexsort((np.arange(512), -a))[:P]
+        cols = np.sort(order)
+        assert np.array_equal(ocol[n], cols)
+        amax = np.float32(a[cols].max())
+        s = np.float16(amax / np.float32(127))
+        assert oscale[n] == s.view(np.uint16)
+        if s == 0:
+            q = np.zeros(P)
+        else:
+            q = np.clip(np.rint(W[n, cols].astype(np.float32) / np.float32(s)), -127, 127)
+        assert np.array_equal(oval[n].astype(np.float64), q.astype(np.float64))
+        res = W[n].copy()
+        res[cols] = 0
+        c4, l4 = oracle.pack_km4(res[None, :])
+        assert np.array_equal(codes[n], c4[0]) and np.array_equal(lut[n], l4[0])
+    assert list(ocol[3][:5]) == [10, 15, 20, 25, 30]
+
+
+def test_km4o_matvec_equals_numpy_gemm_and_outliers_help():
+    rng = np.random.default_rng(52)
+    W = (rng.standard_normal((40, 256)) * 0.02).astype(np.float16)
+    big = rng.choice(256, size=4, replace=False)
+    W[:, big] = (rng.standard_normal((40, 4)) * 0.5).astype(np.float16)   # heavy columns
+    x = rng.standard_normal((3, 256)).astype(np.float16)
+    packed = oracle.pack_km4o(W, 4)
+    D = _km4o_dense_numpy(*packed)
+    y = oracle.matvec_km4o(*packed, x)
+    assert np.allclose(y, x.astype(np.float64) @ D.T, rtol=1e-13, atol=1e-15)
+    # outliers taken out of the table lower the weight error against plain km4
+    c4, l4 = oracle.pack_km4(W)
+    e4 = np.abs(oracle.dequant("km4", c4, l4) - W.astype(np.float64)).mean()
+    eo = np.abs(D - W.astype(np.float64)).mean()
+    assert eo < 0.75 * e4
