@@ -251,6 +251,18 @@ def main():
                 extras["%s_B%d_us" % (fmt, bb)] = round(msb * 1e3, 2)
                 extras["%s_B%d_GBps" % (fmt, bb)] = round(nb / (msb * 1e-3) / 1e9, 1)
             del pk
+        # km4 rows plus 16 int8 outliers per row (0.8% of the weights)
+        e0.record()
+        pko = qmv.qpack_km4o(W, 16)
+        e1.record()
+        torch.cuda.synchronize()
+        extras["km4o16_pack_ms"] = round(e0.elapsed_time(e1), 3)
+        pks = [pko] + [tuple(a.clone() for a in pko) for _ in range(len(copies) - 1)]
+        nbo = algo_bytes("km4", N_ROWS, K_DIM) + N_ROWS * (16 * 3 + 2)
+        mso = timed(lambda i: qmv.qmatvec_km4o(*pks[i % len(pks)], x1, y=y[:1]), args.steps, args.warmup)
+        extras["km4o16_B1_us"] = round(mso * 1e3, 2)
+        extras["km4o16_B1_GBps"] = round(nbo / (mso * 1e-3) / 1e9, 1)
+        del pks, pko
         # fp16 dense GEMV on the same shape (torch), for the per-op ratio against fp16
         wcp = [W] + [W.clone() for _ in range(1)]
         msd = timed(lambda i: torch.matmul(x1, wcp[i % 2].t()), max(10, args.steps // 4), 5)

@@ -162,6 +162,31 @@ qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t 
 qmv_status qmatvec_int8km(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                           const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 
+/* ---------------------------------------------------------------------- */
+/* 4-bit k-means rows plus int8 outliers ["Kernel campaign - session       */
+/* handoff", NEXT per lever, Stream D: a mixed int4 + int8-outlier matvec  */
+/* on the int4 k-means linear, bridging the int4 quality cliff at about    */
+/* int4 bandwidth]. Per row, the nout entries of largest magnitude (ties  */
+/* to the lower column) are outliers, listed by increasing column: ocol    */
+/* uint16 [N][nout], oval int8 [N][nout], and one fp16 scale per row       */
+/* oscale [N] = fp16(max |w| of the outliers / 127), oval = clamp(rint(w / */
+/* scale), -127, 127) (scale 0: 0). The row with its outliers set to +0 is */
+/* palettized exactly as qpack_km4 (codes [N][K/2], lut [N][16]). The     */
+/* weight is lut[n][code] + (k an outlier ? oscale[n] * oval : 0).        */
+/* 0 <= nout <= min(256, K); K <= 4096 (packing) / 65536 (matvec); with   */
+/* nout == 0, ocol and oval may be NULL and oscale is written as zeros.   */
+/* ---------------------------------------------------------------------- */
+qmv_status qpack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int nout, int max_iter,
+                      uint8_t *codes, uint16_t *lut, uint16_t *ocol, int8_t *oval, uint16_t *oscale,
+                      void *stream);
+
+/* y[b][n] = sum_k W_hat[n][k] * x[b][k] with the outliers added in fp32;
+ * x fp16 or fp32 [B][K], B <= 8, y fp32 [B][N]; the tables and codes as
+ * qmatvec_km4. */
+qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
+                        const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
+                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+
 /* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
  * weight is exact in fp32, except affine int4, where s * u + b is rounded
  * once to the nearest fp32) [S3 "Theoretical size" for the plane shapes]. */

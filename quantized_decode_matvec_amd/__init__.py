@@ -26,7 +26,7 @@ EPILOGUES = {"none": QMV_EPI_NONE, "swiglu": QMV_EPI_SWIGLU, "combine": QMV_EPI_
 # every symbol include/qmv.h declares
 EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_km4", "qpack_int4aff",
            "qpack_int8km", "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
-           "qmatvec_int8km", "qdequant",
+           "qmatvec_int8km", "qpack_km4o", "qmatvec_km4o", "qdequant",
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read")
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "qmatvec_km4": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_int4aff": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_int8km": ([P, P, i64, i64, P, ci, ci, P, P], ci),
+            "qpack_km4o": ([P, i64, i64, ci, ci, P, P, P, P, P, P], ci),
+            "qmatvec_km4o": ([P, P, P, P, P, i64, i64, ci, P, ci, ci, P, P], ci),
             "qdequant": ([ci, P, P, i64, i64, P, P], ci),
             "qmoe_route": ([P, ci, ci, ci, P, P, P], ci),
             "gather_qmatvec_workspace_bytes": ([ci, ci, ci, i64, ci], sz),
@@ -224,6 +226,36 @@ def qmatvec_int4aff(codes, plane, x, y=None, stream=None):
 
 def qmatvec_int8km(codes, lut, x, y=None, stream=None):
     return _matvec("qmatvec_int8km", "int8km", codes, lut, x, y, stream)
+
+
+def qpack_km4o(W, nout, max_iter=20, stream=None):
+    """W fp16 [N, K] -> (codes [N, K/2] uint8, lut [N, 16] uint16, ocol [N, nout]
+    uint16, oval [N, nout] int8, oscale [N] uint16): 4-bit k-means rows plus
+    nout int8 outliers per row."""
+    torch = _torch()
+    if W.dtype != torch.float16:
+        raise TypeError("qpack_km4o takes fp16 weights")
+    N, K = W.shape
+    codes = _empty((N, K // 2), torch.uint8, W)
+    lut = _empty((N, 16), torch.uint16, W)
+    ocol = _empty((N, nout), torch.uint16, W)
+    oval = _empty((N, nout), torch.int8, W)
+    oscale = _empty((N,), torch.uint16, W)
+    _check("qpack_km4o", lib().qpack_km4o(_ptr(W), N, K, int(nout), int(max_iter), _ptr(codes), _ptr(lut),
+                                          _ptr(ocol), _ptr(oval), _ptr(oscale), _stream(stream)))
+    return codes, lut, ocol, oval, oscale
+
+
+def qmatvec_km4o(codes, lut, ocol, oval, oscale, x, y=None, stream=None):
+    torch = _torch()
+    N, K = codes.shape[0], codes.shape[1] * 2
+    nout = ocol.shape[1]
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    B = x2.shape[0]
+    y = _empty((B, N), torch.float32, codes) if y is None else y
+    _check("qmatvec_km4o", lib().qmatvec_km4o(_ptr(codes), _ptr(lut), _ptr(ocol), _ptr(oval), _ptr(oscale), N, K,
+                                              int(nout), _ptr(x2), _dt(x2), B, _ptr(y), _stream(stream)))
+    return y
 
 
 def qmatvec(fmt, codes, plane, x, y=None, stream=None):

@@ -167,6 +167,30 @@ qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t 
     return launch_status(qmv::launch_matvec(QMV_INT4AFF, codes, plane, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
+qmv_status qpack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int nout, int max_iter, uint8_t *codes,
+                      uint16_t *lut, uint16_t *ocol, int8_t *oval, uint16_t *oscale, void *stream) {
+    qmv_status s = check_wk(W_f16, QMV_F16, N, K);
+    if (s != QMV_OK) return s;
+    if (!codes || !lut || !oscale || (nout > 0 && (!ocol || !oval))) return QMV_E_NULL;
+    if (K > 4096 || max_iter < 1 || max_iter > 1000 || nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;
+    if (N > INT32_MAX) return QMV_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(lut, 2) || !aligned(ocol, 2) || !aligned(oscale, 2)) return QMV_E_ALIGN;
+    return launch_status(
+        qmv::launch_pack_km4o(W_f16, N, K, nout, max_iter, codes, lut, ocol, oval, oscale, as_stream(stream)));
+}
+
+qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
+                        const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt, int B,
+                        float *y, void *stream) {
+    qmv_status s = check_mv(codes, lut, 2, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    if (!oscale || (nout > 0 && (!ocol || !oval))) return QMV_E_NULL;
+    if (nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;   // columns fit uint16: K <= 65536
+    if (!aligned(ocol, 2) || !aligned(oscale, 2)) return QMV_E_ALIGN;
+    return launch_status(
+        qmv::launch_matvec_km4o(codes, lut, ocol, oval, oscale, N, K, nout, x, xdt, B, y, as_stream(stream)));
+}
+
 qmv_status qpack_int8km(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
                         void *stream) {
     if (!W_f16 || !codes || !lut) return QMV_E_NULL;

@@ -46,14 +46,28 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
     return k;
 }
 
+// int8 outliers added to 4-bit k-means rows ("Kernel campaign - session
+// handoff", NEXT per lever, Stream D): per row, n columns (increasing), int8
+// values and one fp16 scale; the row's weight is the table value plus the
+// outlier, so y gains scale * q * x[col] per outlier.
+struct OutlierArgs {
+    const uint16_t *col = nullptr;   // [N][n]
+    const int8_t *val = nullptr;     // [N][n]
+    const uint16_t *scale = nullptr; // [N]
+    int n = 0;
+};
+
 // ARGMAX: instead of storing y, each wave keeps the largest key per batch row
 // over its rows and writes it to part[wave][b] (the fused lm_head + argmax);
 // waves past the last row write 0.
-template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK, bool ARGMAX = false>
+// OUTL: add the int8 outliers of each row (4-bit k-means rows only).
+template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK, bool ARGMAX = false,
+          bool OUTL = false>
 __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict__ codes,
                                                       const void *__restrict__ plane, int64_t N, int K,
                                                       const _Float16 *__restrict__ x, int B,
-                                                      float *__restrict__ y, uint64_t *__restrict__ part = nullptr) {
+                                                      float *__restrict__ y, uint64_t *__restrict__ part,
+                                                      OutlierArgs ol) {
     constexpr int RPW = kWave / LPR;            // rows per row group
     constexpr int XW = ChunkTraits<FMT>::kXWords;
     constexpr int ROWS_IT = R * RPW;            // rows per iteration
@@ -218,6 +232,25 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 acc[g * BT + b] = a;
             }
         }
+        if constexpr (OUTL) {
+            // lane `sub` of a row takes its outliers sub, sub + LPR, ...
+            const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);
+#pragma unroll
+            for (int g = 0; g < R; g++) {
+                int rr = g * RPW + rsub;
+                rr = rr <= last ? rr : last;
+                const int64_t row = row0 + rr;
+                const float so = f16_bits_to_f32(ol.scale[row]);
+                for (int o = sub; o < ol.n; o += LPR) {
+                    const float t = (float)ol.val[row * ol.n + o] * so;   // exact: 8 x 11 significant bits
+                    const int col = ol.col[row * ol.n + o];
+#pragma unroll
+                    for (int b = 0; b < BT; b++)
+                        if (BT == 1 || b < B)
+                            acc[g * BT + b] = __builtin_fmaf(t, (float)x[(size_t)b * K + col], acc[g * BT + b]);
+                }
+            }
+        }
         if constexpr ((FMT == KM4 || KM8) && ITERS > 1) {
             // the next iteration rewrites the tables: keep this iteration's reads above it
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -345,10 +378,11 @@ __device__ __forceinline__ void decode_chunk_f32(const uint8_t *__restrict__ cod
 template <typename XT>
 __device__ __forceinline__ float load_x(const XT *p) { return (float)*p; }
 
-template <int FMT, typename XT>
+template <int FMT, typename XT, bool OUTL = false>
 __global__ __launch_bounds__(256) void mv_generic(const uint8_t *__restrict__ codes,
                                                   const void *__restrict__ plane, int64_t N, int K,
-                                                  const XT *__restrict__ x, int B, float *__restrict__ y) {
+                                                  const XT *__restrict__ x, int B, float *__restrict__ y,
+                                                  OutlierArgs ol) {
     constexpr int E = ChunkTraits<FMT>::kElems;
     const int lane = threadIdx.x & 63;
     const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -367,6 +401,16 @@ __global__ __launch_bounds__(256) void mv_generic(const uint8_t *__restrict__ co
 #pragma unroll
                     for (int i = 0; i < E; i++) acc[b] = __builtin_fmaf(w[i], load_x(xp + i), acc[b]);
                 }
+            }
+        }
+        if constexpr (OUTL) {
+            const float so = f16_bits_to_f32(ol.scale[row]);
+            for (int o = lane; o < ol.n; o += kWave) {
+                const float t = (float)ol.val[row * ol.n + o] * so;
+                const int col = ol.col[row * ol.n + o];
+#pragma unroll
+                for (int b = 0; b < 8; b++)
+                    if (b < B) acc[b] = __builtin_fmaf(t, load_x(x + (size_t)b * K + col), acc[b]);
             }
         }
 #pragma unroll
@@ -433,22 +477,23 @@ template <int FMT, int BT, bool ARGMAX> struct ShapeFor : LaunchShape<FMT, BT> {
     static constexpr int ITERS = ARGMAX ? 4 * LaunchShape<FMT, BT>::ITERS : LaunchShape<FMT, BT>::ITERS;
 };
 
-template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false>
+template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
 static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr) {
+                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr,
+                              OutlierArgs ol = OutlierArgs()) {
     using S = ShapeFor<FMT, BT, ARGMAX>;
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
     if (nparts) *nparts = grid * S::WAVES;
     const int cpr = (FMT == INT8 || FMT == INT8KM) ? K / 16 : K / 32;
     if (cpr == LPR * CPL)
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, ARGMAX>), dim3((unsigned)grid),
-                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
-                           part);
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, ARGMAX, OUTL>),
+                           dim3((unsigned)grid), dim3(64 * S::WAVES), 0, st, codes, plane, N, K,
+                           reinterpret_cast<const _Float16 *>(x), B, y, part, ol);
     else
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false, ARGMAX>), dim3((unsigned)grid),
-                           dim3(64 * S::WAVES), 0, st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
-                           part);
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false, ARGMAX, OUTL>),
+                           dim3((unsigned)grid), dim3(64 * S::WAVES), 0, st, codes, plane, N, K,
+                           reinterpret_cast<const _Float16 *>(x), B, y, part, ol);
     return hipGetLastError();
 }
 
@@ -460,19 +505,19 @@ constexpr bool dot2_takes(int B) {
     return B <= 2 || (B <= 4 && CPL * 4 * XW <= 128) || (B <= 8 && CPL * 8 * XW <= 128);
 }
 
-template <int FMT, int LPR, int CPL, bool ARGMAX = false>
+template <int FMT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
 static hipError_t dispatch_b(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
                              float *y, hipStream_t st, bool *handled, uint64_t *part = nullptr,
-                             int64_t *nparts = nullptr) {
+                             int64_t *nparts = nullptr, OutlierArgs ol = OutlierArgs()) {
     *handled = true;
     constexpr int XW = ChunkTraits<FMT>::kXWords;
-    if (B == 1) return launch_fast<FMT, 1, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
-    if (B == 2) return launch_fast<FMT, 2, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
+    if (B == 1) return launch_fast<FMT, 1, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+    if (B == 2) return launch_fast<FMT, 2, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
     if constexpr (CPL * 4 * XW <= 128) {
-        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
+        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
     }
     if constexpr (CPL * 8 * XW <= 128) {
-        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL, ARGMAX>(codes, plane, N, K, x, B, y, st, part, nparts);
+        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
     }
     *handled = false;
     return hipSuccess;
@@ -499,10 +544,10 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
     int grid = grid_for_waves(N);
     if (xdt == QMV_F16)
         hipLaunchKernelGGL((mv_generic<FMT, _Float16>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
-                           reinterpret_cast<const _Float16 *>(x), B, y);
+                           reinterpret_cast<const _Float16 *>(x), B, y, OutlierArgs());
     else
         hipLaunchKernelGGL((mv_generic<FMT, float>), dim3(grid), dim3(256), 0, st, codes, plane, N, K,
-                           reinterpret_cast<const float *>(x), B, y);
+                           reinterpret_cast<const float *>(x), B, y, OutlierArgs());
     return hipGetLastError();
 }
 
@@ -590,6 +635,35 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
     case INT8: return matvec_fmt<INT8>(c, plane, N, (int)K, x, xdt, B, y, st);
     default: return matvec_fmt<KM4>(c, plane, N, (int)K, x, xdt, B, y, st);
     }
+}
+
+hipError_t launch_matvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
+                              const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt,
+                              int B, float *y, hipStream_t st) {
+    OutlierArgs ol;
+    ol.col = ocol;
+    ol.val = oval;
+    ol.scale = oscale;
+    ol.n = nout;
+    const int k = (int)K;
+    const int cpr = k / 32;
+    bool handled = false;
+    hipError_t err = hipSuccess;
+    if (xdt == QMV_F16) {
+        if (cpr <= 16) err = dispatch_b<KM4, 16, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
+        else if (cpr <= 32) err = dispatch_b<KM4, 32, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
+        else if (cpr <= 64) err = dispatch_b<KM4, 64, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
+        else if (cpr <= 128) err = dispatch_b<KM4, 64, 2, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
+        if (handled) return err;
+    }
+    const int grid = grid_for_waves(N);
+    if (xdt == QMV_F16)
+        hipLaunchKernelGGL((mv_generic<KM4, _Float16, true>), dim3(grid), dim3(256), 0, st, codes, lut, N, k,
+                           reinterpret_cast<const _Float16 *>(x), B, y, ol);
+    else
+        hipLaunchKernelGGL((mv_generic<KM4, float, true>), dim3(grid), dim3(256), 0, st, codes, lut, N, k,
+                           reinterpret_cast<const float *>(x), B, y, ol);
+    return hipGetLastError();
 }
 
 hipError_t launch_dequant(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, float *out,

@@ -235,9 +235,12 @@ __device__ __forceinline__ uint16_t unsort_key(uint16_t k) {
 
 constexpr int kKmThreads = 256;
 
+// With outliers (nout > 0, columns ocol[row][.]) the row is palettized with
+// those entries taken as +0; they are stored apart (pack_outliers_kernel).
 __global__ __launch_bounds__(kKmThreads) void pack_km4_kernel(const uint16_t *__restrict__ W, int64_t N, int K,
                                                               int P, int max_iter, uint8_t *__restrict__ codes,
-                                                              uint16_t *__restrict__ lut) {
+                                                              uint16_t *__restrict__ lut,
+                                                              const uint16_t *__restrict__ ocol, int nout) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint16_t *keys = reinterpret_cast<uint16_t *>(smem);                        // P keys
     int64_t *ps = reinterpret_cast<int64_t *>(smem + ((2 * P + 15) & ~15));     // K + 1 prefix sums
@@ -245,12 +248,22 @@ __global__ __launch_bounds__(kKmThreads) void pack_km4_kernel(const uint16_t *__
     __shared__ int tcnt[kKmThreads];
     __shared__ int64_t cent[16];
     __shared__ int ndistinct;
+    __shared__ uint32_t omask[128];   // outlier columns (K <= 4096)
 
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
     const uint16_t *wr = W + row * (int64_t)K;
 
     for (int i = tid; i < P; i += kKmThreads) keys[i] = i < K ? sort_key(wr[i]) : (uint16_t)0xFFFFu;
+    if (nout > 0) {
+        for (int i = tid; i < 128; i += kKmThreads) omask[i] = 0;
+        __syncthreads();
+        for (int o = tid; o < nout; o += kKmThreads) {
+            const int col = ocol[row * nout + o];
+            keys[col] = sort_key(0);
+            atomicOr(&omask[col >> 5], 1u << (col & 31));
+        }
+    }
     __syncthreads();
     // bitonic sort, ascending
     for (int k = 2; k <= P; k <<= 1) {
@@ -359,6 +372,10 @@ __global__ __launch_bounds__(kKmThreads) void pack_km4_kernel(const uint16_t *__
 #pragma unroll
         for (int e = 0; e < 8; e++) {
             uint32_t h = (d[e / 2] >> (16 * (e & 1))) & 0xFFFFu;
+            if (nout > 0) {
+                const int col = 8 * g + e;
+                if ((omask[col >> 5] >> (col & 31)) & 1u) h = 0;
+            }
             int64_t x2 = 2 * units_of_f16(h);
             uint32_t a = 0;
 #pragma unroll
@@ -368,6 +385,76 @@ __global__ __launch_bounds__(kKmThreads) void pack_km4_kernel(const uint16_t *__
         crow[g] = v;
     }
     if (tid < 16) lut[row * 16 + tid] = f16_of_units(cent[tid]);
+}
+
+// ---------------------------------------------------------------------------
+// Outliers of a 4-bit k-means row ("Kernel campaign - session handoff", NEXT
+// per lever, Stream D: int4 plus int8 outliers): the nout entries of largest
+// magnitude (ties to the lower column), listed by increasing column, as int8
+// with one fp16 scale per row (s = fp16(max |w| / 127), q = rint(w / s)).
+// One workgroup per row: magnitude/column keys sorted in LDS (descending),
+// the chosen columns sorted again (ascending).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kKmThreads) void pack_outliers_kernel(const uint16_t *__restrict__ W, int K, int P,
+                                                                   int nout, uint16_t *__restrict__ ocol,
+                                                                   int8_t *__restrict__ oval,
+                                                                   uint16_t *__restrict__ oscale) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint32_t *keys = reinterpret_cast<uint32_t *>(smem);   // P keys (P a power of two >= K)
+    __shared__ uint32_t cols[256];
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const uint16_t *wr = W + row * (int64_t)K;
+    // larger magnitude first; equal magnitudes: the lower column first
+    for (int i = tid; i < P; i += kKmThreads)
+        keys[i] = i < K ? (((uint32_t)wr[i] & 0x7FFFu) << 16) | (0xFFFFu - (uint32_t)i) : 0u;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int p = tid; p < P / 2; p += kKmThreads) {
+                const int i = 2 * p - (p & (j - 1));
+                const int ixj = i + j;
+                const uint32_t a = keys[i], b = keys[ixj];
+                if ((a < b) == ((i & k) == 0)) {
+                    keys[i] = b;
+                    keys[ixj] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // the chosen columns, ascending (256 slots, unused ones sort last)
+    cols[tid] = tid < nout ? 0xFFFFu - (keys[tid] & 0xFFFFu) : 0xFFFFFFFFu;
+    __syncthreads();
+    for (int k = 2; k <= 256; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const int ixj = tid ^ j;
+            uint32_t a = 0, b = 0;
+            const bool act = ixj > tid;
+            if (act) {
+                a = cols[tid];
+                b = cols[ixj];
+            }
+            __syncthreads();
+            if (act && ((a > b) == ((tid & k) == 0))) {
+                cols[tid] = b;
+                cols[ixj] = a;
+            }
+            __syncthreads();
+        }
+    }
+    const float amax = f16_bits_to_f32((uint16_t)(keys[0] >> 16));
+    const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+    const float sc = f16_bits_to_f32(s16);
+    if (tid == 0) oscale[row] = s16;
+    if (tid < nout) {
+        const int col = (int)cols[tid];
+        const float w = f16_bits_to_f32(wr[col]);
+        float q = 0.f;
+        if (sc != 0.f) q = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(__fdiv_rn(w, sc)), -127.f), 127.f);
+        ocol[row * nout + tid] = (uint16_t)col;
+        oval[row * nout + tid] = (int8_t)q;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -669,7 +756,7 @@ hipError_t launch_pack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, u
 }
 
 hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
-                           hipStream_t st) {
+                           hipStream_t st, const uint16_t *ocol, int nout) {
     int P = 32;
     while (P < K) P <<= 1;
     size_t shmem = (size_t)((2 * P + 15) & ~15) + sizeof(int64_t) * (size_t)(K + 1);
@@ -678,11 +765,38 @@ hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter
     for (int64_t r0 = 0; r0 < N; r0 += chunk) {
         int64_t rows = N - r0 < chunk ? N - r0 : chunk;
         hipLaunchKernelGGL(pack_km4_kernel, dim3((unsigned)rows), dim3(kKmThreads), shmem, st, W + r0 * K, rows,
-                           (int)K, P, max_iter, codes + r0 * (K / 2), lut + r0 * 16);
+                           (int)K, P, max_iter, codes + r0 * (K / 2), lut + r0 * 16,
+                           ocol ? ocol + r0 * nout : nullptr, nout);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void zero_u16_kernel(uint16_t *__restrict__ p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_pack_km4o(const uint16_t *W, int64_t N, int64_t K, int nout, int max_iter, uint8_t *codes,
+                            uint16_t *lut, uint16_t *ocol, int8_t *oval, uint16_t *oscale, hipStream_t st) {
+    if (nout > 0) {
+        int P = 32;
+        while (P < K) P <<= 1;
+        const int64_t chunk = 1 << 30;
+        for (int64_t r0 = 0; r0 < N; r0 += chunk) {
+            int64_t rows = N - r0 < chunk ? N - r0 : chunk;
+            hipLaunchKernelGGL(pack_outliers_kernel, dim3((unsigned)rows), dim3(kKmThreads), sizeof(uint32_t) * P, st,
+                               W + r0 * K, (int)K, P, nout, ocol + r0 * nout, oval + r0 * nout, oscale + r0);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    } else {
+        hipLaunchKernelGGL(zero_u16_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, oscale, N);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_pack_km4(W, N, K, max_iter, codes, lut, st, nout > 0 ? ocol : nullptr, nout);
 }
 
 hipError_t launch_pack_int8km(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,

@@ -40,7 +40,12 @@ hipError_t launch_pack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, u
 hipError_t launch_pack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t *codes, uint32_t *plane,
                                hipStream_t st);
 hipError_t launch_pack_km4(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
-                           hipStream_t st);
+                           hipStream_t st, const uint16_t *ocol = nullptr, int nout = 0);
+hipError_t launch_pack_km4o(const uint16_t *W, int64_t N, int64_t K, int nout, int max_iter, uint8_t *codes,
+                            uint16_t *lut, uint16_t *ocol, int8_t *oval, uint16_t *oscale, hipStream_t st);
+hipError_t launch_matvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
+                              const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt,
+                              int B, float *y, hipStream_t st);
 hipError_t launch_pack_int8km(const uint16_t *W, int64_t N, int64_t K, int max_iter, uint8_t *codes, uint16_t *lut,
                               hipStream_t st);
 

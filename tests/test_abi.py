@@ -75,6 +75,14 @@ def test_pack_validation(L):
     assert L.qmatvec_int8km(FAKE, FAKE, 40, 64, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_int8km(FAKE, half, 64, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
     assert L.qdequant(5, FAKE, FAKE, 40, 64, FAKE, S) == E_SHAPE
+    # km4 + outliers: nout range, K limit for packing, NULL outlier arrays only with nout == 0
+    assert L.qpack_km4o(FAKE, 8, 64, 300, 20, FAKE, FAKE, FAKE, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_km4o(FAKE, 8, 64, 65, 20, FAKE, FAKE, FAKE, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_km4o(FAKE, 8, 8192, 4, 20, FAKE, FAKE, FAKE, FAKE, FAKE, S) == E_SHAPE
+    assert L.qpack_km4o(FAKE, 8, 64, 4, 20, FAKE, FAKE, NUL, FAKE, FAKE, S) == E_NULL
+    assert L.qmatvec_km4o(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 64, -1, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4o(FAKE, FAKE, NUL, NUL, NUL, 8, 64, 0, FAKE, 1, 1, FAKE, S) == E_NULL   # oscale needed
+    assert L.qmatvec_km4o(FAKE, FAKE, ODD, FAKE, FAKE, 8, 64, 2, FAKE, 1, 1, FAKE, S) == E_ALIGN
 
 
 @pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
