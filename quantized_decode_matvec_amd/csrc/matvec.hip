@@ -111,6 +111,10 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     float sc[R][CPL];
     float bi[AFF ? R : 1][AFF ? CPL : 1];   // affine bias per block
     uint32_t lutv[LUT_PER_LANE];
+    // outliers (n >= 1): lane `sub` prefetches outlier min(sub, n - 1) of each row
+    uint32_t ocol_r[OUTL ? R : 1];
+    int32_t oval_r[OUTL ? R : 1];
+    uint32_t osc_r[OUTL ? R : 1];
     auto issue_loads = [&](int64_t row0) {
         const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);   // last valid row offset
         const uint8_t *cbase = codes + row0 * (int64_t)row_bytes;
@@ -154,6 +158,18 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             const uint32_t *lsrc = reinterpret_cast<const uint32_t *>(plane) + (row0 / 32) * 128;
 #pragma unroll
             for (int q = 0; q < LUT_PER_LANE; q++) lutv[q] = lsrc[q * kWave + lane];
+        }
+        if constexpr (OUTL) {
+            const int o = sub < ol.n ? sub : ol.n - 1;
+#pragma unroll
+            for (int g = 0; g < R; g++) {
+                int rr = g * RPW + rsub;
+                rr = rr <= last ? rr : last;
+                const int64_t row = row0 + rr;
+                ocol_r[g] = ol.col[row * ol.n + o];
+                oval_r[g] = ol.val[row * ol.n + o];
+                osc_r[g] = ol.scale[row];
+            }
         }
     };
 
@@ -206,6 +222,18 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+        // outliers: this iteration's x values at the outlier columns, gathered
+        // now so the loads are in flight during the dot products
+        float ot[OUTL ? R : 1];
+        _Float16 ox[OUTL ? R : 1][OUTL ? BT : 1];
+        if constexpr (OUTL) {
+#pragma unroll
+            for (int g = 0; g < R; g++) {
+                ot[g] = sub < ol.n ? (float)oval_r[g] * f16_bits_to_f32((uint16_t)osc_r[g]) : 0.f;   // exact
+#pragma unroll
+                for (int b = 0; b < BT; b++) ox[g][b] = x[(size_t)(b < B ? b : 0) * K + ocol_r[g]];
+            }
+        }
         if (ITERS > 1 && it + 1 < ITERS && row0 + ROWS_IT < N) issue_loads(row0 + ROWS_IT);
 
         float acc[R * BT];
@@ -233,7 +261,12 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             }
         }
         if constexpr (OUTL) {
-            // lane `sub` of a row takes its outliers sub, sub + LPR, ...
+            // lane `sub` of a row takes its outliers sub (prefetched), sub + LPR, ...
+#pragma unroll
+            for (int g = 0; g < R; g++)
+#pragma unroll
+                for (int b = 0; b < BT; b++)
+                    if (BT == 1 || b < B) acc[g * BT + b] = __builtin_fmaf(ot[g], (float)ox[g][b], acc[g * BT + b]);
             const int last = (int)((N - 1 - row0) < ROWS_IT ? (N - 1 - row0) : ROWS_IT);
 #pragma unroll
             for (int g = 0; g < R; g++) {
@@ -241,7 +274,7 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
                 rr = rr <= last ? rr : last;
                 const int64_t row = row0 + rr;
                 const float so = f16_bits_to_f32(ol.scale[row]);
-                for (int o = sub; o < ol.n; o += LPR) {
+                for (int o = sub + LPR; o < ol.n; o += LPR) {
                     const float t = (float)ol.val[row * ol.n + o] * so;   // exact: 8 x 11 significant bits
                     const int col = ol.col[row * ol.n + o];
 #pragma unroll
@@ -640,6 +673,7 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
 hipError_t launch_matvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
                               const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt,
                               int B, float *y, hipStream_t st) {
+    if (nout == 0) return launch_matvec(KM4, codes, lut, N, K, x, xdt, B, y, st);
     OutlierArgs ol;
     ol.col = ocol;
     ol.val = oval;
