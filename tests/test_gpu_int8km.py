@@ -148,3 +148,16 @@ def test_lm_head_shape_sampled_groups():
     hl = host(lut)
     want = oracle.matvec("int8km", host(codes[rows]), np.concatenate([hl[g:g + 1] for g in groups]), c.x)
     assert rel_err(y[:, rows], want) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["km4", "int8km"])
+def test_pack_heavily_repeated_value_bit_exact(fmt):
+    """Half of every row is one value: repeated starting entries, empty
+    clusters that keep their value (both k-means packers)."""
+    rng = np.random.default_rng(60)
+    W = (rng.standard_normal((64, 512)) * 0.3).astype(np.float16)
+    W[:, ::2] = np.float16(0.5)
+    want = oracle.pack(fmt, W)
+    got = qmv.qpack(fmt, dev(W))
+    assert np.array_equal(want[1], host(got[1]))
+    assert np.array_equal(want[0], host(got[0]))

@@ -851,3 +851,21 @@ def test_km4o_matvec_equals_numpy_gemm_and_outliers_help():
     e4 = np.abs(oracle.dequant("km4", c4, l4) - W.astype(np.float64)).mean()
     eo = np.abs(D - W.astype(np.float64)).mean()
     assert eo < 0.75 * e4
+
+
+@pytest.mark.parametrize("fmt", ["km4", "int8km"])
+def test_kmeans_empty_entries_stay_in_place(fmt):
+    """Half the values equal 0.5: the starting order statistics repeat 0.5 many
+    times, the repeated entries above the first get no members (the midpoint
+    rule sends 0.5 to the lowest of them) and must keep their value, so the
+    table stays ascending and (in some row) still holds 0.5 more than once."""
+    rng = np.random.default_rng(60)
+    rows = 32 if fmt == "int8km" else 4
+    W = (rng.standard_normal((rows, 512)) * 0.3).astype(np.float16)
+    W[:, ::2] = np.float16(0.5)
+    codes, lut = oracle.pack(fmt, W)
+    L = lut.view(np.float16).astype(np.float64)
+    assert np.all(np.diff(L, axis=-1) >= 0)
+    assert max(np.sum(L[r] == 0.5) for r in range(L.shape[0])) >= 2
+    if fmt == "int8km":
+        _int8km_check_nearest(W, codes, lut)
