@@ -65,8 +65,9 @@ __device__ __forceinline__ h8 h8_of(uint32_t a, uint32_t b, uint32_t c, uint32_t
 //  INT8: two dwords (codes 4q..4q+3 and 16+4q..16+4q+3 of the block)
 template <int FMT>
 __device__ __forceinline__ h8 decode8(uint32_t v, uint32_t v2) {
-    if constexpr (FMT == INT4) {
-        const h2 b0 = as_h2(0x64086408u);   // (1032, 1032)
+    if constexpr (FMT == INT4 || FMT == INT4AFF) {
+        // int4: u - 8; affine int4: u (its bias is added per block)
+        const h2 b0 = as_h2(FMT == INT4 ? 0x64086408u : 0x64006400u);   // (1032, 1032) or (1024, 1024)
         const uint32_t magic = 0x64006400u;
         h2 a0 = as_h2(and_or(v, 0x000F000Fu, magic)) - b0;
         h2 a1 = as_h2(and_or(v >> 4, 0x000F000Fu, magic)) - b0;
@@ -137,7 +138,7 @@ __device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, 
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
         uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * g);
-        if constexpr (FMT == INT4) {
+        if constexpr (FMT == INT4 || FMT == INT4AFF) {
             // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
             return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
                               __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
@@ -154,10 +155,17 @@ __device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, 
 constexpr int kCodeRowLds = 256 + 16;
 constexpr bool kLdsCodes = true;   // staged loads measured faster on MI355X
 constexpr int kZeroLds = 256;
-template <int FMT> constexpr int scale_pad() { return (FMT == INT4) ? 8 : (FMT == KM4 ? 0 : 4); }
-// per-row bytes of the scale plane (KM4: the row's 16-entry fp16 table)
+template <int FMT> constexpr int scale_pad() {
+    return (FMT == INT4) ? 8 : (FMT == INT4AFF ? 16 : (FMT == KM4 ? 0 : 4));
+}
+// per-row bytes of the scale plane (KM4: the row's 16-entry fp16 table;
+// INT4AFF: a 32-bit scale + bias word per block)
 template <int FMT> __host__ __device__ constexpr int scale_row_bytes(int K) {
-    return (FMT == KM4) ? 32 : ((FMT == FP4) ? K / 32 : K / 16);   // one e8m0 byte or one fp16 per block
+    return (FMT == KM4) ? 32 : ((FMT == FP4) ? K / 32 : (FMT == INT4AFF ? K / 8 : K / 16));
+}
+// affine int4: per-workgroup LDS table of the x block sums, [K/32][16 batch] fp32
+template <int FMT> __host__ __device__ constexpr int xsum_lds_bytes(int K) {
+    return (FMT == INT4AFF) ? (K / 32) * 16 * 4 : 0;
 }
 template <int FMT, bool LDS_CODES> __host__ __device__ constexpr int wave_lds_bytes(int K) {
     return (LDS_CODES ? 16 * kCodeRowLds : 0) + ((16 * (scale_row_bytes<FMT>(K) + scale_pad<FMT>()) + 15) / 16) * 16;
@@ -196,6 +204,25 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
     }
     uint8_t *const zl = reinterpret_cast<uint8_t *>(xs + B * KP);
     if (threadIdx.x < kZeroLds / 16) reinterpret_cast<uint4 *>(zl)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    float *const xsum_l = reinterpret_cast<float *>(zl + kZeroLds);
+    if constexpr (FMT == INT4AFF) {
+        // the affine bias multiplies the block sum of x: [block][batch], batches >= B zero
+        for (int i = threadIdx.x; i < (K / 32) * 16; i += 64 * kMfmaWaves) {
+            const int blk = i >> 4, b = i & 15;
+            float sum = 0.f;
+            if (b < B) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(x + (size_t)b * K + 32 * blk);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint4 v = p[u];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) sum = dot2(as_h2(w4[e]), as_h2(0x3C003C00u), sum);
+                }
+            }
+            xsum_l[i] = sum;
+        }
+    }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
@@ -208,7 +235,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
     const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
     const int srb = scale_row_bytes<FMT>(K);
     const int srs = srb + scale_pad<FMT>();            // padded scale row in LDS
-    uint8_t *wl = zl + kZeroLds + wave * wave_lds_bytes<FMT, LDS_CODES>(K);
+    uint8_t *wl = zl + kZeroLds + xsum_lds_bytes<FMT>(K) + wave * wave_lds_bytes<FMT, LDS_CODES>(K);
     uint8_t *cl = wl;                                       // codes [16][kCodeRowLds]
     uint8_t *sl = wl + (LDS_CODES ? 16 * kCodeRowLds : 0);  // scales [16][srs]
     // A operand of j-step j: xa + xstride * j, then 64 bytes per block. Batch
@@ -316,7 +343,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                     uint32_t w[4] = {c4.x, c4.y, c4.z, c4.w};
                     transpose4(w);
                     uint32_t s0w = 0, s1w = 0;
-                    if constexpr (FMT == INT4) {
+                    uint4 s4 = make_uint4(0u, 0u, 0u, 0u);
+                    if constexpr (FMT == INT4AFF) {
+                        s4 = *reinterpret_cast<const uint4 *>(sl + srow * srs + 16 * j);
+                    } else if constexpr (FMT == INT4) {
                         const uint2 s2 = *reinterpret_cast<const uint2 *>(sl + srow * srs + 8 * j);
                         s0w = s2.x;
                         s1w = s2.y;
@@ -352,7 +382,14 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
 #pragma unroll
                     for (int m = 0; m < MPJ; m++) {
                         float scl;
-                        if constexpr (FMT == INT4) {
+                        if constexpr (FMT == INT4AFF) {
+                            const uint32_t sb = (m == 0) ? s4.x : (m == 1) ? s4.y : (m == 2) ? s4.z : s4.w;
+                            scl = f16_bits_to_f32((uint16_t)(sb & 0xFFFFu));
+                            const float bia = f16_bits_to_f32((uint16_t)(sb >> 16));
+                            const f4 xsm = *reinterpret_cast<const f4 *>(xsum_l + (4 * j + m) * 16 + 4 * q);
+#pragma unroll
+                            for (int v = 0; v < 4; v++) acc[v] = __builtin_fmaf(xsm[v], bia, acc[v]);
+                        } else if constexpr (FMT == INT4) {
                             const uint32_t pr = (m < 2) ? s0w : s1w;
                             scl = f16_bits_to_f32((uint16_t)((m & 1) ? (pr >> 16) : (pr & 0xFFFFu)));
                         } else if constexpr (FMT == FP4) {
@@ -390,25 +427,28 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
 
 template <int FMT>
 static size_t mfma_lds_bytes(int64_t K, int B) {
-    return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
+    return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)xsum_lds_bytes<FMT>((int)K) +
+           (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
 }
 
-// The batched matrix-core path takes int4, fp4, int8 and km4 (not affine
-// int4), fp16 x, 3 <= B <= 8 (km4: 5 <= B; below that the dot2 path is as
-// fast), whole load steps (K % 512 == 0, int8
+// The batched matrix-core path takes int4, affine int4 (K <= 2048), fp4, int8
+// and km4 (not int8 k-means), fp16 x, 3 <= B <= 8 (km4: 5 <= B; below that
+// the dot2 path is as fast), whole load steps (K % 512 == 0, int8
 // K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned scale plane, and
-// staging that fits in 64 KiB of LDS.
+// staging that fits in 64 KiB of LDS (affine int4: 80 KiB, two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
     // km4 table lookups from 16 rows at once meet LDS bank conflicts; below
     // B = 5 its dot2 path (one row's table per instruction) is faster
-    if (fmt == INT4AFF || fmt == INT8KM || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
+    if (fmt == INT8KM || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
+    if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
+                 : (fmt == INT4AFF) ? mfma_lds_bytes<INT4AFF>(K, B)
                  : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
                  : (fmt == INT8) ? mfma_lds_bytes<INT8>(K, B) : mfma_lds_bytes<KM4>(K, B);
-    return lds <= 64 * 1024;
+    return lds <= (fmt == INT4AFF ? 80 : 64) * 1024;
 }
 
 template <int FMT, int SP>
@@ -417,8 +457,15 @@ static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_
     constexpr int RG = 8, D = 2;
     const int64_t rows_wg = (int64_t)kMfmaWaves * RG * 16;
     const int64_t grid = (N + rows_wg - 1) / rows_wg;
-    hipLaunchKernelGGL((mv_mfma<FMT, RG, SP, D, kLdsCodes>), dim3((unsigned)grid), dim3(64 * kMfmaWaves),
-                       mfma_lds_bytes<FMT>(K, B), st, codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+    const size_t lds = mfma_lds_bytes<FMT>(K, B);
+    if (lds > 64 * 1024) {
+        // two workgroups still fit a CU's 160 KiB; allow the larger dynamic allocation
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mv_mfma<FMT, RG, SP, D, kLdsCodes>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((mv_mfma<FMT, RG, SP, D, kLdsCodes>), dim3((unsigned)grid), dim3(64 * kMfmaWaves), lds, st,
+                       codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
     return hipGetLastError();
 }
 
@@ -437,6 +484,7 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
     if (!*handled) return hipSuccess;
     switch (fmt) {
     case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st);
+    case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st);
     case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st);
     case INT8: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
     default: return launch_mfma_fmt<KM4>(codes, plane, N, (int)K, x, B, y, st);

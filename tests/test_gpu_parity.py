@@ -135,19 +135,20 @@ def test_batched_matvec_parity(fmt, N, K, Bs):
         assert rel_err(y, want) <= RTOL
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8"])
+@pytest.mark.parametrize("fmt", ["int4", "int8", "int4aff"])
 def test_batched_matvec_with_unaligned_scale_plane(fmt):
-    """A scale plane that is only 2-byte aligned is valid input; the batched
-    path, which reads scales as whole words, leaves it to the dot2 path."""
+    """A scale plane aligned to its element size only (2 bytes; 4 for the
+    affine words) is valid input; the batched path, which reads a group's
+    scales as 16-byte pieces, leaves it to the dot2 path."""
     import torch
     N, K, B = 96, 1024, 8
     W, x = _case(fmt, N, K, B=B, seed=3)
     codes, plane = oracle.pack(fmt, W)
     want = oracle.matvec(fmt, codes, plane, x)
-    flat = np.concatenate([np.zeros(1, np.uint16), plane.reshape(-1)])
+    flat = np.concatenate([np.zeros(1, plane.dtype), plane.reshape(-1)])
     dflat = dev(flat)
     dp = dflat[1:].view(plane.shape)
-    assert dp.data_ptr() % 4 == 2
+    assert dp.data_ptr() % 16 != 0
     y = host(qmv.qmatvec(fmt, dev(codes), dp, dev(x)))
     assert rel_err(y, want) <= RTOL
 
