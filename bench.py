@@ -75,14 +75,17 @@ def calibrate():
     print(json.dumps({"calibration_bytes_per_copy": n, "copies": 5, "stream_reads": 5}))
 
 
-def gpu_warm(seconds=0.5):
-    """Keep the GPU busy for a moment so clocks are up before anything is timed."""
+def gpu_warm(fn, seconds=0.2):
+    """Run the timed operation itself, untimed, for a moment so the clocks have
+    left their idle state before the warm-up steps (a heavier load here, such
+    as GEMMs, leaves the chip power-limited for what follows)."""
     import torch
-    a = torch.randn(4096, 4096, device="cuda", dtype=torch.float16)
     t0 = time.perf_counter()
+    i = 0
     while time.perf_counter() - t0 < seconds:
-        for _ in range(20):
-            a = torch.tanh(a @ a * 1e-3)
+        for _ in range(50):
+            fn(i)
+            i += 1
         torch.cuda.synchronize()
 
 
@@ -207,7 +210,7 @@ def main():
         cc, ll = copies[i % len(copies)]
         qmv.qmatvec_km4(cc, ll, x1, y=y[:1])
 
-    gpu_warm()
+    gpu_warm(step)
     ms = timed(step, args.steps, args.warmup)
     nbytes = algo_bytes("km4", N_ROWS, K_DIM)
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -498,7 +498,7 @@ static int grid_for_waves(int64_t waves_needed) {
 // its compile-time table offsets; more batch rows need more rows per wave to
 // amortize the x slices held in registers.
 template <int FMT, int BT> struct LaunchShape {
-    static constexpr int R = (BT == 1) ? ((FMT == INT4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
+    static constexpr int R = (BT == 1) ? ((FMT == INT4 || FMT == KM4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
     static constexpr int ITERS = (FMT == KM4 || FMT == INT8KM) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
                                               : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
     static constexpr int WAVES = (FMT == KM4 || FMT == INT8KM) ? 1 : 4;
