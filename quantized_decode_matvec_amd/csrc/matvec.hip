@@ -494,11 +494,16 @@ static int grid_for_waves(int64_t waves_needed) {
 
 // Launch shape per format and batch width (rows per iteration R, iterations
 // per wave ITERS, waves per workgroup WAVES), chosen by measurement on MI355X
-// at the lm_head shape (248320 x 2048). km4 needs one wave per workgroup for
-// its compile-time table offsets; more batch rows need more rows per wave to
-// amortize the x slices held in registers.
-template <int FMT, int BT> struct LaunchShape {
-    static constexpr int R = (BT == 1) ? ((FMT == INT4 || FMT == KM4) ? 8 : 4) : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
+// at the lm_head shape (248320 x 2048) under sustained load. km4 needs one
+// wave per workgroup for its compile-time table offsets; more batch rows need
+// more rows per wave to amortize the x slices held in registers. TALL (batch
+// 1, at least kTallRows rows): 8 rows per wave for the table formats and
+// affine int4, which halves the x slice loads per row; shorter matrices keep
+// 4 so that enough waves fill the chip.
+constexpr int64_t kTallRows = 32768;
+template <int FMT, int BT, bool TALL = false> struct LaunchShape {
+    static constexpr int R = (BT == 1) ? ((FMT == INT4 || (TALL && FMT != FP4 && FMT != INT8)) ? 8 : 4)
+                                       : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
     static constexpr int ITERS = (FMT == KM4 || FMT == INT8KM) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
                                               : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
     static constexpr int WAVES = (FMT == KM4 || FMT == INT8KM) ? 1 : 4;
@@ -506,15 +511,14 @@ template <int FMT, int BT> struct LaunchShape {
 
 // The argmax epilogue writes one key per wave: waves cover 4x more rows (at
 // least 16) so the reduction that follows reads few keys.
-template <int FMT, int BT, bool ARGMAX> struct ShapeFor : LaunchShape<FMT, BT> {
-    static constexpr int ITERS = ARGMAX ? 4 * LaunchShape<FMT, BT>::ITERS : LaunchShape<FMT, BT>::ITERS;
+template <int FMT, int BT, bool ARGMAX, bool TALL = false> struct ShapeFor : LaunchShape<FMT, BT, TALL> {
+    static constexpr int ITERS = ARGMAX ? 4 * LaunchShape<FMT, BT, TALL>::ITERS : LaunchShape<FMT, BT, TALL>::ITERS;
 };
 
-template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
-static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr,
-                              OutlierArgs ol = OutlierArgs()) {
-    using S = ShapeFor<FMT, BT, ARGMAX>;
+template <int FMT, int BT, int LPR, int CPL, bool ARGMAX, bool OUTL, bool TALL>
+static hipError_t launch_shape(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                               float *y, hipStream_t st, uint64_t *part, int64_t *nparts, OutlierArgs ol) {
+    using S = ShapeFor<FMT, BT, ARGMAX, TALL>;
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
     if (nparts) *nparts = grid * S::WAVES;
@@ -528,6 +532,18 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
                            dim3((unsigned)grid), dim3(64 * S::WAVES), 0, st, codes, plane, N, K,
                            reinterpret_cast<const _Float16 *>(x), B, y, part, ol);
     return hipGetLastError();
+}
+
+// the argmax epilogue keeps its shorter shape: more waves, shorter key lists per wave
+template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
+static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr,
+                              OutlierArgs ol = OutlierArgs()) {
+    if constexpr (BT == 1 && !ARGMAX) {
+        if (N >= kTallRows)
+            return launch_shape<FMT, BT, LPR, CPL, ARGMAX, OUTL, true>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+    }
+    return launch_shape<FMT, BT, LPR, CPL, ARGMAX, OUTL, false>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
 }
 
 // Register budget for the x slices held per lane (CPL * BT * XW words): the

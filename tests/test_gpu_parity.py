@@ -205,3 +205,26 @@ def test_stream_read_checksum():
     a = rng.integers(0, 2 ** 32, size=(1 << 20) + 4, dtype=np.uint32)
     sink = host(qmv.qmv_stream_read(dev(a.view(np.int32))))
     assert np.bitwise_xor.reduce(sink.view(np.uint32)) == np.bitwise_xor.reduce(a)
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff", "km4o"])
+def test_tall_batch1_shape_on_sampled_rows(fmt):
+    """At batch 1 a matrix of at least 32768 rows takes the tall launch shape
+    (8 rows per wave for most formats). The GPU packs and multiplies the whole
+    ragged matrix; the oracle packs the sampled rows (rows are packed
+    independently) and computes their outputs."""
+    from tests.gpu_helpers import sample_rows
+    N, K = 32768 + 37, 1024
+    c = wl.small_dense("km4", N, K, batch=1, seed=21, outlier_frac=0.01)
+    W, x = c.W, c.x
+    rows = sample_rows(N, n=96, seed=4)
+    print("tall", fmt, N, K, flush=True)
+    if fmt == "km4o":
+        y = host(qmv.qmatvec_km4o(*qmv.qpack_km4o(dev(W), 8), dev(x)))
+        want = oracle.matvec_km4o(*oracle.pack_km4o(W[rows], 8), x)
+    else:
+        codes, plane = qmv.qpack(fmt, dev(W))
+        y = host(qmv.qmatvec(fmt, codes, plane, dev(x)))
+        oc, op = oracle.pack(fmt, W[rows])
+        want = oracle.matvec(fmt, oc, op, x)
+    assert rel_err(y[:, rows], want) <= RTOL
