@@ -78,6 +78,18 @@ def grid(path, match=None):
     return out
 
 
+def window(path, match, last):
+    """Durations of the last `last` dispatches of the kernels matching `match`
+    (the timed region of a bench run comes last): mean, min, max in us, and
+    the wall time from the first start to the last end divided by `last`."""
+    rows = [r for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    rows = rows[-last:]
+    d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    wall = (int(rows[-1]["End_Timestamp"]) - int(rows[0]["Start_Timestamp"])) / 1e3 / len(rows)
+    return len(d), sum(d) / len(d), min(d), max(d), wall
+
+
 def traffic(args):
     fetch_name, fetch_kib, nf = _pick(_per_kernel(args.fetch, "FETCH_SIZE"), args.kernel)
     write_name, write_kib, nw = _pick(_per_kernel(args.write, "WRITE_SIZE"), args.kernel)
@@ -118,6 +130,10 @@ def main():
     g = sub.add_parser("grid")
     g.add_argument("csv")
     g.add_argument("--match")
+    w = sub.add_parser("window")
+    w.add_argument("csv")
+    w.add_argument("--match", required=True)
+    w.add_argument("--last", type=int, required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True)
     t.add_argument("--key", required=True)
@@ -134,6 +150,11 @@ def main():
         print("|---|---|---|---|---|")
         for name, calls, avg, mn, mx in stats(a.csv, a.match):
             print("| %s | %d | %.2f | %.2f | %.2f |" % (name[:110], calls, avg / 1e3, mn / 1e3, mx / 1e3))
+    elif a.cmd == "window":
+        n, avg, mn, mx, wall = window(a.csv, a.match, a.last)
+        print("| dispatches | avg us | min us | max us | wall us per dispatch |")
+        print("|---|---|---|---|---|")
+        print("| %d | %.2f | %.2f | %.2f | %.2f |" % (n, avg, mn, mx, wall))
     elif a.cmd == "grid":
         print("| kernel | grid x (threads) | grid y | workgroup | calls | median us | min us |")
         print("|---|---|---|---|---|---|---|")
