@@ -15,8 +15,8 @@
 //     by that lane's own block scale (fp32 FMA) before accumulation; the
 //     decoded values stay exact in fp16 as in the dot2 path. The 16 rows of
 //     one MFMA all take the same 32-k block. km4 has no block scale: its
-//     MFMAs accumulate directly, and its codes are looked up in the 16 rows'
-//     tables in LDS (one SDWA add per code forms the address).
+//     MFMAs accumulate directly, and each lane holds its row's table in
+//     registers as byte planes, looked up with v_perm (no LDS reads).
 //   - Codes reach the MFMA layout through a small per-wave LDS stage (global
 //     loads stay whole cache lines): lane (r, q) takes 16-byte chunk 4j + q
 //     of row r, and a 4 x 4 dword transpose across the four 16-lane rows
@@ -90,40 +90,28 @@ __device__ __forceinline__ h8 decode8(uint32_t v, uint32_t v2) {
     }
 }
 
-// KM4: the 8 codes of one dword looked up in the lane's row table in LDS
-// (tbase: its LDS byte address). Even codes' byte offsets 2c sit in the bytes
-// of (w << 1) & 0x1E1E1E1E, odd codes' in (w >> 3) & 0x1E1E1E1E; one SDWA
-// add per code forms the address. Result order c0 .. c7.
-template <int S>
-__device__ __forceinline__ uint32_t add_byte(uint32_t base, uint32_t w) {
-    uint32_t r;
-    if constexpr (S == 0)
-        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(base), "v"(w));
-    else if constexpr (S == 1)
-        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(base), "v"(w));
-    else if constexpr (S == 2)
-        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(base), "v"(w));
-    else
-        asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(base), "v"(w));
-    return r;
-}
-
-__device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
-    return *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((size_t)addr);
-}
-
-__device__ __forceinline__ h8 decode8_km4(uint32_t w, uint32_t tbase) {
-    const uint32_t e = (w << 1) & 0x1E1E1E1Eu, o = (w >> 3) & 0x1E1E1E1Eu;
-    h2 v0, v1, v2, v3;
-    v0.x = lds_half(add_byte<0>(tbase, e));
-    v0.y = lds_half(add_byte<0>(tbase, o));
-    v1.x = lds_half(add_byte<1>(tbase, e));
-    v1.y = lds_half(add_byte<1>(tbase, o));
-    v2.x = lds_half(add_byte<2>(tbase, e));
-    v2.y = lds_half(add_byte<2>(tbase, o));
-    v3.x = lds_half(add_byte<3>(tbase, e));
-    v3.y = lds_half(add_byte<3>(tbase, o));
-    return h8_of(as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3));
+// KM4 from registers: the lane's row table as byte planes, L[k] = low bytes
+// and H[k] = high bytes of entries 4k .. 4k + 3. One v_perm looks up four
+// codes in an 8-entry byte plane (selector = code & 7); entries 8..15 come
+// from the second pair of planes and a byte-wise select on bit 3 of the code
+// (v_perm's sign-replicating selectors spread that bit over its byte).
+// Result order c0 c2 c1 c3 c4 c6 c5 c7 (x is staged to match). No LDS access:
+// sixteen rows' tables looked up from LDS in one instruction meet bank
+// conflicts, which limited the LDS form to about half this rate.
+__device__ __forceinline__ uint32_t bsel(uint32_t m, uint32_t a, uint32_t b) { return (m & a) | (~m & b); }
+__device__ __forceinline__ h8 decode8_km4_reg(uint32_t w, const uint32_t (&L)[4], const uint32_t (&H)[4]) {
+    const uint32_t se = w & 0x07070707u;            // even codes c0 c2 c4 c6, low 3 bits
+    const uint32_t so = (w >> 4) & 0x07070707u;     // odd codes c1 c3 c5 c7
+    // 0xFF where bit 3 of the code is set: selectors 8..11 replicate bit 15 /
+    // 31 of the second / first operand
+    const uint32_t me = __builtin_amdgcn_perm(w << 12, w << 4, 0x090B080Au);   // bits 3, 11, 19, 27
+    const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);         // bits 7, 15, 23, 31
+    const uint32_t le = bsel(me, __builtin_amdgcn_perm(L[3], L[2], se), __builtin_amdgcn_perm(L[1], L[0], se));
+    const uint32_t he = bsel(me, __builtin_amdgcn_perm(H[3], H[2], se), __builtin_amdgcn_perm(H[1], H[0], se));
+    const uint32_t lo = bsel(mo, __builtin_amdgcn_perm(L[3], L[2], so), __builtin_amdgcn_perm(L[1], L[0], so));
+    const uint32_t ho = bsel(mo, __builtin_amdgcn_perm(H[3], H[2], so), __builtin_amdgcn_perm(H[1], H[0], so));
+    return h8_of(__builtin_amdgcn_perm(he, le, 0x05010400u), __builtin_amdgcn_perm(ho, lo, 0x05010400u),
+                 __builtin_amdgcn_perm(he, le, 0x07030602u), __builtin_amdgcn_perm(ho, lo, 0x07030602u));
 }
 
 // One 8-element x group (16 bytes) in decoder order; group g of a row is
@@ -138,6 +126,11 @@ __device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, 
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     } else {
         uint4 v = *reinterpret_cast<const uint4 *>(xrow + 8 * g);
+        if constexpr (FMT == KM4) {
+            // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x2)(x1 x3)(x4 x6)(x5 x7)
+            return make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                              __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+        }
         if constexpr (FMT == INT4 || FMT == INT4AFF) {
             // (x0 x1)(x2 x3)(x4 x5)(x6 x7) -> (x0 x4)(x1 x5)(x2 x6)(x3 x7)
             return make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
@@ -290,6 +283,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
     f4 kacc[MPJ];
 #pragma unroll
     for (int m = 0; m < MPJ; m++) kacc[m] = f4{0.f, 0.f, 0.f, 0.f};
+    uint32_t kL[4] = {0u, 0u, 0u, 0u}, kH[4] = {0u, 0u, 0u, 0u};   // km4: the lane's row table as byte planes
     for (int s0 = 0; s0 < nsteps; s0 += D) {
 #pragma unroll
         for (int u = 0; u < D; u++) {
@@ -335,6 +329,19 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                 // LDS scale row of this lane's row (see the partial-group note above)
                 const int delta = (int)(grow + 16 <= N ? 0 : grow - (N - 16));
                 const int srow = r + delta < 16 ? r + delta : 15;
+                if constexpr (FMT == KM4) {
+                    if (t == 0) {
+                        // entries 2i, 2i + 1 in dword i; split into low / high byte planes
+                        const uint4 a = *reinterpret_cast<const uint4 *>(sl + srow * srs);
+                        const uint4 b = *reinterpret_cast<const uint4 *>(sl + srow * srs + 16);
+                        const uint32_t tw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                        for (int k = 0; k < 4; k++) {
+                            kL[k] = __builtin_amdgcn_perm(tw[2 * k + 1], tw[2 * k], 0x06040200u);
+                            kH[k] = __builtin_amdgcn_perm(tw[2 * k + 1], tw[2 * k], 0x07050301u);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int jj = 0; jj < 4; jj++) {
                     const int j = 4 * t + jj;   // J % 4 == 0: no partial steps
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                     for (int m = 0; m < MPJ; m++) {
                         ax[m] = *reinterpret_cast<const h8 *>(xa + xstride * (uint32_t)j + 64 * m);
                         if constexpr (FMT == KM4)
-                            bw[m] = decode8_km4(w[m], (uint32_t)(uintptr_t)(sl + srow * srs));
+                            bw[m] = decode8_km4_reg(w[m], kL, kH);
                         else
                             bw[m] = (FMT == INT8) ? decode8<FMT>(w[2 * m], w[2 * m + 1]) : decode8<FMT>(w[m], 0u);
                     }
@@ -432,14 +439,12 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
 }
 
 // The batched matrix-core path takes int4, affine int4 (K <= 2048), fp4, int8
-// and km4 (not int8 k-means), fp16 x, 3 <= B <= 8 (km4: 5 <= B; below that
-// the dot2 path is as fast), whole load steps (K % 512 == 0, int8
-// K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned scale plane, and
-// staging that fits in 64 KiB of LDS (affine int4: 80 KiB, two workgroups per CU).
+// and km4 (not int8 k-means), fp16 x, 3 <= B <= 8, whole load steps
+// (K % 512 == 0, int8 K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned
+// scale plane, and staging that fits in 64 KiB of LDS (affine int4: 80 KiB,
+// two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
-    // km4 table lookups from 16 rows at once meet LDS bank conflicts; below
-    // B = 5 its dot2 path (one row's table per instruction) is faster
-    if (fmt == INT8KM || B < (fmt == KM4 ? 5 : 3) || B > 8 || N < 16) return false;
+    if (fmt == INT8KM || B < 3 || B > 8 || N < 16) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
