@@ -114,12 +114,31 @@ __device__ __forceinline__ h8 decode8_km4_reg(uint32_t w, const uint32_t (&L)[4]
                  __builtin_amdgcn_perm(he, le, 0x07030602u), __builtin_amdgcn_perm(ho, lo, 0x07030602u));
 }
 
+// INT8KM: the 8 byte codes of two dwords (the INT8 element order) looked up
+// in the row group's 256-entry table in LDS at byte address tbase: one SDWA
+// shift and one add per code form the address.
+__device__ __forceinline__ _Float16 lds_half(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) _Float16 *>((size_t)addr);
+}
+__device__ __forceinline__ h8 decode8_km8(uint32_t w0, uint32_t w1, uint32_t tbase) {
+    h2 v0, v1, v2, v3;
+    v0.x = lds_half(tbase + byte_shl1<0>(w0));
+    v0.y = lds_half(tbase + byte_shl1<1>(w0));
+    v1.x = lds_half(tbase + byte_shl1<2>(w0));
+    v1.y = lds_half(tbase + byte_shl1<3>(w0));
+    v2.x = lds_half(tbase + byte_shl1<0>(w1));
+    v2.y = lds_half(tbase + byte_shl1<1>(w1));
+    v3.x = lds_half(tbase + byte_shl1<2>(w1));
+    v3.y = lds_half(tbase + byte_shl1<3>(w1));
+    return h8_of(as_u32(v0), as_u32(v1), as_u32(v2), as_u32(v3));
+}
+
 // One 8-element x group (16 bytes) in decoder order; group g of a row is
 // staged at halfs 8g .. 8g + 7. For INT8, group 4c + q holds elements
 // 32c + 4q .. +3 and 32c + 16 + 4q .. +3.
 template <int FMT>
 __device__ __forceinline__ uint4 stage_group(const _Float16 *__restrict__ xrow, int g) {
-    if constexpr (FMT == INT8) {
+    if constexpr (FMT == INT8 || FMT == INT8KM) {
         const int c = g >> 2, q = g & 3;
         uint2 lo = *reinterpret_cast<const uint2 *>(xrow + 32 * c + 4 * q);
         uint2 hi = *reinterpret_cast<const uint2 *>(xrow + 32 * c + 16 + 4 * q);
@@ -149,12 +168,13 @@ constexpr int kCodeRowLds = 256 + 16;
 constexpr bool kLdsCodes = true;   // staged loads measured faster on MI355X
 constexpr int kZeroLds = 256;
 template <int FMT> constexpr int scale_pad() {
-    return (FMT == INT4) ? 8 : (FMT == INT4AFF ? 16 : (FMT == KM4 ? 0 : 4));
+    return (FMT == INT4) ? 8 : (FMT == INT4AFF ? 16 : ((FMT == KM4 || FMT == INT8KM) ? 0 : 4));
 }
 // per-row bytes of the scale plane (KM4: the row's 16-entry fp16 table;
 // INT4AFF: a 32-bit scale + bias word per block)
 template <int FMT> __host__ __device__ constexpr int scale_row_bytes(int K) {
-    return (FMT == KM4) ? 32 : ((FMT == FP4) ? K / 32 : (FMT == INT4AFF ? K / 8 : K / 16));
+    // INT8KM: a row group's 256-entry table, 512 bytes over 16 rows
+    return (FMT == KM4 || FMT == INT8KM) ? 32 : ((FMT == FP4) ? K / 32 : (FMT == INT4AFF ? K / 8 : K / 16));
 }
 // affine int4: per-workgroup LDS table of the x block sums, [K/32][16 batch] fp32
 template <int FMT> __host__ __device__ constexpr int xsum_lds_bytes(int K) {
@@ -188,7 +208,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                                                           const _Float16 *__restrict__ x, int B,
                                                           float *__restrict__ y) {
     extern __shared__ __align__(16) _Float16 xs[];
-    constexpr int MPJ = (FMT == INT8) ? 2 : 4;   // blocks (MFMAs) per j-step
+    constexpr bool BYTES = (FMT == INT8 || FMT == INT8KM);   // one code per byte
+    constexpr bool TABLE = (FMT == KM4 || FMT == INT8KM);   // no block scales
+    constexpr int MPJ = BYTES ? 2 : 4;                      // blocks (MFMAs) per j-step
     const int KP = K + 8;                         // padded x row in LDS, halfs
     const int groups = K / 8;
     for (int i = threadIdx.x; i < B * groups; i += 64 * kMfmaWaves) {
@@ -223,9 +245,9 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
     const int r = lane & 15, q = lane >> 4;
     const int64_t rows0 = ((int64_t)blockIdx.x * kMfmaWaves + wave) * (RG * 16);
     if (rows0 >= N) return;
-    const int J = (FMT == INT8) ? K / 64 : K / 128;   // j-steps per row
+    const int J = BYTES ? K / 64 : K / 128;   // j-steps per row
     const int cpr = 4 * J;                             // 16-byte chunks per row
-    const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
+    const uint32_t row_bytes = BYTES ? (uint32_t)K : (uint32_t)K / 2;
     const int srb = scale_row_bytes<FMT>(K);
     const int srs = srb + scale_pad<FMT>();            // padded scale row in LDS
     uint8_t *wl = zl + kZeroLds + xsum_lds_bytes<FMT>(K) + wave * wave_lds_bytes<FMT, LDS_CODES>(K);
@@ -268,7 +290,8 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
         // bytes. A last, partial group reads rows N - 16 .. N - 1 instead
         // (N >= 16) and looks its rows up shifted by the difference.
         const int64_t g0 = grow + 16 <= N ? grow : N - 16;
-        const uint8_t *sp = reinterpret_cast<const uint8_t *>(plane) + g0 * srb;
+        // int8km: the table of the row group's 32-row group (N % 32 == 0, so no partial groups)
+        const uint8_t *sp = reinterpret_cast<const uint8_t *>(plane) + (FMT == INT8KM ? (g0 / 32) * 512 : g0 * srb);
 #pragma unroll
         for (int u = 0; u < SP; u++) {
             int off = 16 * (lane + 64 * u);
@@ -357,7 +380,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                         const uint2 s2 = *reinterpret_cast<const uint2 *>(sl + srow * srs + 8 * j);
                         s0w = s2.x;
                         s1w = s2.y;
-                    } else if constexpr (FMT != KM4) {
+                    } else if constexpr (!TABLE) {
                         s0w = *reinterpret_cast<const uint32_t *>(sl + srow * srs + 4 * j);
                     }
                     // the j-step's MFMAs are independent: decode and read every
@@ -370,10 +393,12 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                         ax[m] = *reinterpret_cast<const h8 *>(xa + xstride * (uint32_t)j + 64 * m);
                         if constexpr (FMT == KM4)
                             bw[m] = decode8_km4_reg(w[m], kL, kH);
+                        else if constexpr (FMT == INT8KM)
+                            bw[m] = decode8_km8(w[2 * m], w[2 * m + 1], (uint32_t)(uintptr_t)sl);
                         else
                             bw[m] = (FMT == INT8) ? decode8<FMT>(w[2 * m], w[2 * m + 1]) : decode8<FMT>(w[m], 0u);
                     }
-                    if constexpr (FMT == KM4) {
+                    if constexpr (TABLE) {
                         // no block scales: the MFMAs accumulate directly (one
                         // accumulator per block position keeps them independent)
 #pragma unroll
@@ -412,7 +437,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
             wave_sync_lds();   // the next step rewrites the staging buffers
             if (valid && t == steps_per_group - 1) {
                 // group done: lane (r, q) holds y[4q + v][row]
-                if constexpr (FMT == KM4) {
+                if constexpr (TABLE) {
 #pragma unroll
                     for (int m = 0; m < MPJ; m++) {
 #pragma unroll
@@ -438,21 +463,22 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
            (size_t)kMfmaWaves * wave_lds_bytes<FMT, kLdsCodes>((int)K);
 }
 
-// The batched matrix-core path takes int4, affine int4 (K <= 2048), fp4, int8
-// and km4 (not int8 k-means), fp16 x, 3 <= B <= 8, whole load steps
-// (K % 512 == 0, int8 K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned
+// The batched matrix-core path takes int4, affine int4 (K <= 2048), fp4, int8,
+// km4 and int8 k-means, fp16 x, 3 <= B <= 8, whole load steps (K % 512 == 0,
+// int8 and int8 k-means K % 256 == 0), K <= 4096, N >= 16, a 16-byte aligned
 // scale plane, and staging that fits in 64 KiB of LDS (affine int4: 80 KiB,
 // two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
-    if (fmt == INT8KM || B < 3 || B > 8 || N < 16) return false;
+    if (B < 3 || B > 8 || N < 16) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
-    if (K % ((fmt == INT8) ? 256 : 512) != 0 || K > 4096) return false;
+    if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
                  : (fmt == INT4AFF) ? mfma_lds_bytes<INT4AFF>(K, B)
                  : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
-                 : (fmt == INT8) ? mfma_lds_bytes<INT8>(K, B) : mfma_lds_bytes<KM4>(K, B);
+                 : (fmt == INT8) ? mfma_lds_bytes<INT8>(K, B)
+                 : (fmt == INT8KM) ? mfma_lds_bytes<INT8KM>(K, B) : mfma_lds_bytes<KM4>(K, B);
     return lds <= (fmt == INT4AFF ? 80 : 64) * 1024;
 }
 
@@ -492,6 +518,7 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
     case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st);
     case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st);
     case INT8: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
+    case INT8KM: return launch_mfma_fmt<INT8KM>(codes, plane, N, (int)K, x, B, y, st);
     default: return launch_mfma_fmt<KM4>(codes, plane, N, (int)K, x, B, y, st);
     }
 }
