@@ -189,7 +189,8 @@ qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_
 
 /* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
  * weight is exact in fp32, except affine int4, where s * u + b is rounded
- * once to the nearest fp32) [S3 "Theoretical size" for the plane shapes]. */
+ * once to the nearest fp32) [S3 "Theoretical size" for the plane shapes].
+ * QMV_INT8KM: N % 32 == 0. */
 qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
                     float *W_hat, void *stream);
 
@@ -248,7 +249,8 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane,
  *  qmoe_route; h [T][topk][I] fp16 = fp16(silu(gate) * up) per slot; y
  *  [T][H] fp32 = sum over slots (in slot order) of weights * (W_down h).
  * 1 <= T <= 8, 1 <= topk <= min(E, 64), E <= 4096; H and I multiples of 32
- * in [32, 8192] (4096 for INT8). Buffers must not overlap. */
+ * in [32, 8192] (4096 for INT8 and INT8KM; the int8 k-means tables then
+ * cover 32-row groups of every expert matrix). Buffers must not overlap. */
 qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane,
                     const void *dn_codes, const void *dn_plane, int E, int64_t H, int64_t I,
                     const float *logits, const void *x, int T, int topk,
@@ -272,9 +274,9 @@ size_t qmatvec_argmax_workspace_bytes(int64_t N, int B);
  * qmatvec_* of `fmt`; x fp16 [B][K]; idx int32 [B]; val fp32 [B]; NaN
  * values are not ordered. 1 <= B <= 8; the shapes of the batch-1..8 dot
  * product path (K multiple of 32, up to 8192 for 4-bit formats and 4096
- * for int8, and at B > 2 the register budget of that path; QMV_E_SHAPE
- * otherwise). workspace >= qmatvec_argmax_workspace_bytes(N, B), 8-byte
- * aligned. */
+ * for int8 and int8 k-means, and at B > 2 the register budget of that path;
+ * QMV_INT8KM also N % 32 == 0; QMV_E_SHAPE otherwise). workspace >=
+ * qmatvec_argmax_workspace_bytes(N, B), 8-byte aligned. */
 qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
                           const void *x, int B, int32_t *idx, float *val,
                           void *workspace, size_t ws_bytes, void *stream);
