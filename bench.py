@@ -1,7 +1,7 @@
 """Benchmark: effective weight GB/s and fraction of HBM peak of the 4-bit
 k-means-palettized (km4) lm_head matvec, 248320 x 2048, batch 1, on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 
 A step is one call of the fused dequantize-matvec on the lm_head weights
 (the decode hot path; quantize-and-pack is export-time work and is timed once
@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--all", action="store_true", help="also time the int8 head and the MoE layer")
+    ap.add_argument("--quick", action="store_true", help="skip the int8 head, the MoE layer and the fp4 4096^2 config")
+    ap.add_argument("--all", action="store_true", help="(default; kept for older command lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-metric", action="store_true", help="time the metric kernel only (for profiling)")
     ap.add_argument("--calibrate", action="store_true",
@@ -104,6 +105,22 @@ def timed(fn, steps, warmup):
     e1.record(st)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def per_call_us(fn, steps):
+    """p10 / median / p90 of single-call durations (an event pair around each
+    of `steps` back-to-back calls, after the timed loop; not used for `value`)."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(st)
+    for i in range(steps):
+        fn(i)
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps))
+    pick = lambda q: round(d[min(len(d) - 1, int(q * len(d)))], 2)
+    return pick(0.1), pick(0.5), pick(0.9)
 
 
 def timed_graph(fn, steps, per_graph=32):
@@ -212,11 +229,16 @@ def main():
 
     gpu_warm(step)
     ms = timed(step, args.steps, args.warmup)
+    p10 = p50 = p90 = None
+    if not args.only_metric:
+        p10, p50, p90 = per_call_us(step, args.steps)
     nbytes = algo_bytes("km4", N_ROWS, K_DIM)
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("km4 B=1: %.2f us/call, %.1f GB/s (%.1f%% of 8 TB/s)" % (ms * 1e3, gbs, gbs / PEAK_GBS * 100))
 
     extras = {"km4_pack_ms": round(pack_ms, 3)}
+    if p50 is not None:
+        extras.update({"km4_B1_us_p10": p10, "km4_B1_us_p50": p50, "km4_B1_us_p90": p90})
     if not args.only_metric:
         # practical read ceiling over the same footprint
         buf = torch.empty((len(copies), nbytes // 16 * 16), dtype=torch.uint8, device="cuda")
@@ -309,7 +331,8 @@ def main():
                 extras["%s_%s_us" % (name, fmt)] = round(msq * 1e3, 2)
                 extras["%s_%s_GBps" % (name, fmt)] = round(algo_bytes(fmt, n, k) / (msq * 1e-3) / 1e9, 1)
                 del pk
-        if args.all:
+        if not args.quick:
+            extras.update(bench_fp4_square(args))
             extras.update(bench_int8_head(args))
             extras.update(bench_moe(args))
 
@@ -338,6 +361,30 @@ def main():
         log("cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(c, c.x[:1])
     print(json.dumps(result), flush=True)
+
+
+def bench_fp4_square(args):
+    """fp4 4096 x 4096 (8.9 MB of codes and scales, batch 1 and 4): 64 weight
+    copies cycled so no call finds its weights in the 256 MB cache; HIP graphs
+    of 64 calls, since one call is launch-latency bound."""
+    import torch
+    import quantized_decode_matvec_amd as qmv
+    from quantized_decode_matvec_amd import workloads as wl
+    c = wl.fp4_square()
+    W = torch.from_numpy(c.W).cuda()
+    p0 = qmv.qpack_fp4(W)
+    del W
+    pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(63)]
+    nb = algo_bytes("fp4", 4096, 4096)
+    out = {}
+    for B in (1, 4):
+        x = torch.from_numpy(c.x[:B]).cuda().contiguous()
+        y = torch.empty((B, 4096), dtype=torch.float32, device="cuda")
+        ms = timed_graph(lambda i: qmv.qmatvec_fp4(pk[i % 64][0], pk[i % 64][1], x, y=y), 4 * args.steps,
+                         per_graph=64)
+        out["fp4_4096sq_B%d_us" % B] = round(ms * 1e3, 2)
+        out["fp4_4096sq_B%d_GBps" % B] = round(nb / (ms * 1e-3) / 1e9, 1)
+    return out
 
 
 def bench_int8_head(args):

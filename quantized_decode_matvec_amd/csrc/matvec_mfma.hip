@@ -470,6 +470,9 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
 // two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
     if (B < 3 || B > 8 || N < 16) return false;
+    // below 16384 rows the dot2 path is as fast at B = 3, 4 (fp4 4096 x 2048:
+    // 6.8 us against 7.4 us); from B = 5 the matrix cores win at any size
+    if (B <= 4 && N < 16384) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
@@ -482,10 +485,10 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     return lds <= (fmt == INT4AFF ? 80 : 64) * 1024;
 }
 
-template <int FMT, int SP>
-static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+template <int FMT, int SP, int RG>
+static hipError_t launch_mfma_rg(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
                                  float *y, hipStream_t st) {
-    constexpr int RG = 8, D = 2;
+    constexpr int D = 2;
     const int64_t rows_wg = (int64_t)kMfmaWaves * RG * 16;
     const int64_t grid = (N + rows_wg - 1) / rows_wg;
     const size_t lds = mfma_lds_bytes<FMT>(K, B);
@@ -498,6 +501,20 @@ static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_
     hipLaunchKernelGGL((mv_mfma<FMT, RG, SP, D, kLdsCodes>), dim3((unsigned)grid), dim3(64 * kMfmaWaves), lds, st,
                        codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
     return hipGetLastError();
+}
+
+// Row groups per wave: about 512 workgroups (two per CU, the residency the
+// LDS staging allows) whatever N; measured on MI355X at B = 4 and 8: 4096 to
+// 32768 rows are fastest with one group per wave, 65536 with two, the
+// 248320-row lm_head with eight.
+template <int FMT, int SP>
+static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
+                                 float *y, hipStream_t st) {
+    const int64_t per_rg1 = (int64_t)kMfmaWaves * 16 * 512;   // rows that give 512 workgroups at RG = 1
+    if (N >= 6 * per_rg1) return launch_mfma_rg<FMT, SP, 8>(codes, plane, N, K, x, B, y, st);
+    if (N >= 3 * per_rg1) return launch_mfma_rg<FMT, SP, 4>(codes, plane, N, K, x, B, y, st);
+    if (N >= (3 * per_rg1) / 2) return launch_mfma_rg<FMT, SP, 2>(codes, plane, N, K, x, B, y, st);
+    return launch_mfma_rg<FMT, SP, 1>(codes, plane, N, K, x, B, y, st);
 }
 
 template <int FMT>

@@ -228,3 +228,27 @@ def test_tall_batch1_shape_on_sampled_rows(fmt):
         oc, op = oracle.pack(fmt, W[rows])
         want = oracle.matvec(fmt, oc, op, x)
     assert rel_err(y[:, rows], want) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff", "int8km"])
+@pytest.mark.parametrize("N,Bs", [(16416, (3, 4, 8)), (49184, (5,)), (98336, (8,))])
+def test_batched_large_matrices_on_sampled_rows(fmt, N, Bs):
+    """The matrix-core path at B = 3 and 4 takes matrices of at least 16384
+    rows, and its rows per wave grow with N (one, two, four row groups here):
+    the GPU packs and multiplies the whole matrix, the oracle packs and
+    multiplies sampled rows (whole 32-row groups for int8 k-means)."""
+    from tests.gpu_helpers import sample_rows
+    K = 1024
+    c = wl.small_dense("km4", N, K, batch=8, seed=N, outlier_frac=0.01)
+    W, x = c.W, c.x
+    print("large batched", fmt, N, Bs, flush=True)
+    codes, plane = qmv.qpack(fmt, dev(W))
+    if fmt == "int8km":
+        groups = np.unique(sample_rows(N // 32, n=6, seed=2))
+        rows = np.concatenate([np.arange(32 * g, 32 * g + 32) for g in groups])
+    else:
+        rows = sample_rows(N, n=96, seed=2)
+    oc, op = oracle.pack(fmt, W[rows])
+    for B in Bs:
+        y = host(qmv.qmatvec(fmt, codes, plane, dev(x[:B])))
+        assert rel_err(y[:, rows], oracle.matvec(fmt, oc, op, x[:B])) <= RTOL, B
