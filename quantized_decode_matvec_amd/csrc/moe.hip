@@ -334,8 +334,8 @@ __device__ __forceinline__ void gather_pass(const GatherArgs &a, const uint8_t *
 #pragma unroll
             for (int q = 0; q < R * PB; q++) {
                 float v = row16_sum(acc[q]);
-                if constexpr (LPR >= 32) v += __shfl_xor(v, 16);
-                if constexpr (LPR == 64) v += __shfl_xor(v, 32);
+                if constexpr (LPR >= 32) v = half_swap_add<16>(v, v);
+                if constexpr (LPR == 64) v = half_swap_add<32>(v, v);
                 acc[q] = v;
             }
             if (sub == 0) {

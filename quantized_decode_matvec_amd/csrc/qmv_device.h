@@ -312,10 +312,29 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Cross-half exchange-and-add without LDS. v_permlane32_swap swaps the upper
+// 32 lanes of its first operand with the lower 32 of its second, so adding the
+// two results gives a(l) + a(l + 32) in lanes 0..31 and b(l - 32) + b(l) in
+// lanes 32..63; v_permlane16_swap does the same between 16-lane rows 0/1 and
+// 2/3 (a in rows 0 and 2, b in rows 1 and 3). The empty asm keeps the second
+// result opaque: without it the optimizer folds the float reinterpretation of
+// the second result into the first and adds the first to itself.
+template <int HALF>
+__device__ __forceinline__ float half_swap_add(float a, float b) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t ua = __builtin_bit_cast(uint32_t, a), ub = __builtin_bit_cast(uint32_t, b);
+    u32x2 s;
+    if constexpr (HALF == 32) s = __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+    else s = __builtin_amdgcn_permlane16_swap(ua, ub, false, false);
+    uint32_t s0 = s[0], s1 = s[1];
+    __asm__("" : "+v"(s1));
+    return __builtin_bit_cast(float, s0) + __builtin_bit_cast(float, s1);
+}
+
 // Reduce V partial sums per lane over groups of LPR lanes (LPR = 16, 32 or 64).
 // Instead of V separate butterflies, each cross-row step exchanges half of the
 // values and keeps the other half ("transposed" reduction), so a step costs
-// V/2 shuffles and the set of live values halves. On return v[0 .. live) hold
+// V/2 lane swaps and the set of live values halves. On return v[0 .. live) hold
 // group sums, identical in every lane of a 16-lane row; value j of lane l is
 // the original index base + j (see live/base below).
 template <int V, int LPR>
@@ -325,28 +344,18 @@ struct GroupReduce {
     static constexpr bool kH16 = (LPR >= 32 && kV1 >= 2);
     static constexpr int live = kH16 ? kV1 / 2 : kV1;
 
-    __device__ __forceinline__ static void run(float (&v)[V], int lane) {
+    __device__ __forceinline__ static void run(float (&v)[V], int /*lane*/) {
         if constexpr (kH32) {
-            const bool up = lane & 32;
 #pragma unroll
-            for (int j = 0; j < V / 2; j++) {
-                float send = up ? v[j] : v[j + V / 2];
-                float keep = up ? v[j + V / 2] : v[j];
-                v[j] = keep + __shfl_xor(send, 32);
-            }
+            for (int j = 0; j < V / 2; j++) v[j] = half_swap_add<32>(v[j], v[j + V / 2]);
         } else if constexpr (LPR == 64) {
-            v[0] += __shfl_xor(v[0], 32);
+            v[0] = half_swap_add<32>(v[0], v[0]);
         }
         if constexpr (kH16) {
-            const bool up = lane & 16;
 #pragma unroll
-            for (int j = 0; j < kV1 / 2; j++) {
-                float send = up ? v[j] : v[j + kV1 / 2];
-                float keep = up ? v[j + kV1 / 2] : v[j];
-                v[j] = keep + __shfl_xor(send, 16);
-            }
+            for (int j = 0; j < kV1 / 2; j++) v[j] = half_swap_add<16>(v[j], v[j + kV1 / 2]);
         } else if constexpr (LPR >= 32) {
-            v[0] += __shfl_xor(v[0], 16);
+            v[0] = half_swap_add<16>(v[0], v[0]);
         }
 #pragma unroll
         for (int j = 0; j < live; j++) v[j] = row16_sum(v[j]);
