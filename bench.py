@@ -170,23 +170,35 @@ def traffic_from_profiles(key):
 
 
 def cpu_baseline(c, x1):
-    """The oracle, untuned: pack a sample of rows, then time its matvec on them."""
+    """The oracle, untuned: pack a sample of rows, then time its matvec on them,
+    on all cores (the reported baseline) and on one thread (an extra)."""
     import oracle
     rows = 4096
     codes, lut = oracle.pack_km4(c.W[:rows])
     bytes_per_row = algo_bytes("km4", 1, K_DIM)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        oracle.matvec("km4", codes, lut, x1)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > 5.0 or reps >= 200:
-            break
-    gbs = rows * bytes_per_row * reps / el / 1e9
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+
+    def rate(seconds):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.matvec("km4", codes, lut, x1)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > seconds or reps >= 10000:
+                break
+        return rows * bytes_per_row * reps / el / 1e9, reps, el
+
+    cores = oracle.num_threads()
+    gbs, reps, el = rate(10.0)
+    oracle.set_num_threads(1)
+    try:
+        gbs1, reps1, el1 = rate(5.0)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "km4 matvec over the first %d of 248320 lm_head rows (batch 1), %d repetitions, %.1f s"
-                      % (rows, reps, el)}
+                      % (rows, reps, el)}, {"cpu_oracle_1thread_GBps": round(gbs1, 4),
+                                            "cpu_oracle_1thread_reps": reps1}
 
 
 def main():
@@ -359,7 +371,8 @@ def main():
     }
     if not args.no_cpu and not args.only_metric:
         log("cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(c, c.x[:1])
+        result["cpu_baseline"], one = cpu_baseline(c, c.x[:1])
+        extras.update(one)
     print(json.dumps(result), flush=True)
 
 

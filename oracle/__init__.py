@@ -78,6 +78,8 @@ def lib():
         L.orc_moe_ffn.argtypes = [ci, P, P, P, P, ci, i64, i64, P, ci, ci, P, P, P, P]
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ci
+        L.orc_set_num_threads.argtypes = [ci]
+        L.orc_set_num_threads.restype = None
         for f in ("orc_pack_fp4", "orc_pack_int4", "orc_pack_int8", "orc_pack_km4",
                   "orc_dequant", "orc_matvec", "orc_moe_route", "orc_moe_ffn"):
             getattr(L, f).restype = None
@@ -105,6 +107,11 @@ def _check_shape(W):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP thread count (results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 # --- scalar fp16 helpers (written from the binary16 definition in oracle.c) ---

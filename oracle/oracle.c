@@ -812,3 +812,11 @@ int orc_num_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Set the thread count of the OpenMP loops (the CPU baseline is timed on all
+ * cores and on one). Results do not depend on it: every parallel loop writes
+ * disjoint outputs and sums in a fixed order. */
+void orc_set_num_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
