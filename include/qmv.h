@@ -203,7 +203,8 @@ qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_
 /* Top-k routing: logits [T][E] fp32 -> ids [T][topk] int32 (largest logit
  * first, equal logits in increasing id order) and weights [T][topk] fp32,
  * the softmax over the selected logits. 1 <= T <= 64, 1 <= topk <= min(E, 64),
- * E <= 4096. */
+ * E <= 4096. NaN logits rank below every number (ids stay valid expert
+ * indices; the weights of such a token are then unspecified). */
 qmv_status qmoe_route(const float *logits, int T, int E, int topk,
                       int32_t *ids, float *weights, void *stream);
 

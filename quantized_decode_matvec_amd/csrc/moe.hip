@@ -43,21 +43,6 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
-template <int CTRL>
-__device__ __forceinline__ int dpp_imov(int v) {
-    return __builtin_amdgcn_update_dpp(0x7fffffff, v, CTRL, 0xF, 0xF, false);
-}
-
-// min over the wave of a non-negative int, returned in every lane
-__device__ __forceinline__ int wave_min(int v) {
-    v = min(v, dpp_imov<0xB1>(v));
-    v = min(v, dpp_imov<0x4E>(v));
-    v = min(v, dpp_imov<0x141>(v));
-    v = min(v, dpp_imov<0x140>(v));
-    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
 __device__ __forceinline__ float wave_sum(float v) {
     v = row16_sum(v);
     return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
@@ -84,12 +69,24 @@ __device__ __forceinline__ void route_token(const float *__restrict__ l, int E, 
         for (int i = 0; i < PER_LANE; i++)
             if (lane + 64 * i < E && !((taken >> i) & 1ull)) best = fmaxf(best, v[i]);
         const float m = wave_max(best);
-        // the lowest untaken expert id holding the maximum
-        int cand = 0x7fffffff;
+        // the lowest untaken expert id holding the maximum: ids lane + 64 i,
+        // so the first slot i with a holder, then its lowest lane (one wave
+        // ballot per slot, scalar find-first-set)
+        int sel = 0x7fffffff;
 #pragma unroll
-        for (int i = PER_LANE - 1; i >= 0; i--)
-            if (lane + 64 * i < E && !((taken >> i) & 1ull) && v[i] == m) cand = lane + 64 * i;
-        const int sel = wave_min(cand);
+        for (int i = PER_LANE - 1; i >= 0; i--) {
+            const uint64_t b = __ballot(lane + 64 * i < E && !((taken >> i) & 1ull) && v[i] == m);
+            if (b != 0ull) sel = 64 * i + __builtin_ctzll(b);
+        }
+        if (sel == 0x7fffffff) {
+            // only NaN logits left untaken: the lowest untaken id (NaN ranks
+            // below every number), so ids stay valid expert indices
+#pragma unroll
+            for (int i = PER_LANE - 1; i >= 0; i--) {
+                const uint64_t b = __ballot(lane + 64 * i < E && !((taken >> i) & 1ull));
+                if (b != 0ull) sel = 64 * i + __builtin_ctzll(b);
+            }
+        }
         if ((sel & 63) == lane) taken |= 1ull << (sel >> 6);
         if (lane == j) {
             my_i = sel;

@@ -105,6 +105,26 @@ def test_route_wide(E, T):
     assert np.allclose(host(w), ow, rtol=1e-6, atol=1e-7)
 
 
+def test_route_nan_logits_rank_last():
+    """NaN logits rank below every number: ids stay valid and distinct and equal
+    the oracle's on the logits with NaN replaced by -inf (there equal logits go
+    to the lower id, as the NaN entries do here); one token has fewer finite
+    logits than topk."""
+    rng = np.random.default_rng(21)
+    T, E, topk = 3, 256, 8
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, rng.choice(E, 5, replace=False)] = np.nan
+    logits[1, :] = np.nan
+    logits[1, rng.choice(E, 6, replace=False)] = rng.standard_normal(6).astype(np.float32)
+    ids, w = qmv.qmoe_route(dev(logits), topk)
+    ids, w = host(ids), host(w)
+    oids, ow = oracle.moe_route(np.where(np.isnan(logits), -np.inf, logits).astype(np.float32), topk)
+    assert np.array_equal(ids, oids)
+    for t in range(T):
+        assert len(set(ids[t].tolist())) == topk and ids[t].min() >= 0 and ids[t].max() < E
+    assert np.allclose(w, ow, rtol=1e-6, atol=1e-7)
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_moe_ffn_replays_identically_in_a_hip_graph(T):
     """qmoe_ffn allocates nothing and never synchronizes, so it can be
