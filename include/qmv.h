@@ -217,7 +217,9 @@ size_t gather_qmatvec_workspace_bytes(int T, int topk, int E, int64_t N, qmv_epi
  *  codes/plane: E stacked expert matrices [E][N][...] in `fmt`'s layout.
  *  x: x_per_slot == 0: [T][K] (one input per token, shared by its slots);
  *     x_per_slot == 1: [T][topk][K] (one input per token and slot).
- *  ids [T][topk] int32 in [0, E); weights [T][topk] fp32 (COMBINE only).
+ *  ids [T][topk] int32 in [0, E) (an id below 0 or at least E is read as 0
+ *  or E - 1: never a memory access outside the slabs); weights [T][topk]
+ *  fp32 (COMBINE only).
  *  epi == QMV_EPI_NONE:    y fp32 [T][topk][N].
  *  epi == QMV_EPI_SWIGLU:  rows [0, N/2) are gate, [N/2, N) up; y fp16
  *                          [T][topk][N/2] = fp16(silu(gate) * up); N even.

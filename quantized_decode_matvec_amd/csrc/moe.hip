@@ -395,7 +395,11 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
             }
         }
     } else {
-        for (int i = tid; i < npairs; i += blockDim.x) s_ids[i] = a.ids[i];
+        // ids outside [0, E) are clamped into it: no read outside the expert slabs
+        for (int i = tid; i < npairs; i += blockDim.x) {
+            const int e = a.ids[i];
+            s_ids[i] = e < 0 ? 0 : (e < a.E ? e : a.E - 1);
+        }
     }
     __syncthreads();
     for (int i = tid; i < npairs; i += blockDim.x) {
@@ -499,7 +503,8 @@ __global__ __launch_bounds__(64) void combine_gather_kernel(GatherArgs a) {
         for (int b = 0; b < SB; b++) {
             // slots past topk repeat the last one with weight 0
             const int s = s0 + b < a.topk ? s0 + b : a.topk - 1;
-            const int e = a.ids[t * a.topk + s];
+            const int e0 = a.ids[t * a.topk + s];
+            const int e = e0 < 0 ? 0 : (e0 < a.E ? e0 : a.E - 1);   // clamped, as in the expert-major kernel
             ws[b] = s0 + b < a.topk ? a.weights[t * a.topk + s] : 0.f;
             const uint8_t *codes_e;
             const void *plane_e;

@@ -105,6 +105,23 @@ def test_route_wide(E, T):
     assert np.allclose(host(w), ow, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("epi", ["none", "swiglu", "combine"])
+def test_gather_clamps_out_of_range_ids(epi):
+    """ids below 0 or at least E read as 0 or E - 1: the same bits as the
+    call with the clamped ids."""
+    fmt, E, H, I, T, topk = "int4", 12, 160, 64, 4, 3
+    guc, gup, dnc, dnp, x, logits = _case(fmt, E, H, I, T, topk, seed=9)
+    oids, ow = oracle.moe_route(logits, topk)
+    bad = oids.copy()
+    bad[0, 0], bad[1, 2], bad[3, 1] = -7, E, E + 100
+    good = np.clip(bad, 0, E - 1).astype(np.int32)
+    w = dev(ow.astype(np.float32)) if epi == "combine" else None
+    codes, plane = dev(guc), dev(gup)
+    yb = host(qmv.gather_qmatvec(fmt, codes, plane, dev(x), dev(bad.astype(np.int32)), weights=w, epi=epi))
+    yg = host(qmv.gather_qmatvec(fmt, codes, plane, dev(x), dev(good), weights=w, epi=epi))
+    assert np.array_equal(yb, yg)
+
+
 def test_route_nan_logits_rank_last():
     """NaN logits rank below every number: ids stay valid and distinct and equal
     the oracle's on the logits with NaN replaced by -inf (there equal logits go
