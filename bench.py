@@ -343,6 +343,20 @@ def main():
                 extras["%s_%s_us" % (name, fmt)] = round(msq * 1e3, 2)
                 extras["%s_%s_GBps" % (name, fmt)] = round(algo_bytes(fmt, n, k) / (msq * 1e-3) / 1e9, 1)
                 del pk
+        # one GPU's share of an lm_head split by rows over 8 GPUs (31040 x 2048):
+        # the 32 distinct row slices of the weight copies, so no call finds its
+        # codes in the cache; matvec and the fused argmax, in HIP graphs
+        ns = N_ROWS // 8
+        sl = [(cc[s * ns:(s + 1) * ns], ll[s * ns:(s + 1) * ns]) for cc, ll in copies for s in range(8)]
+        mss = timed_graph(lambda i: qmv.qmatvec_km4(sl[i % len(sl)][0], sl[i % len(sl)][1], x1, y=y[:1, :ns]),
+                          4 * args.steps, per_graph=len(sl))
+        wss = torch.empty((qmv.qmatvec_argmax_workspace_bytes(ns, 1),), dtype=torch.uint8, device="cuda")
+        msx = timed_graph(lambda i: qmv.qmatvec_argmax("km4", sl[i % len(sl)][0], sl[i % len(sl)][1], x1, idx=aidx,
+                                                       val=aval, workspace=wss), 4 * args.steps, per_graph=len(sl))
+        extras["km4_shard8_%d_us" % ns] = round(mss * 1e3, 2)
+        extras["km4_shard8_%d_GBps" % ns] = round(algo_bytes("km4", ns, K_DIM) / (mss * 1e-3) / 1e9, 1)
+        extras["km4_shard8_%d_argmax_us" % ns] = round(msx * 1e3, 2)
+        del sl, wss
         if not args.quick:
             extras.update(bench_fp4_square(args))
             extras.update(bench_int8_head(args))
