@@ -272,14 +272,15 @@ size_t qmatvec_argmax_workspace_bytes(int64_t N, int B);
 /* Fused matvec + argmax: for each batch row b, idx[b] = the row n with the
  * largest y[b][n] = sum_k dequant(W)[n][k] * x[b][k] (fp32 accumulation, as
  * qmatvec_*), the lowest n among equal largest values, and val[b] = that
- * y[b][n]. y itself is never written; each wave of the matvec keeps its
- * best (value, row) and a second launch reduces those. codes/plane as for
+ * y[b][n]. The matvec writes y into the workspace (the caller allocates no
+ * logits) and a second launch takes each row's argmax. codes/plane as for
  * qmatvec_* of `fmt`; x fp16 [B][K]; idx int32 [B]; val fp32 [B]; NaN
  * values are not ordered. 1 <= B <= 8; the shapes of the batch-1..8 dot
  * product path (K multiple of 32, up to 8192 for 4-bit formats and 4096
  * for int8 and int8 k-means, and at B > 2 the register budget of that path;
  * QMV_INT8KM also N % 32 == 0; QMV_E_SHAPE otherwise). workspace >=
- * qmatvec_argmax_workspace_bytes(N, B), 8-byte aligned. */
+ * qmatvec_argmax_workspace_bytes(N, B) (128 bytes + B * N fp32), 8-byte
+ * aligned; calls sharing a workspace must not overlap. */
 qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
                           const void *x, int B, int32_t *idx, float *val,
                           void *workspace, size_t ws_bytes, void *stream);

@@ -30,6 +30,10 @@ namespace qmv {
 // Argmax keys: the fp32 value in order-preserving form above the complement
 // of the row index, so the largest key is the largest value and, among equal
 // values, the lowest row. Every finite value gives a key above 0.
+// argmax workspace: kArgmaxHeader 64-bit words (maxima of batch rows 0..7,
+// then the reduction's workgroup counter) before the per-wave keys
+constexpr int kArgmaxHeader = 16;
+
 __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
     uint32_t b = __builtin_bit_cast(uint32_t, v);
     b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
@@ -57,16 +61,16 @@ struct OutlierArgs {
     int n = 0;
 };
 
-// ARGMAX: instead of storing y, each wave keeps the largest key per batch row
-// over its rows and writes it to part[wave][b] (the fused lm_head + argmax);
-// waves past the last row write 0.
+// hdr: if not null, the first wave zeroes kArgmaxHeader words there (the
+// per-row maxima and the workgroup counter of the argmax launch that follows
+// this matvec in the fused lm_head + argmax).
 // OUTL: add the int8 outliers of each row (4-bit k-means rows only).
-template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK, bool ARGMAX = false,
+template <int FMT, int BT, int LPR, int CPL, int R, int ITERS, int WAVES, bool FULLK,
           bool OUTL = false>
 __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict__ codes,
                                                       const void *__restrict__ plane, int64_t N, int K,
                                                       const _Float16 *__restrict__ x, int B,
-                                                      float *__restrict__ y, uint64_t *__restrict__ part,
+                                                      float *__restrict__ y, uint64_t *__restrict__ hdr,
                                                       OutlierArgs ol) {
     constexpr int RPW = kWave / LPR;            // rows per row group
     constexpr int XW = ChunkTraits<FMT>::kXWords;
@@ -92,15 +96,8 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     const int nb = K / 32;                                                          // blocks per row
     const uint32_t row_bytes = (FMT == INT8 || KM8) ? (uint32_t)K : (uint32_t)K / 2;
     const int64_t wrow0 = ((int64_t)blockIdx.x * WAVES + wave) * ROWS_IT * ITERS;
-    if (wrow0 >= N) {
-        if constexpr (ARGMAX) {
-            if (lane < B) part[((int64_t)blockIdx.x * WAVES + wave) * B + lane] = 0;
-        }
-        return;
-    }
-    uint64_t kbest[ARGMAX ? BT : 1];
-#pragma unroll
-    for (int b = 0; b < (ARGMAX ? BT : 1); b++) kbest[b] = 0;
+    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
+    if (wrow0 >= N) return;
 
     // Loads of one iteration. Wave-uniform bases, 32-bit per-lane offsets.
     // Loads are unconditional: a row past the end reads row N-1 and a chunk
@@ -298,54 +295,57 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
             for (int j = 0; j < Red::live; j++) {
                 int idx = base + j, g = idx / BT, b = idx % BT;
                 int64_t row = row0 + g * RPW + rsub;
-                if constexpr (ARGMAX) {
-                    if (row < N) {
-                        const uint64_t key = argmax_key(acc[j], row);
-#pragma unroll
-                        for (int bb = 0; bb < BT; bb++)
-                            if (bb == b && key > kbest[bb]) kbest[bb] = key;
-                    }
-                } else {
-                    if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
-                }
+                if (row < N && b < B) y[(size_t)b * N + row] = acc[j];
             }
-        }
-    }
-    if constexpr (ARGMAX) {
-#pragma unroll
-        for (int bb = 0; bb < BT; bb++) {
-            const uint64_t k = wave_max_u64(kbest[bb]);
-            if (lane == 0 && bb < B) part[((int64_t)blockIdx.x * WAVES + wave) * B + bb] = k;
         }
     }
 }
 
-// Largest key over the partials of each batch row -> (index, value). Four
-// independent loads per thread and step keep the reads in flight.
-__global__ __launch_bounds__(1024) void argmax_reduce_kernel(const uint64_t *__restrict__ part, int64_t nparts, int B,
-                                                             int32_t *__restrict__ idx, float *__restrict__ val) {
-    const int b = blockIdx.x;
+// Argmax over each batch row of y [B][N] -> (index, value). A grid of (G, B)
+// workgroups: each takes every G-th stretch of 4096 values of its row, four
+// independent loads per thread and step, keeps the largest key (value order,
+// then the lower row), and merges it into the header word of its row with a
+// 64-bit atomic max. The last workgroup to finish (by the header counter,
+// zeroed by the matvec launch before) turns the maxima into (index, value).
+__global__ __launch_bounds__(1024) void argmax_rows_kernel(const float *__restrict__ y, int64_t N, int B,
+                                                           uint64_t *__restrict__ hdr, int32_t *__restrict__ idx,
+                                                           float *__restrict__ val) {
+    const int b = blockIdx.y;
+    const int G = gridDim.x;
+    const float *yr = y + (int64_t)b * N;
     uint64_t k = 0;
-    for (int64_t i0 = threadIdx.x; i0 < nparts; i0 += 4 * 1024) {
-        uint64_t v[4];
+    for (int64_t i0 = (int64_t)blockIdx.x * 4096 + threadIdx.x; i0 < N; i0 += (int64_t)G * 4096) {
+        float v[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
             const int64_t i = i0 + u * 1024;
-            v[u] = i < nparts ? part[(i < nparts ? i : 0) * B + b] : 0;
+            v[u] = yr[i < N ? i : 0];
         }
 #pragma unroll
-        for (int u = 0; u < 4; u++) k = v[u] > k ? v[u] : k;
+        for (int u = 0; u < 4; u++) {
+            const int64_t i = i0 + u * 1024;
+            const uint64_t key = i < N ? argmax_key(v[u], i) : 0;
+            k = key > k ? key : k;
+        }
     }
     k = wave_max_u64(k);
     __shared__ uint64_t red[16];
+    __shared__ int last;
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int w = 0; w < 16; w++) k = red[w] > k ? red[w] : k;
-        const uint32_t hi = (uint32_t)(k >> 32);
+        __hip_atomic_fetch_max(&hdr[b], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t done = __hip_atomic_fetch_add(&hdr[8], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        last = done + 1 == (uint64_t)G * (uint64_t)B;
+    }
+    __syncthreads();
+    if (last && (int)threadIdx.x < B) {
+        const uint64_t kk = __hip_atomic_load(&hdr[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t hi = (uint32_t)(kk >> 32);
         const uint32_t bits = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
-        idx[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)k);
-        val[b] = __builtin_bit_cast(float, bits);
+        idx[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+        val[threadIdx.x] = __builtin_bit_cast(float, bits);
     }
 }
 
@@ -509,41 +509,31 @@ template <int FMT, int BT, bool TALL = false> struct LaunchShape {
     static constexpr int WAVES = (FMT == KM4 || FMT == INT8KM) ? 1 : 4;
 };
 
-// The argmax epilogue writes one key per wave: waves cover 4x more rows (at
-// least 16) so the reduction that follows reads few keys.
-template <int FMT, int BT, bool ARGMAX, bool TALL = false> struct ShapeFor : LaunchShape<FMT, BT, TALL> {
-    static constexpr int ITERS = ARGMAX ? 4 * LaunchShape<FMT, BT, TALL>::ITERS : LaunchShape<FMT, BT, TALL>::ITERS;
-};
-
-template <int FMT, int BT, int LPR, int CPL, bool ARGMAX, bool OUTL, bool TALL>
+template <int FMT, int BT, int LPR, int CPL, bool OUTL, bool TALL>
 static hipError_t launch_shape(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                               float *y, hipStream_t st, uint64_t *part, int64_t *nparts, OutlierArgs ol) {
-    using S = ShapeFor<FMT, BT, ARGMAX, TALL>;
+                               float *y, hipStream_t st, uint64_t *hdr, OutlierArgs ol) {
+    using S = LaunchShape<FMT, BT, TALL>;
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
-    if (nparts) *nparts = grid * S::WAVES;
     const int cpr = (FMT == INT8 || FMT == INT8KM) ? K / 16 : K / 32;
     if (cpr == LPR * CPL)
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, ARGMAX, OUTL>),
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, true, OUTL>),
                            dim3((unsigned)grid), dim3(64 * S::WAVES), 0, st, codes, plane, N, K,
-                           reinterpret_cast<const _Float16 *>(x), B, y, part, ol);
+                           reinterpret_cast<const _Float16 *>(x), B, y, hdr, ol);
     else
-        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false, ARGMAX, OUTL>),
+        hipLaunchKernelGGL((mv_fast<FMT, BT, LPR, CPL, S::R, S::ITERS, S::WAVES, false, OUTL>),
                            dim3((unsigned)grid), dim3(64 * S::WAVES), 0, st, codes, plane, N, K,
-                           reinterpret_cast<const _Float16 *>(x), B, y, part, ol);
+                           reinterpret_cast<const _Float16 *>(x), B, y, hdr, ol);
     return hipGetLastError();
 }
 
-// the argmax epilogue keeps its shorter shape: more waves, shorter key lists per wave
-template <int FMT, int BT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
+template <int FMT, int BT, int LPR, int CPL, bool OUTL = false>
 static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                              float *y, hipStream_t st, uint64_t *part = nullptr, int64_t *nparts = nullptr,
-                              OutlierArgs ol = OutlierArgs()) {
-    if constexpr (BT == 1 && !ARGMAX) {
-        if (N >= kTallRows)
-            return launch_shape<FMT, BT, LPR, CPL, ARGMAX, OUTL, true>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+                              float *y, hipStream_t st, uint64_t *hdr = nullptr, OutlierArgs ol = OutlierArgs()) {
+    if constexpr (BT == 1) {
+        if (N >= kTallRows) return launch_shape<FMT, BT, LPR, CPL, OUTL, true>(codes, plane, N, K, x, B, y, st, hdr, ol);
     }
-    return launch_shape<FMT, BT, LPR, CPL, ARGMAX, OUTL, false>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+    return launch_shape<FMT, BT, LPR, CPL, OUTL, false>(codes, plane, N, K, x, B, y, st, hdr, ol);
 }
 
 // Register budget for the x slices held per lane (CPL * BT * XW words): the
@@ -554,19 +544,19 @@ constexpr bool dot2_takes(int B) {
     return B <= 2 || (B <= 4 && CPL * 4 * XW <= 128) || (B <= 8 && CPL * 8 * XW <= 128);
 }
 
-template <int FMT, int LPR, int CPL, bool ARGMAX = false, bool OUTL = false>
+template <int FMT, int LPR, int CPL, bool OUTL = false>
 static hipError_t dispatch_b(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                             float *y, hipStream_t st, bool *handled, uint64_t *part = nullptr,
-                             int64_t *nparts = nullptr, OutlierArgs ol = OutlierArgs()) {
+                             float *y, hipStream_t st, bool *handled, uint64_t *hdr = nullptr,
+                             OutlierArgs ol = OutlierArgs()) {
     *handled = true;
     constexpr int XW = ChunkTraits<FMT>::kXWords;
-    if (B == 1) return launch_fast<FMT, 1, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
-    if (B == 2) return launch_fast<FMT, 2, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+    if (B == 1) return launch_fast<FMT, 1, LPR, CPL, OUTL>(codes, plane, N, K, x, B, y, st, hdr, ol);
+    if (B == 2) return launch_fast<FMT, 2, LPR, CPL, OUTL>(codes, plane, N, K, x, B, y, st, hdr, ol);
     if constexpr (CPL * 4 * XW <= 128) {
-        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+        if (B <= 4) return launch_fast<FMT, 4, LPR, CPL, OUTL>(codes, plane, N, K, x, B, y, st, hdr, ol);
     }
     if constexpr (CPL * 8 * XW <= 128) {
-        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL, ARGMAX, OUTL>(codes, plane, N, K, x, B, y, st, part, nparts, ol);
+        if (B <= 8) return launch_fast<FMT, 8, LPR, CPL, OUTL>(codes, plane, N, K, x, B, y, st, hdr, ol);
     }
     *handled = false;
     return hipSuccess;
@@ -601,8 +591,8 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
-// Fused matvec + argmax: the dot2 kernel with the ARGMAX epilogue writes one
-// key per wave and batch row, then one workgroup per batch row reduces them.
+// Fused matvec + argmax: the dot2 matvec writes y into the workspace (and
+// zeroes the header), then a grid of workgroups takes the argmax of each row.
 // ---------------------------------------------------------------------------
 template <int FMT>
 static bool argmax_shape(int K, int B, int *lpr, int *cpl) {
@@ -633,43 +623,44 @@ bool argmax_supported(int fmt, int64_t K, int B) {
     }
 }
 
-// every argmax launch shape covers at least 16 rows per wave; the last
-// workgroup may hold up to 4 waves past the end
+// the header, then y [B][N] fp32 of the dot2 matvec
 size_t argmax_workspace_bytes(int64_t N, int B) {
-    return (size_t)((N + 15) / 16 + 4) * (size_t)B * sizeof(uint64_t);
+    return (size_t)kArgmaxHeader * sizeof(uint64_t) + (((size_t)N * (size_t)B * sizeof(float) + 15) / 16) * 16;
 }
 
 template <int FMT>
 static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                             int32_t *idx, float *val, uint64_t *part, hipStream_t st) {
+                             int32_t *idx, float *val, uint64_t *ws, hipStream_t st) {
+    float *yw = reinterpret_cast<float *>(ws + kArgmaxHeader);
     int lpr = 0, cpl = 0;
     if (!argmax_shape<FMT>(K, B, &lpr, &cpl)) return hipErrorInvalidValue;
     bool handled = false;
-    int64_t nparts = 0;
     hipError_t err;
-    if (lpr == 16) err = dispatch_b<FMT, 16, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
-    else if (lpr == 32) err = dispatch_b<FMT, 32, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
-    else if (cpl == 1) err = dispatch_b<FMT, 64, 1, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
-    else if (cpl == 2) err = dispatch_b<FMT, 64, 2, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
-    else if (cpl == 3) err = dispatch_b<FMT, 64, 3, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
-    else err = dispatch_b<FMT, 64, 4, true>(codes, plane, N, K, x, B, nullptr, st, &handled, part, &nparts);
+    if (lpr == 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    else if (lpr == 32) err = dispatch_b<FMT, 32, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    else if (cpl == 1) err = dispatch_b<FMT, 64, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    else if (cpl == 2) err = dispatch_b<FMT, 64, 2>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    else if (cpl == 3) err = dispatch_b<FMT, 64, 3>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    else err = dispatch_b<FMT, 64, 4>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     if (err != hipSuccess) return err;
     if (!handled) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(argmax_reduce_kernel, dim3(B), dim3(1024), 0, st, part, nparts, B, idx, val);
+    const int64_t g = (N + 4095) / 4096;
+    const dim3 grid((unsigned)(g < 1 ? 1 : (g > 64 ? 64 : g)), (unsigned)B);
+    hipLaunchKernelGGL(argmax_rows_kernel, grid, dim3(1024), 0, st, yw, N, B, ws, idx, val);
     return hipGetLastError();
 }
 
 hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                                 int B, int32_t *idx, float *val, void *workspace, hipStream_t st) {
     const uint8_t *c = reinterpret_cast<const uint8_t *>(codes);
-    uint64_t *part = reinterpret_cast<uint64_t *>(workspace);
+    uint64_t *ws = reinterpret_cast<uint64_t *>(workspace);
     switch (fmt) {
-    case INT4: return argmax_fmt<INT4>(c, plane, N, (int)K, x, B, idx, val, part, st);
-    case INT4AFF: return argmax_fmt<INT4AFF>(c, plane, N, (int)K, x, B, idx, val, part, st);
-    case INT8KM: return argmax_fmt<INT8KM>(c, plane, N, (int)K, x, B, idx, val, part, st);
-    case FP4: return argmax_fmt<FP4>(c, plane, N, (int)K, x, B, idx, val, part, st);
-    case INT8: return argmax_fmt<INT8>(c, plane, N, (int)K, x, B, idx, val, part, st);
-    default: return argmax_fmt<KM4>(c, plane, N, (int)K, x, B, idx, val, part, st);
+    case INT4: return argmax_fmt<INT4>(c, plane, N, (int)K, x, B, idx, val, ws, st);
+    case INT4AFF: return argmax_fmt<INT4AFF>(c, plane, N, (int)K, x, B, idx, val, ws, st);
+    case INT8KM: return argmax_fmt<INT8KM>(c, plane, N, (int)K, x, B, idx, val, ws, st);
+    case FP4: return argmax_fmt<FP4>(c, plane, N, (int)K, x, B, idx, val, ws, st);
+    case INT8: return argmax_fmt<INT8>(c, plane, N, (int)K, x, B, idx, val, ws, st);
+    default: return argmax_fmt<KM4>(c, plane, N, (int)K, x, B, idx, val, ws, st);
     }
 }
 
@@ -700,10 +691,10 @@ hipError_t launch_matvec_km4o(const uint8_t *codes, const uint16_t *lut, const u
     bool handled = false;
     hipError_t err = hipSuccess;
     if (xdt == QMV_F16) {
-        if (cpr <= 16) err = dispatch_b<KM4, 16, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
-        else if (cpr <= 32) err = dispatch_b<KM4, 32, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
-        else if (cpr <= 64) err = dispatch_b<KM4, 64, 1, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
-        else if (cpr <= 128) err = dispatch_b<KM4, 64, 2, false, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, nullptr, ol);
+        if (cpr <= 16) err = dispatch_b<KM4, 16, 1, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, ol);
+        else if (cpr <= 32) err = dispatch_b<KM4, 32, 1, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, ol);
+        else if (cpr <= 64) err = dispatch_b<KM4, 64, 1, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, ol);
+        else if (cpr <= 128) err = dispatch_b<KM4, 64, 2, true>(codes, lut, N, k, x, B, y, st, &handled, nullptr, ol);
         if (handled) return err;
     }
     const int grid = grid_for_waves(N);
