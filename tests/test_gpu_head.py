@@ -72,6 +72,26 @@ def test_lm_head_argmax_full_size_fp4():
         _check_argmax(host(idx), host(val), ref)
 
 
+def test_argmax_past_the_first_stretch_of_each_workgroup():
+    """270000 rows: more than 64 x 4096, so reduction workgroups take several
+    stretches. Token 0 wins at row 263000 (a later stretch of the first
+    workgroup), token 1 ties between rows 5 and 269990 (lowest row wins),
+    token 2 wins at the last row."""
+    N, K = 270000, 64
+    rng = np.random.default_rng(31)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float16)
+    x = rng.standard_normal((3, K)).astype(np.float16)
+    W[263000] = (np.sign(x[0]) * 0.06).astype(np.float16)
+    W[5] = W[269990] = (np.sign(x[1]) * 0.07).astype(np.float16)
+    W[N - 1] = (np.sign(x[2]) * 0.08).astype(np.float16)
+    codes, plane = oracle.pack("fp4", W)
+    ref = oracle.matvec("fp4", codes, plane, x)
+    idx, val = qmv.qmatvec_argmax("fp4", dev(codes), dev(plane), dev(x))
+    idx, val = host(idx), host(val)
+    _check_argmax(idx, val, ref)
+    assert idx.tolist() == [263000, 5, N - 1]
+
+
 def test_argmax_replays_in_a_hip_graph():
     import torch
     c = wl.small_dense("km4", 4000, 2048, batch=2, seed=9)
