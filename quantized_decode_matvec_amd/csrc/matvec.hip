@@ -499,20 +499,35 @@ static int grid_for_waves(int64_t waves_needed) {
 // more rows per wave to amortize the x slices held in registers. TALL (batch
 // 1, at least kTallRows rows): 8 rows per wave for the table formats and
 // affine int4, which halves the x slice loads per row; shorter matrices keep
-// 4 so that enough waves fill the chip.
+// 4 so that enough waves fill the chip, and fewer as rows get longer (RS,
+// see short_rows).
 constexpr int64_t kTallRows = 32768;
-template <int FMT, int BT, bool TALL = false> struct LaunchShape {
-    static constexpr int R = (BT == 1) ? ((FMT == INT4 || (TALL && FMT != FP4 && FMT != INT8)) ? 8 : 4)
+template <int FMT, int BT, bool TALL = false, int RS = 0> struct LaunchShape {
+    static constexpr int R = (BT == 1 && RS > 0) ? RS
+                           : (BT == 1) ? ((FMT == INT4 || (TALL && FMT != FP4 && FMT != INT8)) ? 8 : 4)
                                        : (BT == 2 ? 4 : (BT == 4 ? ((FMT == KM4) ? 4 : 2) : 1));
     static constexpr int ITERS = (FMT == KM4 || FMT == INT8KM) ? ((BT == 1) ? 1 : (BT == 8 ? 16 : 2))
                                               : ((BT == 1) ? 1 : (BT == 2 ? 2 : (BT == 4 ? 4 : 8)));
     static constexpr int WAVES = (FMT == KM4 || FMT == INT8KM) ? 1 : 4;
 };
 
-template <int FMT, int BT, int LPR, int CPL, bool OUTL, bool TALL>
+// Batch 1, fewer than kTallRows rows of at least 1 KiB (4-bit K >= 2048): rows
+// per wave by row length, measured on q/o-projection shapes in HIP graphs
+// (2048 x 4096: km4 3.75 us at 1 row against 4.89 at 4; fp4 2.78 at 2 against
+// 3.75; int4 3.19 at 1 against 4.45 at 8. 4096 x 2048: km4 3.56 at 2 against
+// 3.85; int4 3.01 at 4 against 3.32). 0 keeps the LaunchShape default.
+template <int FMT>
+static int short_rows(int64_t row_bytes) {
+    if constexpr (FMT == KM4) return row_bytes >= 2048 ? 1 : (row_bytes >= 1024 ? 2 : 0);
+    else if constexpr (FMT == FP4) return row_bytes >= 2048 ? 2 : 0;
+    else if constexpr (FMT == INT4 || FMT == INT4AFF) return row_bytes >= 2048 ? 1 : (row_bytes >= 1024 ? 4 : 0);
+    else return 0;
+}
+
+template <int FMT, int BT, int LPR, int CPL, bool OUTL, bool TALL, int RS = 0>
 static hipError_t launch_shape(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
                                float *y, hipStream_t st, uint64_t *hdr, OutlierArgs ol) {
-    using S = LaunchShape<FMT, BT, TALL>;
+    using S = LaunchShape<FMT, BT, TALL, RS>;
     constexpr int ROWS_WG = S::WAVES * S::R * S::ITERS * (kWave / LPR);
     int64_t grid = (N + ROWS_WG - 1) / ROWS_WG;
     const int cpr = (FMT == INT8 || FMT == INT8KM) ? K / 16 : K / 32;
@@ -532,6 +547,12 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
                               float *y, hipStream_t st, uint64_t *hdr = nullptr, OutlierArgs ol = OutlierArgs()) {
     if constexpr (BT == 1) {
         if (N >= kTallRows) return launch_shape<FMT, BT, LPR, CPL, OUTL, true>(codes, plane, N, K, x, B, y, st, hdr, ol);
+        if constexpr (LPR == 64) {
+            const int rs = short_rows<FMT>((FMT == INT8 || FMT == INT8KM) ? (int64_t)K : (int64_t)K / 2);
+            if (rs == 1) return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);
+            if (rs == 2) return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 2>(codes, plane, N, K, x, B, y, st, hdr, ol);
+            if (rs == 4) return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 4>(codes, plane, N, K, x, B, y, st, hdr, ol);
+        }
     }
     return launch_shape<FMT, BT, LPR, CPL, OUTL, false>(codes, plane, N, K, x, B, y, st, hdr, ol);
 }
