@@ -320,7 +320,14 @@ def main():
         ms2 = timed(two_step, args.steps, args.warmup)
         extras["km4_argmax_fused_us"] = round(msa * 1e3, 2)
         extras["km4_matvec_then_argmax_us"] = round(ms2 * 1e3, 2)
-        del ws
+        # batch 8: the matrix-core matvec then the argmax launch
+        ws8 = torch.empty((qmv.qmatvec_argmax_workspace_bytes(N_ROWS, 8),), dtype=torch.uint8, device="cuda")
+        aidx8 = torch.empty((8,), dtype=torch.int32, device="cuda")
+        aval8 = torch.empty((8,), dtype=torch.float32, device="cuda")
+        msa8 = timed(lambda i: qmv.qmatvec_argmax("km4", copies[i % len(copies)][0], copies[i % len(copies)][1], x8,
+                                                  idx=aidx8, val=aval8, workspace=ws8), max(10, args.steps // 4), 5)
+        extras["km4_argmax_fused_B8_us"] = round(msa8 * 1e3, 2)
+        del ws, ws8
         # int8 embedding dequant-gather from a table of the same shape, 8 tokens (HIP graphs)
         tq, ts = qmv.qpack_int8_rows(W)
         gids = torch.randint(0, N_ROWS, (8,), dtype=torch.int32, device="cuda",

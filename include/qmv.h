@@ -272,8 +272,9 @@ size_t qmatvec_argmax_workspace_bytes(int64_t N, int B);
 /* Fused matvec + argmax: for each batch row b, idx[b] = the row n with the
  * largest y[b][n] = sum_k dequant(W)[n][k] * x[b][k] (fp32 accumulation, as
  * qmatvec_*), the lowest n among equal largest values, and val[b] = that
- * y[b][n]. The matvec writes y into the workspace (the caller allocates no
- * logits) and a second launch takes each row's argmax. codes/plane as for
+ * y[b][n]. The matvec (the kernel qmatvec_* runs for the shape, so y is
+ * bit-identical to its output) writes y into the workspace (the caller
+ * allocates no logits) and a second launch takes each row's argmax. codes/plane as for
  * qmatvec_* of `fmt`; x fp16 [B][K]; idx int32 [B]; val fp32 [B]; NaN
  * values are not ordered. 1 <= B <= 8; the shapes of the batch-1..8 dot
  * product path (K multiple of 32, up to 8192 for 4-bit formats and 4096

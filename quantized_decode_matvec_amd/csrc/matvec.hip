@@ -612,9 +612,15 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
-// Fused matvec + argmax: the dot2 matvec writes y into the workspace (and
-// zeroes the header), then a grid of workgroups takes the argmax of each row.
+// Fused matvec + argmax: the matvec writes y into the workspace, then a grid
+// of workgroups takes the argmax of each row. The matvec is the one the plain
+// entry point would run for the shape: the dot2 kernel zeroes the header as
+// it goes; after a matrix-core matvec a one-wave kernel zeroes it.
 // ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void argmax_header_zero(uint64_t *__restrict__ hdr) {
+    if (threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
+}
+
 template <int FMT>
 static bool argmax_shape(int K, int B, int *lpr, int *cpl) {
     const int cpr = K / ChunkTraits<FMT>::kElems;
@@ -656,8 +662,11 @@ static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N,
     int lpr = 0, cpl = 0;
     if (!argmax_shape<FMT>(K, B, &lpr, &cpl)) return hipErrorInvalidValue;
     bool handled = false;
-    hipError_t err;
-    if (lpr == 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
+    hipError_t err = launch_matvec_mfma(FMT, codes, plane, N, K, x, B, yw, st, &handled);
+    if (handled) {
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(argmax_header_zero, dim3(1), dim3(64), 0, st, ws);
+    } else if (lpr == 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     else if (lpr == 32) err = dispatch_b<FMT, 32, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     else if (cpl == 1) err = dispatch_b<FMT, 64, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     else if (cpl == 2) err = dispatch_b<FMT, 64, 2>(codes, plane, N, K, x, B, yw, st, &handled, ws);
@@ -665,6 +674,7 @@ static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N,
     else err = dispatch_b<FMT, 64, 4>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     if (err != hipSuccess) return err;
     if (!handled) return hipErrorInvalidValue;
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     const int64_t g = (N + 4095) / 4096;
     const dim3 grid((unsigned)(g < 1 ? 1 : (g > 64 ? 64 : g)), (unsigned)B);
     hipLaunchKernelGGL(argmax_rows_kernel, grid, dim3(1024), 0, st, yw, N, B, ws, idx, val);

@@ -53,19 +53,20 @@ def test_matvec_argmax_parity(fmt, N, K, Bs):
             assert idx[0] == N // 3
             if B > 1:
                 assert idx[1] == 11
-        # the same rows through the plain matvec give the same winner and value
+        # the fused call runs the plain matvec's kernel for the shape (dot2 or
+        # matrix cores), so it gives the same winner and value
         y = host(qmv.qmatvec(fmt, dc, dp, dev(x[:B])))
-        if B < 3:   # the plain matvec takes the matrix-core path at B >= 3
-            assert np.array_equal(idx, np.argmax(y, axis=1))
-            assert np.array_equal(val, y[np.arange(B), idx])
+        assert np.array_equal(idx, np.argmax(y, axis=1))
+        assert np.array_equal(val, y[np.arange(B), idx])
 
 
 def test_lm_head_argmax_full_size_fp4():
-    """248320 x 2048 (the lm_head shape), fp4, batch 1 and 4."""
+    """248320 x 2048 (the lm_head shape), fp4, batch 1 (dot2 matvec), 4 and 8
+    (matrix-core matvec)."""
     c = wl.lm_head_km4()
     codes, plane = oracle.pack("fp4", c.W)
     dc, dp = dev(codes), dev(plane)
-    for B in (1, 4):
+    for B in (1, 4, 8):
         print("lm_head argmax fp4 B", B, flush=True)
         ref = oracle.matvec("fp4", codes, plane, c.x[:B])
         idx, val = qmv.qmatvec_argmax("fp4", dc, dp, dev(c.x[:B]))
@@ -92,14 +93,17 @@ def test_argmax_past_the_first_stretch_of_each_workgroup():
     assert idx.tolist() == [263000, 5, N - 1]
 
 
-def test_argmax_replays_in_a_hip_graph():
+@pytest.mark.parametrize("B", [2, 6])
+def test_argmax_replays_in_a_hip_graph(B):
+    """Batch 2 (the dot2 matvec zeroes the header) and 6 (a matrix-core matvec
+    and the header-zeroing kernel)."""
     import torch
-    c = wl.small_dense("km4", 4000, 2048, batch=2, seed=9)
+    c = wl.small_dense("km4", 4000, 2048, batch=B, seed=9)
     codes, plane = oracle.pack("km4", c.W)
     dc, dp, xd = dev(codes), dev(plane), dev(c.x)
-    idx = torch.empty((2,), dtype=torch.int32, device="cuda")
-    val = torch.empty((2,), dtype=torch.float32, device="cuda")
-    ws = torch.empty((qmv.qmatvec_argmax_workspace_bytes(4000, 2),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B,), dtype=torch.int32, device="cuda")
+    val = torch.empty((B,), dtype=torch.float32, device="cuda")
+    ws = torch.empty((qmv.qmatvec_argmax_workspace_bytes(4000, B),), dtype=torch.uint8, device="cuda")
     qmv.qmatvec_argmax("km4", dc, dp, xd, idx=idx, val=val, workspace=ws)
     torch.cuda.synchronize()
     ref = (host(idx).copy(), host(val).copy())
