@@ -28,6 +28,11 @@ CASES = [
     (6, 64, 2048, 2, 2),
     (300, 64, 32, 4, 8),
     (1500, 64, 32, 2, 8),
+    # one token at hidden sizes 1280..2048 (several slots, the down rows of
+    # 16 and 32 lanes)
+    (10, 2048, 512, 1, 8),
+    (12, 1536, 256, 1, 6),
+    (8, 1280, 1024, 1, 4),
 ]
 
 
@@ -142,12 +147,12 @@ def test_route_nan_logits_rank_last():
     assert np.allclose(w, ow, rtol=1e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("T", [1, 4])
-def test_moe_ffn_replays_identically_in_a_hip_graph(T):
+@pytest.mark.parametrize("T,E,H,I,topk", [(1, 16, 256, 128, 3), (4, 16, 256, 128, 3), (1, 10, 2048, 512, 8)])
+def test_moe_ffn_replays_identically_in_a_hip_graph(T, E, H, I, topk):
     """qmoe_ffn allocates nothing and never synchronizes, so it can be
     captured; each replay (with eager work between) equals the eager call."""
     import torch
-    fmt, E, H, I, topk = "km4", 16, 256, 128, 3
+    fmt = "km4"
     guc, gup, dnc, dnp, x, logits = _case(fmt, E, H, I, T, topk, seed=5)
     d = [dev(a) for a in (guc, gup, dnc, dnp)]
     xd, ld = dev(x), dev(logits)
