@@ -31,7 +31,7 @@ namespace qmv {
 // of the row index, so the largest key is the largest value and, among equal
 // values, the lowest row. Every finite value gives a key above 0.
 // argmax workspace: kArgmaxHeader 64-bit words (maxima of batch rows 0..7,
-// then the reduction's workgroup counter) before the per-wave keys
+// then the reduction's workgroup counter) before y [B][N] fp32
 constexpr int kArgmaxHeader = 16;
 
 __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
