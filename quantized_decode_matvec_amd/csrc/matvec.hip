@@ -30,9 +30,7 @@ namespace qmv {
 // Argmax keys: the fp32 value in order-preserving form above the complement
 // of the row index, so the largest key is the largest value and, among equal
 // values, the lowest row. Every finite value gives a key above 0.
-// argmax workspace: kArgmaxHeader 64-bit words (maxima of batch rows 0..7,
-// then the reduction's workgroup counter) before y [B][N] fp32
-constexpr int kArgmaxHeader = 16;
+// argmax workspace: the kArgmaxHeader-word header, then y [B][N] fp32
 
 __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
     uint32_t b = __builtin_bit_cast(uint32_t, v);
@@ -305,8 +303,10 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
 // workgroups: each takes every G-th stretch of 4096 values of its row, four
 // independent loads per thread and step, keeps the largest key (value order,
 // then the lower row), and merges it into the header word of its row with a
-// 64-bit atomic max. The last workgroup to finish (by the header counter,
-// zeroed by the matvec launch before) turns the maxima into (index, value).
+// 64-bit atomic max. The last of a row's G workgroups to finish (by the row's
+// header counter, zeroed by the matvec launch before) turns that row's
+// maximum into (index, value); one counter per row keeps the rows'
+// same-address atomics apart.
 __global__ __launch_bounds__(1024) void argmax_rows_kernel(const float *__restrict__ y, int64_t N, int B,
                                                            uint64_t *__restrict__ hdr, int32_t *__restrict__ idx,
                                                            float *__restrict__ val) {
@@ -330,22 +330,19 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const float *__restri
     }
     k = wave_max_u64(k);
     __shared__ uint64_t red[16];
-    __shared__ int last;
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int w = 0; w < 16; w++) k = red[w] > k ? red[w] : k;
         __hip_atomic_fetch_max(&hdr[b], k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t done = __hip_atomic_fetch_add(&hdr[8], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = done + 1 == (uint64_t)G * (uint64_t)B;
-    }
-    __syncthreads();
-    if (last && (int)threadIdx.x < B) {
-        const uint64_t kk = __hip_atomic_load(&hdr[threadIdx.x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t hi = (uint32_t)(kk >> 32);
-        const uint32_t bits = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
-        idx[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-        val[threadIdx.x] = __builtin_bit_cast(float, bits);
+        const uint64_t done = __hip_atomic_fetch_add(&hdr[8 + b], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        if (done + 1 == (uint64_t)G) {
+            const uint64_t kk = __hip_atomic_load(&hdr[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t hi = (uint32_t)(kk >> 32);
+            const uint32_t bits = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
+            idx[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
+            val[b] = __builtin_bit_cast(float, bits);
+        }
     }
 }
 
@@ -612,15 +609,11 @@ static hipError_t matvec_fmt(const uint8_t *codes, const void *plane, int64_t N,
 }
 
 // ---------------------------------------------------------------------------
-// Fused matvec + argmax: the matvec writes y into the workspace, then a grid
-// of workgroups takes the argmax of each row. The matvec is the one the plain
-// entry point would run for the shape: the dot2 kernel zeroes the header as
-// it goes; after a matrix-core matvec a one-wave kernel zeroes it.
+// Fused matvec + argmax: the matvec writes y into the workspace and zeroes
+// the header, then a grid of workgroups takes the argmax of each row. The
+// matvec is the one the plain entry point would run for the shape (dot2 or
+// matrix cores).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void argmax_header_zero(uint64_t *__restrict__ hdr) {
-    if (threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
-}
-
 template <int FMT>
 static bool argmax_shape(int K, int B, int *lpr, int *cpl) {
     const int cpr = K / ChunkTraits<FMT>::kElems;
@@ -662,10 +655,9 @@ static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N,
     int lpr = 0, cpl = 0;
     if (!argmax_shape<FMT>(K, B, &lpr, &cpl)) return hipErrorInvalidValue;
     bool handled = false;
-    hipError_t err = launch_matvec_mfma(FMT, codes, plane, N, K, x, B, yw, st, &handled);
+    hipError_t err = launch_matvec_mfma(FMT, codes, plane, N, K, x, B, yw, st, &handled, ws);
     if (handled) {
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL(argmax_header_zero, dim3(1), dim3(64), 0, st, ws);
     } else if (lpr == 16) err = dispatch_b<FMT, 16, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     else if (lpr == 32) err = dispatch_b<FMT, 32, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);
     else if (cpl == 1) err = dispatch_b<FMT, 64, 1>(codes, plane, N, K, x, B, yw, st, &handled, ws);

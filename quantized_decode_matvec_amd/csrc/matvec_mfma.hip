@@ -206,8 +206,10 @@ template <int FMT, int RG, int SP, int D, bool LDS_CODES>
 __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__restrict__ codes,
                                                           const void *__restrict__ plane, int64_t N, int K,
                                                           const _Float16 *__restrict__ x, int B,
-                                                          float *__restrict__ y) {
+                                                          float *__restrict__ y, uint64_t *__restrict__ hdr) {
     extern __shared__ __align__(16) _Float16 xs[];
+    // fused argmax: the first workgroup zeroes the reduction header
+    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
     constexpr bool BYTES = (FMT == INT8 || FMT == INT8KM);   // one code per byte
     constexpr bool TABLE = (FMT == KM4 || FMT == INT8KM);   // no block scales
     constexpr int MPJ = BYTES ? 2 : 4;                      // blocks (MFMAs) per j-step
@@ -487,7 +489,7 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
 
 template <int FMT, int SP, int RG>
 static hipError_t launch_mfma_rg(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                                 float *y, hipStream_t st) {
+                                 float *y, hipStream_t st, uint64_t *hdr) {
     constexpr int D = 2;
     const int64_t rows_wg = (int64_t)kMfmaWaves * RG * 16;
     const int64_t grid = (N + rows_wg - 1) / rows_wg;
@@ -499,7 +501,7 @@ static hipError_t launch_mfma_rg(const uint8_t *codes, const void *plane, int64_
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((mv_mfma<FMT, RG, SP, D, kLdsCodes>), dim3((unsigned)grid), dim3(64 * kMfmaWaves), lds, st,
-                       codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y);
+                       codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y, hdr);
     return hipGetLastError();
 }
 
@@ -509,34 +511,34 @@ static hipError_t launch_mfma_rg(const uint8_t *codes, const void *plane, int64_
 // 248320-row lm_head with eight.
 template <int FMT, int SP>
 static hipError_t launch_mfma_sp(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                                 float *y, hipStream_t st) {
+                                 float *y, hipStream_t st, uint64_t *hdr) {
     const int64_t per_rg1 = (int64_t)kMfmaWaves * 16 * 512;   // rows that give 512 workgroups at RG = 1
-    if (N >= 6 * per_rg1) return launch_mfma_rg<FMT, SP, 8>(codes, plane, N, K, x, B, y, st);
-    if (N >= 3 * per_rg1) return launch_mfma_rg<FMT, SP, 4>(codes, plane, N, K, x, B, y, st);
-    if (N >= (3 * per_rg1) / 2) return launch_mfma_rg<FMT, SP, 2>(codes, plane, N, K, x, B, y, st);
-    return launch_mfma_rg<FMT, SP, 1>(codes, plane, N, K, x, B, y, st);
+    if (N >= 6 * per_rg1) return launch_mfma_rg<FMT, SP, 8>(codes, plane, N, K, x, B, y, st, hdr);
+    if (N >= 3 * per_rg1) return launch_mfma_rg<FMT, SP, 4>(codes, plane, N, K, x, B, y, st, hdr);
+    if (N >= (3 * per_rg1) / 2) return launch_mfma_rg<FMT, SP, 2>(codes, plane, N, K, x, B, y, st, hdr);
+    return launch_mfma_rg<FMT, SP, 1>(codes, plane, N, K, x, B, y, st, hdr);
 }
 
 template <int FMT>
 static hipError_t launch_mfma_fmt(const uint8_t *codes, const void *plane, int64_t N, int K, const void *x, int B,
-                                  float *y, hipStream_t st) {
+                                  float *y, hipStream_t st, uint64_t *hdr) {
     const int sp = scale_pieces<FMT>(K);
-    if (sp <= 1) return launch_mfma_sp<FMT, 1>(codes, plane, N, K, x, B, y, st);
-    if (sp <= 2) return launch_mfma_sp<FMT, 2>(codes, plane, N, K, x, B, y, st);
-    return launch_mfma_sp<FMT, 4>(codes, plane, N, K, x, B, y, st);
+    if (sp <= 1) return launch_mfma_sp<FMT, 1>(codes, plane, N, K, x, B, y, st, hdr);
+    if (sp <= 2) return launch_mfma_sp<FMT, 2>(codes, plane, N, K, x, B, y, st, hdr);
+    return launch_mfma_sp<FMT, 4>(codes, plane, N, K, x, B, y, st, hdr);
 }
 
 hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
-                              int B, float *y, hipStream_t st, bool *handled) {
+                              int B, float *y, hipStream_t st, bool *handled, uint64_t *hdr) {
     *handled = mfma_eligible(fmt, plane, N, K, B);
     if (!*handled) return hipSuccess;
     switch (fmt) {
-    case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st);
-    case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st);
-    case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st);
-    case INT8: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st);
-    case INT8KM: return launch_mfma_fmt<INT8KM>(codes, plane, N, (int)K, x, B, y, st);
-    default: return launch_mfma_fmt<KM4>(codes, plane, N, (int)K, x, B, y, st);
+    case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st, hdr);
+    case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st, hdr);
+    case FP4: return launch_mfma_fmt<FP4>(codes, plane, N, (int)K, x, B, y, st, hdr);
+    case INT8: return launch_mfma_fmt<INT8>(codes, plane, N, (int)K, x, B, y, st, hdr);
+    case INT8KM: return launch_mfma_fmt<INT8KM>(codes, plane, N, (int)K, x, B, y, st, hdr);
+    default: return launch_mfma_fmt<KM4>(codes, plane, N, (int)K, x, B, y, st, hdr);
     }
 }
 

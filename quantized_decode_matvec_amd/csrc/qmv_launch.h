@@ -16,8 +16,11 @@ int device_cu_count();   // compute units of the current device (cached per devi
 hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                          qmv_dtype xdt, int B, float *y, hipStream_t st);
 // batched matrix-core path; *handled is false when the shape is not one it takes
+// Fused argmax workspace header: 64-bit words, the maxima of batch rows 0..7
+// then one workgroup counter per batch row; a matvec given `hdr` zeroes them.
+constexpr int kArgmaxHeader = 16;
 hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
-                              int B, float *y, hipStream_t st, bool *handled);
+                              int B, float *y, hipStream_t st, bool *handled, uint64_t *hdr = nullptr);
 bool argmax_supported(int fmt, int64_t K, int B);
 size_t argmax_workspace_bytes(int64_t N, int B);
 hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,

@@ -95,8 +95,8 @@ def test_argmax_past_the_first_stretch_of_each_workgroup():
 
 @pytest.mark.parametrize("B", [2, 6])
 def test_argmax_replays_in_a_hip_graph(B):
-    """Batch 2 (the dot2 matvec zeroes the header) and 6 (a matrix-core matvec
-    and the header-zeroing kernel)."""
+    """Batch 2 (the dot2 matvec zeroes the reduction header) and 6 (the
+    matrix-core matvec zeroes it)."""
     import torch
     c = wl.small_dense("km4", 4000, 2048, batch=B, seed=9)
     codes, plane = oracle.pack("km4", c.W)
