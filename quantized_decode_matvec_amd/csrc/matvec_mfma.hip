@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
                 if (row < N) {
 #pragma unroll
                     for (int v = 0; v < 4; v++)
-                        if (4 * q + v < B) __builtin_nontemporal_store(acc[v], &y[(size_t)(4 * q + v) * N + row]);
+                        if (4 * q + v < B) y[(size_t)(4 * q + v) * N + row] = acc[v];
                 }
                 acc = f4{0.f, 0.f, 0.f, 0.f};
             }
