@@ -117,14 +117,16 @@ def test_matvec_parity(fmt, N, K, B):
 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("N,K,Bs", [(1000, 2048, (3, 5, 6, 7, 8)), (16, 512, (8,)), (17, 1536, (4, 8)),
-                                    (600, 4096, (3,)), (300, 3584, (8,)), (517, 640, (4,)), (260, 256, (8,))])
+                                    (600, 4096, (3,)), (300, 3584, (8,)), (517, 640, (4,)), (260, 256, (8,)),
+                                    (4113, 2048, (5, 8)), (4113, 1536, (8,))])
 def test_batched_matvec_parity(fmt, N, K, Bs):
     """The matrix-core batched path: several workgroups and a ragged last row
-    group, every batch width it takes, a single row group (N = 16) and one
-    plus a row, one load step per row (K = 512) and three (K = 1536), the
-    largest K it stages (4096, at B = 3); and shapes it hands to the dot2
-    path (x too large for its LDS stage at K = 3584, K = 640 not a multiple
-    of 512, int8 K = 256 taken but the 4-bit formats not)."""
+    group, every batch width it takes, a single row group (N = 16), one load
+    step per row (K = 512) and three (K = 1536, past 4096 rows), the largest K
+    it stages (4096, at B = 3); and shapes it hands to the dot2 path (up to
+    4096 rows of K 1025..2048 at B = 5-8 outside the table formats, x too
+    large for its LDS stage at K = 3584, K = 640 not a multiple of 512, int8
+    K = 256 taken but the 4-bit formats not)."""
     W, x = _case(fmt, N, K, B=8, seed=N + K)
     codes, plane = oracle.pack(fmt, W)
     dc, dp = dev(codes), dev(plane)
