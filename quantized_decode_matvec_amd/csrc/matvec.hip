@@ -553,7 +553,7 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
         }
     }
     constexpr bool TABLE = (FMT == KM4 || FMT == INT8KM);
-    if constexpr ((BT == 2 || BT == 4 || (BT == 8 && !TABLE)) && LPR == 64) {
+    if constexpr ((BT == 2 || BT == 4 || BT == 8) && LPR == 64) {
         // Batch 2-4 on fewer than kTallRows rows: one iteration per wave and
         // about 1024 waves, measured in HIP graphs against the tall-matrix
         // shape (fp4 4096 x 4096 at B = 4: 6.2 us with 4 rows per wave against
@@ -561,9 +561,10 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
         // against 9.5; int4 4096 x 2048 at B = 2: 3.5 us against 5.0). The
         // table formats (one wave per workgroup) take 2 rows: km4 2048 x 4096
         // at B = 4: 6.0 us against 8.8; int8 k-means 4096 x 2048: 5.1 against 6.5.
-        // Batch 5-8 (matrices the matrix-core path leaves here) takes 2 rows.
+        // Batch 5-8 (matrices the matrix-core path leaves here) takes 2 rows,
+        // km4 4 from 4096 rows (4096 x 2048 at B = 8: 6.4 us against 7.2).
         if (N < kTallRows) {
-            if (N >= 4096 && !TABLE && BT <= 4)
+            if (N >= 4096 && ((!TABLE && BT <= 4) || (FMT == KM4 && BT == 8)))
                 return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 4, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);
             if (N >= 2048) return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 2, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);
             return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 1, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);

@@ -476,10 +476,11 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     // 6.8 us against 7.4 us); from B = 5 the matrix cores win at any size
     if (B <= 4 && N < 16384) return false;
     // up to 4096 rows of one 1024-byte chunk per lane (4-bit K 1025..2048,
-    // int8 two chunks) the dot2 kernel at 2 rows per wave is faster at B = 5-8
-    // too (fp4 4096 x 2048: 5.9 / 6.2 us against 7.0 / 7.6 at B = 5 / 8; int4
-    // 7.0 / 7.4 against 8.3 / 8.9)
-    if (N <= 4096 && K > 1024 && K <= 2048 && fmt != KM4 && fmt != INT8KM) return false;
+    // int8 two chunks) the dot2 kernel is faster at B = 5-8 too (HIP graphs,
+    // B = 5 / 8: fp4 4096 x 2048 5.9 / 6.2 us against 7.0 / 7.6; int4 7.0 /
+    // 7.4 against 8.3 / 8.9; km4 5.9 / 6.4 against 8.6 / 9.2; int8 k-means
+    // 6.4 / 6.5 against 12.9 / 13.5)
+    if (N <= 4096 && K > 1024 && K <= 2048) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces

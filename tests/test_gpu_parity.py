@@ -124,7 +124,7 @@ def test_batched_matvec_parity(fmt, N, K, Bs):
     group, every batch width it takes, a single row group (N = 16), one load
     step per row (K = 512) and three (K = 1536, past 4096 rows), the largest K
     it stages (4096, at B = 3); and shapes it hands to the dot2 path (up to
-    4096 rows of K 1025..2048 at B = 5-8 outside the table formats, x too
+    4096 rows of K 1025..2048 at B = 5-8, x too
     large for its LDS stage at K = 3584, K = 640 not a multiple of 512, int8
     K = 256 taken but the 4-bit formats not)."""
     W, x = _case(fmt, N, K, B=8, seed=N + K)
