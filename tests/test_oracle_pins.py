@@ -379,6 +379,75 @@ def test_km4_lloyd_invariants():
     _km4_check_invariants(W, codes, lut, iters, 20)
 
 
+def test_km4_starting_table_is_order_statistics():
+    """With no Lloyd step the table of a row with more than 16 distinct values
+    is the row's order statistics at ranks (2j+1)K/32 (numpy sort), and every
+    weight takes its nearest entry (ties to the lower index)."""
+    rng = np.random.default_rng(44)
+    for K in (32, 96, 2048):
+        W = (rng.standard_normal((6, K)) * 0.02).astype(np.float16)
+        W[2, ::5] *= 25
+        codes, lut, iters = oracle.pack_km4(W, max_iter=0, return_iters=True)
+        assert np.all(iters == 0)
+        ranks = (2 * np.arange(16) + 1) * K // 32
+        S = np.sort(W.astype(np.float64), axis=1)
+        assert np.array_equal(lut.view(np.float16).astype(np.float64), S[:, ranks]), K
+        _km4_check_invariants(W, codes, lut, iters, 0)
+
+
+# A row of 32 distinct integers worked through the Lloyd steps by hand with the
+# midpoint rule (a weight goes to the number of adjacent entry pairs whose sum
+# is strictly below twice the weight) and exact member means (all fp16 numbers).
+_KM4_HAND_ROW = list(range(24)) + [33, 37, 38, 39, 48, 49, 62, 63]
+_KM4_HAND_HEAD = [1.0] + [2 * j + 1.5 for j in range(1, 11)] + [23.0]   # entries 0..11 after step 1
+_KM4_HAND_TABLES = {
+    # start: ranks 1, 3, ..., 31 of the sorted row
+    0: [2 * j + 1.0 for j in range(12)] + [37.0, 39.0, 49.0, 63.0],
+    # step 1 (midpoints 2, 4, .., 22, 30, 38, 44, 56): {0,1,2} {3,4} .. {21,22} {23}
+    # {33,37,38} {39} {48,49} {62,63}
+    1: _KM4_HAND_HEAD + [36.0, 39.0, 48.5, 62.5],
+    # step 2 (midpoints .., 29.5, 37.5, 43.75, 55.5): 38 moves up: {33,37} {38,39}
+    2: _KM4_HAND_HEAD + [35.0, 38.5, 48.5, 62.5],
+    # step 3 (midpoints .., 29, 36.75, 43.5, 55.5): 37 moves up: {33} {37,38,39}
+    3: _KM4_HAND_HEAD + [33.0, 38.0, 48.5, 62.5],
+    # step 4 (midpoints .., 28, 35.5, 43.25, 55.5) moves nothing: stop
+}
+
+
+def _km4_hand_codes(table):
+    t = np.array(table)
+    v = np.array(_KM4_HAND_ROW, np.float64)
+    return np.sum((t[:-1] + t[1:])[None, :] < 2 * v[:, None], axis=1)
+
+
+@pytest.mark.parametrize("max_iter", [0, 1, 2, 3, 4, 20])
+def test_km4_hand_worked_lloyd_steps(max_iter):
+    perm = np.random.default_rng(45).permutation(32)          # weights in a scrambled order
+    row = np.array(_KM4_HAND_ROW, np.float16)[perm][None, :]
+    codes, lut, iters = oracle.pack_km4(row, max_iter=max_iter, return_iters=True)
+    table = _KM4_HAND_TABLES[min(max_iter, 3)]
+    assert iters[0] == min(max_iter, 4)
+    assert lut[0].view(np.float16).astype(np.float64).tolist() == table
+    assert np.array_equal(_unpack_nibbles(codes)[0], _km4_hand_codes(table)[perm])
+
+
+def test_km4_default_is_twenty_lloyd_steps():
+    """The default table is the one after at most 20 steps: on rows that need
+    more, it equals max_iter=20 and differs from 19 and 21."""
+    rng = np.random.default_rng(46)
+    W = rng.standard_normal((64, 2048)).astype(np.float16)
+    _, _, iters = oracle.pack_km4(W, max_iter=500, return_iters=True)
+    slow = np.nonzero(iters > 22)[0][:4]
+    assert slow.size > 0
+    W = W[slow]
+    c, l = oracle.pack_km4(W)
+    c20, l20 = oracle.pack_km4(W, max_iter=20)
+    assert np.array_equal(c, c20) and np.array_equal(l, l20)
+    for m in (19, 21):
+        cm, lm = oracle.pack_km4(W, max_iter=m)
+        assert not np.array_equal(lm, l20), m
+
+
 def test_km4_gaussian_reaches_lloyd_max_levels():
     """A long Gaussian row converges to the 16-level Lloyd-Max quantizer of
     N(0, 1) (Max, 1960: levels +-0.1284, 0.3881, 0.6568, 0.9424, 1.2562, 1.6181,
