@@ -182,7 +182,7 @@ qmv_status qpack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int nout, int
 
 /* y[b][n] = sum_k W_hat[n][k] * x[b][k] with the outliers added in fp32;
  * x fp16 or fp32 [B][K], B <= 8, y fp32 [B][N]; the tables and codes as
- * qmatvec_km4. */
+ * qmatvec_km4 (lut 4-byte aligned: the tables are read as 32-bit words). */
 qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
                         const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
                         const void *x, qmv_dtype xdt, int B, float *y, void *stream);

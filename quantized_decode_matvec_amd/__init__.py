@@ -120,42 +120,126 @@ def _empty(shape, dtype, like):
     return _torch().empty(shape, dtype=dtype, device=like.device)
 
 
+# ---------------------------------------------------------------- argument checks
+#
+# The C ABI receives bare pointers and sizes, so it cannot see a tensor's shape,
+# strides, dtype or device. Every wrapper checks those here, before any pointer
+# reaches the library: a short or strided buffer would otherwise be read or
+# written past its end on the GPU.
+
+def _bad(fn, msg):
+    raise ValueError("%s: %s" % (fn, msg))
+
+
+def _tensor(fn, name, t, shape=None, itemsize=None, dtypes=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: %s must be a torch.Tensor, got %s" % (fn, name, type(t).__name__))
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s: %s has dtype %s, expected one of %s" % (fn, name, t.dtype, ", ".join(map(str, dtypes))))
+    if itemsize is not None and t.element_size() != itemsize:
+        raise TypeError("%s: %s has %d-byte elements, expected %d" % (fn, name, t.element_size(), itemsize))
+    if ndim is not None and t.dim() != ndim:
+        _bad(fn, "%s has %d dimensions, expected %d" % (name, t.dim(), ndim))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _bad(fn, "%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        _bad(fn, "%s must be contiguous" % name)
+    return t
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _plane_bytes(fn, name, t, want):
+    if _nbytes(t) != want:
+        _bad(fn, "%s holds %d bytes, expected %d" % (name, _nbytes(t), want))
+
+
+def _on_gpu(fn, *ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) != 1:
+        _bad(fn, "tensors are on different devices: %s" % sorted(map(str, devs)))
+    d = devs.pop()
+    if d.type != "cuda":
+        _bad(fn, "tensors must be in GPU memory, got device %s" % d)
+
+
+def _fp(fn, name, t, allow_f32=True):
+    torch = _torch()
+    ok = (torch.float16, torch.float32) if allow_f32 else (torch.float16,)
+    return _tensor(fn, name, t, dtypes=ok)
+
+
+def _plane_row_bytes(fmt, K):
+    """Bytes of the scale/table plane per row of K weights."""
+    return {"int4": K // 16, "fp4": K // 32, "int8": K // 16, "km4": 32, "int4aff": K // 8,
+            "int8km": 16}[fmt]
+
+
+def _as_batch(fn, x, K, allow_f32=True):
+    """x [K] or [B, K] -> [B, K] view."""
+    _fp(fn, "x", x, allow_f32)
+    if x.dim() == 1:
+        x = x.view(1, -1)
+    if x.dim() != 2 or x.shape[1] != K:
+        _bad(fn, "x has shape %s, expected [B, %d] or [%d]" % (tuple(x.shape), K, K))
+    return x
+
+
+def _codes2d(fn, fmt, codes):
+    _tensor(fn, "codes", codes, itemsize=1, ndim=2)
+    K = codes.shape[1] if fmt in ("int8", "int8km") else codes.shape[1] * 2
+    return codes.shape[0], K
+
+
 # ---------------------------------------------------------------- packing
+
+def _pack_args(fn, W, codes, plane, code_cols, plane_cols, plane_item, code_dtype, plane_dtype, allow_f32=True):
+    torch = _torch()
+    _fp(fn, "W", W, allow_f32)
+    if W.dim() != 2:
+        _bad(fn, "W must be [N, K], got shape %s" % (tuple(W.shape),))
+    N, K = W.shape
+    if K % 32 != 0:
+        _bad(fn, "K = %d is not a multiple of 32" % K)
+    codes = _empty((N, code_cols(K)), code_dtype, W) if codes is None else codes
+    plane = _empty((N, plane_cols(K)), plane_dtype, W) if plane is None else plane
+    _tensor(fn, "codes", codes, shape=(N, code_cols(K)), itemsize=1)
+    _tensor(fn, "plane", plane, shape=(N, plane_cols(K)), itemsize=plane_item)
+    _on_gpu(fn, W, codes, plane)
+    return N, K, codes, plane
+
 
 def qpack_int4(W, codes=None, scale=None, stream=None):
     torch = _torch()
-    N, K = W.shape
-    codes = _empty((N, K // 2), torch.uint8, W) if codes is None else codes
-    scale = _empty((N, K // 32), torch.uint16, W) if scale is None else scale
+    N, K, codes, scale = _pack_args("qpack_int4", W, codes, scale, lambda K: K // 2, lambda K: K // 32, 2,
+                                    torch.uint8, torch.uint16)
     _check("qpack_int4", lib().qpack_int4(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(scale), _stream(stream)))
     return codes, scale
 
 
 def qpack_fp4(W, codes=None, scale=None, stream=None):
     torch = _torch()
-    N, K = W.shape
-    codes = _empty((N, K // 2), torch.uint8, W) if codes is None else codes
-    scale = _empty((N, K // 32), torch.uint8, W) if scale is None else scale
+    N, K, codes, scale = _pack_args("qpack_fp4", W, codes, scale, lambda K: K // 2, lambda K: K // 32, 1,
+                                    torch.uint8, torch.uint8)
     _check("qpack_fp4", lib().qpack_fp4(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(scale), _stream(stream)))
     return codes, scale
 
 
 def qpack_int8(W, codes=None, scale=None, stream=None):
     torch = _torch()
-    N, K = W.shape
-    codes = _empty((N, K), torch.int8, W) if codes is None else codes
-    scale = _empty((N, K // 32), torch.uint16, W) if scale is None else scale
+    N, K, codes, scale = _pack_args("qpack_int8", W, codes, scale, lambda K: K, lambda K: K // 32, 2,
+                                    torch.int8, torch.uint16)
     _check("qpack_int8", lib().qpack_int8(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(scale), _stream(stream)))
     return codes, scale
 
 
 def qpack_km4(W, max_iter=20, codes=None, lut=None, stream=None):
     torch = _torch()
-    if W.dtype != torch.float16:
-        raise TypeError("qpack_km4 takes fp16 weights")
-    N, K = W.shape
-    codes = _empty((N, K // 2), torch.uint8, W) if codes is None else codes
-    lut = _empty((N, 16), torch.uint16, W) if lut is None else lut
+    N, K, codes, lut = _pack_args("qpack_km4", W, codes, lut, lambda K: K // 2, lambda K: 16, 2,
+                                  torch.uint8, torch.uint16, allow_f32=False)
     _check("qpack_km4", lib().qpack_km4(_ptr(W), N, K, int(max_iter), _ptr(codes), _ptr(lut), _stream(stream)))
     return codes, lut
 
@@ -163,9 +247,8 @@ def qpack_km4(W, max_iter=20, codes=None, lut=None, stream=None):
 def qpack_int4aff(W, codes=None, plane=None, stream=None):
     """W [N, K] -> (codes uint8 [N, K/2], plane uint32-as-int32 [N, K/32]: fp16 scale | fp16 bias << 16)."""
     torch = _torch()
-    N, K = W.shape
-    codes = _empty((N, K // 2), torch.uint8, W) if codes is None else codes
-    plane = _empty((N, K // 32), torch.int32, W) if plane is None else plane
+    N, K, codes, plane = _pack_args("qpack_int4aff", W, codes, plane, lambda K: K // 2, lambda K: K // 32, 4,
+                                    torch.uint8, torch.int32)
     _check("qpack_int4aff", lib().qpack_int4aff(_ptr(W), _dt(W), N, K, _ptr(codes), _ptr(plane), _stream(stream)))
     return codes, plane
 
@@ -173,11 +256,15 @@ def qpack_int4aff(W, codes=None, plane=None, stream=None):
 def qpack_int8km(W, max_iter=20, codes=None, lut=None, stream=None):
     """W fp16 [N, K], N % 32 == 0 -> (codes uint8 [N, K], lut uint16 [N/32, 256])."""
     torch = _torch()
-    if W.dtype != torch.float16:
-        raise TypeError("qpack_int8km takes fp16 weights")
+    _fp("qpack_int8km", "W", W, allow_f32=False)
+    if W.dim() != 2 or W.shape[0] % 32 != 0:
+        _bad("qpack_int8km", "W must be [N, K] with N a multiple of 32, got shape %s" % (tuple(W.shape),))
     N, K = W.shape
     codes = _empty((N, K), torch.uint8, W) if codes is None else codes
     lut = _empty((N // 32, 256), torch.uint16, W) if lut is None else lut
+    _tensor("qpack_int8km", "codes", codes, shape=(N, K), itemsize=1)
+    _tensor("qpack_int8km", "lut", lut, shape=(N // 32, 256), itemsize=2)
+    _on_gpu("qpack_int8km", W, codes, lut)
     _check("qpack_int8km", lib().qpack_int8km(_ptr(W), N, K, int(max_iter), _ptr(codes), _ptr(lut), _stream(stream)))
     return codes, lut
 
@@ -193,12 +280,28 @@ def _kdim(fmt, codes):
     return codes.shape[-1] if fmt in ("int8", "int8km") else codes.shape[-1] * 2
 
 
+def _dense_plane(fn, fmt, plane, N, K):
+    _tensor(fn, "plane", plane)
+    if fmt == "int8km" and N % 32 != 0:
+        _bad(fn, "int8km needs N % 32 == 0, got N = %d" % N)
+    _plane_bytes(fn, "plane", plane, N * _plane_row_bytes(fmt, K))
+
+
+def _y_out(fn, y, shape, dtype, like, name="y"):
+    if y is None:
+        return _empty(shape, dtype, like)
+    _tensor(fn, name, y, shape=shape, dtypes=(dtype,))
+    return y
+
+
 def _matvec(name, fmt, codes, plane, x, y, stream):
     torch = _torch()
-    N, K = codes.shape[0], _kdim(fmt, codes)
-    x2 = x if x.dim() == 2 else x.view(1, -1)
+    N, K = _codes2d(name, fmt, codes)
+    _dense_plane(name, fmt, plane, N, K)
+    x2 = _as_batch(name, x, K)
     B = x2.shape[0]
-    y = _empty((B, N), torch.float32, codes) if y is None else y
+    y = _y_out(name, y, (B, N), torch.float32, codes)
+    _on_gpu(name, codes, plane, x2, y)
     fn = getattr(lib(), name)
     _check(name, fn(_ptr(codes), _ptr(plane), N, K, _ptr(x2), _dt(x2), B, _ptr(y), _stream(stream)))
     return y
@@ -233,8 +336,10 @@ def qpack_km4o(W, nout, max_iter=20, stream=None):
     uint16, oval [N, nout] int8, oscale [N] uint16): 4-bit k-means rows plus
     nout int8 outliers per row."""
     torch = _torch()
-    if W.dtype != torch.float16:
-        raise TypeError("qpack_km4o takes fp16 weights")
+    _fp("qpack_km4o", "W", W, allow_f32=False)
+    if W.dim() != 2:
+        _bad("qpack_km4o", "W must be [N, K], got shape %s" % (tuple(W.shape),))
+    _on_gpu("qpack_km4o", W)
     N, K = W.shape
     codes = _empty((N, K // 2), torch.uint8, W)
     lut = _empty((N, 16), torch.uint16, W)
@@ -248,11 +353,18 @@ def qpack_km4o(W, nout, max_iter=20, stream=None):
 
 def qmatvec_km4o(codes, lut, ocol, oval, oscale, x, y=None, stream=None):
     torch = _torch()
-    N, K = codes.shape[0], codes.shape[1] * 2
+    fn = "qmatvec_km4o"
+    N, K = _codes2d(fn, "km4", codes)
+    _dense_plane(fn, "km4", lut, N, K)
+    _tensor(fn, "ocol", ocol, itemsize=2, ndim=2)
     nout = ocol.shape[1]
-    x2 = x if x.dim() == 2 else x.view(1, -1)
+    _tensor(fn, "ocol", ocol, shape=(N, nout))
+    _tensor(fn, "oval", oval, shape=(N, nout), itemsize=1)
+    _tensor(fn, "oscale", oscale, shape=(N,), itemsize=2)
+    x2 = _as_batch(fn, x, K)
     B = x2.shape[0]
-    y = _empty((B, N), torch.float32, codes) if y is None else y
+    y = _y_out(fn, y, (B, N), torch.float32, codes)
+    _on_gpu(fn, codes, lut, ocol, oval, oscale, x2, y)
     _check("qmatvec_km4o", lib().qmatvec_km4o(_ptr(codes), _ptr(lut), _ptr(ocol), _ptr(oval), _ptr(oscale), N, K,
                                               int(nout), _ptr(x2), _dt(x2), B, _ptr(y), _stream(stream)))
     return y
@@ -264,8 +376,12 @@ def qmatvec(fmt, codes, plane, x, y=None, stream=None):
 
 def qdequant(fmt, codes, plane, out=None, stream=None):
     torch = _torch()
-    N, K = codes.shape[0], _kdim(fmt, codes)
-    out = _empty((N, K), torch.float32, codes) if out is None else out
+    if fmt not in FORMATS:
+        raise ValueError("qdequant: unknown format %r" % (fmt,))
+    N, K = _codes2d("qdequant", fmt, codes)
+    _dense_plane("qdequant", fmt, plane, N, K)
+    out = _y_out("qdequant", out, (N, K), torch.float32, codes, "out")
+    _on_gpu("qdequant", codes, plane, out)
     _check("qdequant", lib().qdequant(FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(out), _stream(stream)))
     return out
 
@@ -274,9 +390,12 @@ def qdequant(fmt, codes, plane, out=None, stream=None):
 
 def qmoe_route(logits, topk, ids=None, weights=None, stream=None):
     torch = _torch()
+    fn = "qmoe_route"
+    _tensor(fn, "logits", logits, dtypes=(torch.float32,), ndim=2)
     T, E = logits.shape
-    ids = _empty((T, topk), torch.int32, logits) if ids is None else ids
-    weights = _empty((T, topk), torch.float32, logits) if weights is None else weights
+    ids = _y_out(fn, ids, (T, topk), torch.int32, logits, "ids")
+    weights = _y_out(fn, weights, (T, topk), torch.float32, logits, "weights")
+    _on_gpu(fn, logits, ids, weights)
     _check("qmoe_route", lib().qmoe_route(_ptr(logits), T, E, topk, _ptr(ids), _ptr(weights), _stream(stream)))
     return ids, weights
 
@@ -289,20 +408,46 @@ def gather_qmatvec(fmt, codes, plane, x, ids, weights=None, epi="none", x_per_sl
                    y=None, workspace=None, stream=None):
     """codes/plane: [E, N, ...] stacked experts; x [T, K] or [T, topk, K] (fp16)."""
     torch = _torch()
+    fn = "gather_qmatvec"
+    if fmt not in FORMATS:
+        raise ValueError("%s: unknown format %r" % (fn, fmt))
+    if epi not in EPILOGUES:
+        raise ValueError("%s: unknown epilogue %r" % (fn, epi))
+    _tensor(fn, "codes", codes, itemsize=1, ndim=3)
     E, N = codes.shape[0], codes.shape[1]
     K = _kdim(fmt, codes)
+    _tensor(fn, "plane", plane)
+    if plane.dim() < 1 or plane.shape[0] != E:
+        _bad(fn, "plane must have E = %d as its first dimension, got shape %s" % (E, tuple(plane.shape)))
+    if fmt == "int8km" and N % 32 != 0:
+        _bad(fn, "int8km needs N % 32 == 0, got N = %d" % N)
+    _plane_bytes(fn, "plane", plane, E * N * _plane_row_bytes(fmt, K))
+    _tensor(fn, "ids", ids, dtypes=(torch.int32,), ndim=2)
     T, topk = ids.shape
+    _tensor(fn, "x", x, dtypes=(torch.float16,))
+    xs = (T, topk, K) if x_per_slot else (T, K)
+    if tuple(x.shape) != xs:
+        _bad(fn, "x has shape %s, expected %s" % (tuple(x.shape), xs))
     e = EPILOGUES[epi]
-    if y is None:
-        if e == QMV_EPI_NONE:
-            y = _empty((T, topk, N), torch.float32, codes)
-        elif e == QMV_EPI_SWIGLU:
-            y = _empty((T, topk, N // 2), torch.float16, codes)
-        else:
-            y = _empty((T, N), torch.float32, codes)
+    if e == QMV_EPI_COMBINE:
+        if weights is None:
+            _bad(fn, "the combine epilogue needs weights")
+        _tensor(fn, "weights", weights, shape=(T, topk), dtypes=(torch.float32,))
+    if e == QMV_EPI_NONE:
+        y = _y_out(fn, y, (T, topk, N), torch.float32, codes)
+    elif e == QMV_EPI_SWIGLU:
+        if N % 2 != 0:
+            _bad(fn, "the SwiGLU epilogue needs an even N, got %d" % N)
+        y = _y_out(fn, y, (T, topk, N // 2), torch.float16, codes)
+    else:
+        y = _y_out(fn, y, (T, N), torch.float32, codes)
+    _on_gpu(fn, codes, plane, x, ids, y, weights if e == QMV_EPI_COMBINE else None)
     need = gather_qmatvec_workspace_bytes(T, topk, E, N, e)
     if need and workspace is None:
         workspace = _empty((need,), torch.uint8, codes)
+    if workspace is not None:
+        _tensor(fn, "workspace", workspace)
+        _on_gpu(fn, codes, workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("gather_qmatvec", lib().gather_qmatvec(
         FORMATS[fmt], _ptr(codes), _ptr(plane), E, N, K, _ptr(x), _dt(x), 1 if x_per_slot else 0,
@@ -318,14 +463,34 @@ def qmoe_ffn(fmt, gu_codes, gu_plane, dn_codes, dn_plane, x, logits, topk, ids=N
     fp16; logits [T, E] fp32. Returns (y [T, H] fp32, ids, weights, h).
     """
     torch = _torch()
+    fn = "qmoe_ffn"
+    if fmt not in FORMATS:
+        raise ValueError("%s: unknown format %r" % (fn, fmt))
+    _tensor(fn, "gu_codes", gu_codes, itemsize=1, ndim=3)
+    _tensor(fn, "dn_codes", dn_codes, itemsize=1, ndim=3)
     E, I2 = gu_codes.shape[0], gu_codes.shape[1]
     H = dn_codes.shape[1]
     I = I2 // 2
+    if I2 % 2 != 0 or dn_codes.shape[0] != E:
+        _bad(fn, "gu_codes [E, 2I, ..] and dn_codes [E, H, ..] do not match: %s, %s"
+             % (tuple(gu_codes.shape), tuple(dn_codes.shape)))
+    if _kdim(fmt, gu_codes) != H or _kdim(fmt, dn_codes) != I:
+        _bad(fn, "gate/up rows must hold H = %d weights and down rows I = %d weights" % (H, I))
+    for name, pl, rows, k in (("gu_plane", gu_plane, I2, H), ("dn_plane", dn_plane, H, I)):
+        _tensor(fn, name, pl)
+        if pl.dim() < 1 or pl.shape[0] != E:
+            _bad(fn, "%s must have E = %d as its first dimension" % (name, E))
+        _plane_bytes(fn, name, pl, E * rows * _plane_row_bytes(fmt, k))
+    _tensor(fn, "x", x, dtypes=(torch.float16,), ndim=2)
     T = x.shape[0]
-    ids = _empty((T, topk), torch.int32, x) if ids is None else ids
-    weights = _empty((T, topk), torch.float32, x) if weights is None else weights
-    h = _empty((T, topk, I), torch.float16, x) if h is None else h
-    y = _empty((T, H), torch.float32, x) if y is None else y
+    if x.shape[1] != H:
+        _bad(fn, "x has shape %s, expected [T, %d]" % (tuple(x.shape), H))
+    _tensor(fn, "logits", logits, shape=(T, E), dtypes=(torch.float32,))
+    ids = _y_out(fn, ids, (T, topk), torch.int32, x, "ids")
+    weights = _y_out(fn, weights, (T, topk), torch.float32, x, "weights")
+    h = _y_out(fn, h, (T, topk, I), torch.float16, x, "h")
+    y = _y_out(fn, y, (T, H), torch.float32, x)
+    _on_gpu(fn, gu_codes, gu_plane, dn_codes, dn_plane, x, logits, ids, weights, h, y)
     _check("qmoe_ffn", lib().qmoe_ffn(
         FORMATS[fmt], _ptr(gu_codes), _ptr(gu_plane), _ptr(dn_codes), _ptr(dn_plane), E, H, I,
         _ptr(logits), _ptr(x), T, topk, _ptr(ids), _ptr(weights), _ptr(h), _ptr(y), _stream(stream)))
@@ -349,13 +514,19 @@ def qmatvec_argmax_workspace_bytes(N, B):
 def qmatvec_argmax(fmt, codes, plane, x, idx=None, val=None, workspace=None, stream=None):
     """Fused matvec + argmax: (idx int32 [B], val fp32 [B]) of the largest y per batch row."""
     torch = _torch()
-    N, K = codes.shape[0], _kdim(fmt, codes)
-    x2 = x if x.dim() == 2 else x.view(1, -1)
+    fn = "qmatvec_argmax"
+    if fmt not in FORMATS:
+        raise ValueError("%s: unknown format %r" % (fn, fmt))
+    N, K = _codes2d(fn, fmt, codes)
+    _dense_plane(fn, fmt, plane, N, K)
+    x2 = _as_batch(fn, x, K, allow_f32=False)
     B = x2.shape[0]
-    idx = _empty((B,), torch.int32, codes) if idx is None else idx
-    val = _empty((B,), torch.float32, codes) if val is None else val
+    idx = _y_out(fn, idx, (B,), torch.int32, codes, "idx")
+    val = _y_out(fn, val, (B,), torch.float32, codes, "val")
     if workspace is None:
         workspace = _empty((qmatvec_argmax_workspace_bytes(N, B),), torch.uint8, codes)
+    _tensor(fn, "workspace", workspace)
+    _on_gpu(fn, codes, plane, x2, idx, val, workspace)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("qmatvec_argmax", lib().qmatvec_argmax(
         FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(x2), B, _ptr(idx), _ptr(val),
@@ -366,9 +537,16 @@ def qmatvec_argmax(fmt, codes, plane, x, idx=None, val=None, workspace=None, str
 def qpack_int8_rows(W, codes=None, scale=None, stream=None):
     """Embedding table W [V, H] -> (codes int8 [V, H], scale fp16 bits uint16 [V])."""
     torch = _torch()
+    fn = "qpack_int8_rows"
+    _fp(fn, "W", W)
+    if W.dim() != 2:
+        _bad(fn, "W must be [V, H], got shape %s" % (tuple(W.shape),))
     V, H = W.shape
     codes = _empty((V, H), torch.int8, W) if codes is None else codes
     scale = _empty((V,), torch.uint16, W) if scale is None else scale
+    _tensor(fn, "codes", codes, shape=(V, H), itemsize=1)
+    _tensor(fn, "scale", scale, shape=(V,), itemsize=2)
+    _on_gpu(fn, W, codes, scale)
     _check("qpack_int8_rows", lib().qpack_int8_rows(_ptr(W), _dt(W), V, H, _ptr(codes), _ptr(scale),
                                                     _stream(stream)))
     return codes, scale
@@ -377,9 +555,14 @@ def qpack_int8_rows(W, codes=None, scale=None, stream=None):
 def qembed_gather_int8(codes, scale, ids, out=None, stream=None):
     """out fp16 [T, H] = fp16(codes[ids] * scale[ids])."""
     torch = _torch()
+    fn = "qembed_gather_int8"
+    _tensor(fn, "codes", codes, itemsize=1, ndim=2)
     V, H = codes.shape
+    _tensor(fn, "scale", scale, shape=(V,), itemsize=2)
+    _tensor(fn, "ids", ids, dtypes=(torch.int32,))
     T = ids.numel()
-    out = _empty((T, H), torch.float16, codes) if out is None else out
+    out = _y_out(fn, out, (T, H), torch.float16, codes, "out")
+    _on_gpu(fn, codes, scale, ids, out)
     _check("qembed_gather_int8", lib().qembed_gather_int8(_ptr(codes), _ptr(scale), V, H, _ptr(ids), T,
                                                           _ptr(out), _stream(stream)))
     return out
@@ -389,8 +572,14 @@ def qembed_gather_int8(codes, scale, ids, out=None, stream=None):
 
 def qmv_stream_read(buf, sink=None, stream=None):
     torch = _torch()
+    fn = "qmv_stream_read"
+    _tensor(fn, "buf", buf)
     nbytes = buf.numel() * buf.element_size()
     words = int(lib().qmv_stream_read_sink_words(nbytes))
     sink = _empty((words,), torch.int32, buf) if sink is None else sink
+    _tensor(fn, "sink", sink, itemsize=4)
+    if sink.numel() < words:
+        _bad(fn, "sink holds %d words, needs %d" % (sink.numel(), words))
+    _on_gpu(fn, buf, sink)
     _check("qmv_stream_read", lib().qmv_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
     return sink

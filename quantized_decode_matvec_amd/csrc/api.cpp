@@ -182,7 +182,7 @@ qmv_status qpack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int nout, int
 qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
                         const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt, int B,
                         float *y, void *stream) {
-    qmv_status s = check_mv(codes, lut, 2, N, K, x, xdt, B, y);
+    qmv_status s = check_mv(codes, lut, 4, N, K, x, xdt, B, y);   // tables are read as 32-bit words
     if (s != QMV_OK) return s;
     if (!oscale || (nout > 0 && (!ocol || !oval))) return QMV_E_NULL;
     if (nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;   // columns fit uint16: K <= 65536

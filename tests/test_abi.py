@@ -83,6 +83,9 @@ def test_pack_validation(L):
     assert L.qmatvec_km4o(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 64, -1, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4o(FAKE, FAKE, NUL, NUL, NUL, 8, 64, 0, FAKE, 1, 1, FAKE, S) == E_NULL   # oscale needed
     assert L.qmatvec_km4o(FAKE, FAKE, ODD, FAKE, FAKE, 8, 64, 2, FAKE, 1, 1, FAKE, S) == E_ALIGN
+    TWO = ctypes.c_void_p(0x10002)    # 2-byte aligned table: read as 32-bit words, refused
+    assert L.qmatvec_km4o(FAKE, TWO, FAKE, FAKE, FAKE, 8, 64, 2, FAKE, 1, 1, FAKE, S) == E_ALIGN
+    assert L.qmatvec_km4(FAKE, TWO, 8, 64, FAKE, 1, 1, FAKE, S) == E_ALIGN
 
 
 @pytest.mark.parametrize("name", ["qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
