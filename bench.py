@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--all", action="store_true", help="(default; kept for older command lines)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-metric", action="store_true", help="time the metric kernel only (for profiling)")
+    ap.add_argument("--case", default=None,
+                    help="time one other kernel only (for profiling): FMT_bB with FMT in fp4, int4, int4aff, "
+                         "int8km, km4 and B in 1, 4, 8 (lm_head shape); int8_head; argmax_bB; moe")
     ap.add_argument("--calibrate", action="store_true",
                     help="run a plain 1 GiB device copy and a 1 GiB streaming read, for HBM byte-counter calibration")
     return ap.parse_args()
@@ -213,6 +216,9 @@ def main():
         sys.exit(1)
     if args.calibrate:
         calibrate()
+        return
+    if args.case:
+        run_case(args)
         return
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
@@ -436,46 +442,99 @@ def bench_int8_head(args):
     return {"int8_head_us": round(ms * 1e3, 2), "int8_head_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
 
-def bench_moe(args):
+def run_case(args):
+    """One kernel alone, `args.steps` timed calls (for counter runs under rocprofv3)."""
+    import torch
+    import quantized_decode_matvec_amd as qmv
+    from quantized_decode_matvec_amd import workloads as wl
+    case = args.case
+    res = {"case": case}
+    if case == "moe":
+        res.update(bench_moe(args, fmts=("int4",)))
+    elif case == "int8_head":
+        res.update(bench_int8_head(args))
+    else:
+        name, b = case.rsplit("_b", 1)
+        B = int(b)
+        c = wl.lm_head_km4(batch=8)
+        W = torch.from_numpy(c.W).cuda()
+        x = torch.from_numpy(c.x[:B]).cuda().contiguous()
+        fmt = "km4" if name == "argmax" else name
+        p0 = qmv.qpack(fmt, W)
+        del W
+        pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(args.copies - 1)]
+        y = torch.empty((B, N_ROWS), dtype=torch.float32, device="cuda")
+        if name == "argmax":
+            ws = torch.empty((qmv.qmatvec_argmax_workspace_bytes(N_ROWS, B),), dtype=torch.uint8, device="cuda")
+            idx = torch.empty((B,), dtype=torch.int32, device="cuda")
+            val = torch.empty((B,), dtype=torch.float32, device="cuda")
+            fn = lambda i: qmv.qmatvec_argmax(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x, idx=idx, val=val,
+                                              workspace=ws)
+        else:
+            fn = lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x, y=y)
+        gpu_warm(fn)
+        ms = timed(fn, args.steps, args.warmup)
+        res.update({"us": round(ms * 1e3, 2), "GBps": round(algo_bytes(fmt, N_ROWS, K_DIM) / (ms * 1e-3) / 1e9, 1)})
+    print(json.dumps(res), flush=True)
+
+
+MOE_CALLS, MOE_COPIES = 128, 4
+
+
+def bench_moe(args, fmts=("int4", "int4aff", "int8km"), tokens=(1, 4, 8)):
     """The MoE layer (E = 256, top-8, H = 2048, I = 512) in the pages' gather
-    formats, at T = 1, 4, 8 tokens, fused entry point and three-call path."""
+    formats at T = 1, 4, 8 tokens, fused entry point and three-call path, in
+    HIP graphs of 128 calls. Each call of a graph routes its own set of router
+    logits (128 sets drawn N(0, 1) with numpy default_rng(1)) against one of 4
+    copies of the expert slabs, so that what a window of calls reads is spread
+    over 4 x 256 expert copies (1.8 GB in int4), far more than twice the 256 MB
+    Infinity Cache: a routed expert is rarely still cached from an earlier call.
+    GB/s counts each call's distinct routed experts once (the gather reads an
+    expert once however many tokens chose it)."""
     import torch
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
     c = wl.moe()
     E, I2, H = c.W_gate_up.shape
     I = I2 // 2
+    lg_all = np.random.default_rng(1).standard_normal((MOE_CALLS, max(tokens), E), dtype=np.float32)
     out = {}
-    for fmt in ("int4", "int4aff", "int8km"):
+    for fmt in fmts:
         guc, gus = qmv.qpack(fmt, torch.from_numpy(c.W_gate_up.reshape(E * I2, H)).cuda())
         dnc, dns = qmv.qpack(fmt, torch.from_numpy(c.W_down.reshape(E * H, I)).cuda())
-        guc, gus = guc.view(E, I2, -1), gus.view(E, -1)
-        dnc, dns = dnc.view(E, H, -1), dns.view(E, -1)
+        slab = (guc.view(E, I2, -1), gus.view(E, -1), dnc.view(E, H, -1), dns.view(E, -1))
+        copies = [slab] + [tuple(a.clone() for a in slab) for _ in range(MOE_COPIES - 1)]
         per_expert = algo_bytes(fmt, I2, H) + algo_bytes(fmt, H, I)
-        for T in (1, 4, 8):
+        for T in tokens:
             x = torch.from_numpy(c.x[:T]).cuda()
-            lg = torch.from_numpy(c.logits[:T]).cuda()
+            lg = torch.from_numpy(np.ascontiguousarray(lg_all[:, :T])).cuda()
             ids = torch.empty((T, c.topk), dtype=torch.int32, device="cuda")
             w = torch.empty((T, c.topk), dtype=torch.float32, device="cuda")
             h = torch.empty((T, c.topk, I), dtype=torch.float16, device="cuda")
             y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+            uniq = []
+            for k in range(MOE_CALLS):
+                qmv.qmoe_route(lg[k], c.topk, ids=ids, weights=w)
+                uniq.append(len(np.unique(ids.cpu().numpy())))
+            moved = float(np.mean(uniq)) * per_expert
 
             def layer(i):
-                qmv.qmoe_ffn(fmt, guc, gus, dnc, dns, x, lg, c.topk, ids=ids, weights=w, h=h, y=y)
+                g, s, d, ds = copies[i % MOE_COPIES]
+                qmv.qmoe_ffn(fmt, g, s, d, ds, x, lg[i % MOE_CALLS], c.topk, ids=ids, weights=w, h=h, y=y)
 
             def layer3(i):
-                qmv.qmoe_route(lg, c.topk, ids=ids, weights=w)
-                qmv.gather_qmatvec(fmt, guc, gus, x, ids, epi="swiglu", y=h)
-                qmv.gather_qmatvec(fmt, dnc, dns, h, ids, weights=w, epi="combine", x_per_slot=True, y=y)
+                g, s, d, ds = copies[i % MOE_COPIES]
+                qmv.qmoe_route(lg[i % MOE_CALLS], c.topk, ids=ids, weights=w)
+                qmv.gather_qmatvec(fmt, g, s, x, ids, epi="swiglu", y=h)
+                qmv.gather_qmatvec(fmt, d, ds, h, ids, weights=w, epi="combine", x_per_slot=True, y=y)
 
-            ms = timed_graph(layer, args.steps, per_graph=16)
-            ms3 = timed_graph(layer3, args.steps, per_graph=16)
-            uniq = len(np.unique(ids.cpu().numpy()))
+            ms = timed_graph(layer, 4 * args.steps, per_graph=MOE_CALLS)
+            ms3 = timed_graph(layer3, 4 * args.steps, per_graph=MOE_CALLS)
             out["moe_%s_T%d_us" % (fmt, T)] = round(ms * 1e3, 2)
-            out["moe_%s_T%d_GBps" % (fmt, T)] = round(uniq * per_expert / (ms * 1e-3) / 1e9, 1)
+            out["moe_%s_T%d_GBps" % (fmt, T)] = round(moved / (ms * 1e-3) / 1e9, 1)
             out["moe_%s_T%d_3call_us" % (fmt, T)] = round(ms3 * 1e3, 2)
-            out["moe_T%d_experts" % T] = uniq
-        del guc, gus, dnc, dns
+            out["moe_T%d_experts_per_call" % T] = round(float(np.mean(uniq)), 2)
+        del copies, slab, guc, gus, dnc, dns
     return out
 
 

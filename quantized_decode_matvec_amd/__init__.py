@@ -48,6 +48,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError("libqmv.so not found at %s; build it with "
                               "`python -m quantized_decode_matvec_amd.build`" % LIB_PATH)
+        # torch carries its own HIP runtime (libamdhip64.so, soname libamdhip64.so.7).
+        # Load it first, so that our library's dependency on that soname binds to
+        # the runtime torch uses: loaded the other way round, the process holds two
+        # HIP runtimes and ours finds no device.
+        _torch()
         L = ctypes.CDLL(LIB_PATH)
         P, i64, ci, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         sigs = {

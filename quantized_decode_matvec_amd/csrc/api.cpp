@@ -3,6 +3,8 @@
 // The contract of each entry point is documented in include/qmv.h.
 #include <hip/hip_runtime.h>
 
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 
 #include "qmv.h"
@@ -32,7 +34,30 @@ inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
-inline qmv_status launch_status(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_E_LAUNCH; }
+// QMV_DEBUG_SYNC=1 in the environment: name the HIP error behind every
+// QMV_E_LAUNCH on stderr, and after every launch wait for the stream and report
+// any error the work itself raised (a debugging aid; off by default).
+inline bool debug_sync() {
+    static const bool on = [] {
+        const char *v = getenv("QMV_DEBUG_SYNC");
+        return v != nullptr && v[0] != '\0' && v[0] != '0';
+    }();
+    return on;
+}
+
+inline qmv_status launch_status_at(const char *fn, hipError_t e, void *stream) {
+    if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess && debug_sync()) fprintf(stderr, "qmv: %s: %s (%s)\n", fn, hipGetErrorName(e), hipGetErrorString(e));
+    return e == hipSuccess ? QMV_OK : QMV_E_LAUNCH;
+}
+#define launch_status(call) launch_status_at(__func__, (call), stream)
+
+// HIP keeps one last-error slot per host thread, and the launchers read it
+// after their launches. Other code on the thread can leave a non-fatal error
+// there (an allocator polling an event that is not ready yet, say), which
+// would then be reported as a failed launch of ours: clear it just before
+// launching. Errors that make the device unusable persist regardless.
+inline void forget_earlier_errors() { (void)hipGetLastError(); }
 
 qmv_status check_wk(const void *W, qmv_dtype wdt, int64_t N, int64_t K) {
     if (!W) return QMV_E_NULL;
@@ -92,6 +117,7 @@ qmv_status qpack_int4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_
     if (s != QMV_OK) return s;
     if (!codes || !scale) return QMV_E_NULL;
     if (!aligned(codes, 16) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_int4(W, wdt, N, K, codes, scale, as_stream(stream)));
 }
 
@@ -101,6 +127,7 @@ qmv_status qpack_fp4(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uint8_t
     if (s != QMV_OK) return s;
     if (!codes || !scale) return QMV_E_NULL;
     if (!aligned(codes, 16)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_fp4(W, wdt, N, K, codes, scale, as_stream(stream)));
 }
 
@@ -110,6 +137,7 @@ qmv_status qpack_int8(const void *W, qmv_dtype wdt, int64_t N, int64_t K, int8_t
     if (s != QMV_OK) return s;
     if (!codes || !scale) return QMV_E_NULL;
     if (!aligned(codes, 16) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_int8(W, wdt, N, K, codes, scale, as_stream(stream)));
 }
 
@@ -119,6 +147,7 @@ qmv_status qpack_int4aff(const void *W, qmv_dtype wdt, int64_t N, int64_t K, uin
     if (s != QMV_OK) return s;
     if (!codes || !plane) return QMV_E_NULL;
     if (!aligned(codes, 16) || !aligned(plane, 4)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_int4aff(W, wdt, N, K, codes, plane, as_stream(stream)));
 }
 
@@ -129,6 +158,7 @@ qmv_status qpack_km4(const uint16_t *W_f16, int64_t N, int64_t K, int max_iter, 
     if (!codes || !lut) return QMV_E_NULL;
     if (K > 4096 || max_iter < 1 || max_iter > 1000) return QMV_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(lut, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_km4(W_f16, N, K, max_iter, codes, lut, as_stream(stream)));
 }
 
@@ -136,6 +166,7 @@ qmv_status qmatvec_int4(const uint8_t *codes, const uint16_t *scale, int64_t N, 
                         qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, scale, 2, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_INT4, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -143,6 +174,7 @@ qmv_status qmatvec_fp4(const uint8_t *codes, const uint8_t *scale, int64_t N, in
                        qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, scale, 1, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_FP4, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -150,6 +182,7 @@ qmv_status qmatvec_int8(const int8_t *codes, const uint16_t *scale, int64_t N, i
                         qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, scale, 2, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_INT8, codes, scale, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -157,6 +190,7 @@ qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int
                        qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, lut, 4, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_KM4, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -164,6 +198,7 @@ qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t 
                            qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, plane, 4, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_INT4AFF, codes, plane, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -175,6 +210,7 @@ qmv_status qpack_km4o(const uint16_t *W_f16, int64_t N, int64_t K, int nout, int
     if (K > 4096 || max_iter < 1 || max_iter > 1000 || nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;
     if (N > INT32_MAX) return QMV_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(lut, 2) || !aligned(ocol, 2) || !aligned(oscale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(
         qmv::launch_pack_km4o(W_f16, N, K, nout, max_iter, codes, lut, ocol, oval, oscale, as_stream(stream)));
 }
@@ -187,6 +223,7 @@ qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_
     if (!oscale || (nout > 0 && (!ocol || !oval))) return QMV_E_NULL;
     if (nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;   // columns fit uint16: K <= 65536
     if (!aligned(ocol, 2) || !aligned(oscale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(
         qmv::launch_matvec_km4o(codes, lut, ocol, oval, oscale, N, K, nout, x, xdt, B, y, as_stream(stream)));
 }
@@ -197,6 +234,7 @@ qmv_status qpack_int8km(const uint16_t *W_f16, int64_t N, int64_t K, int max_ite
     if (N < 32 || N % 32 != 0 || K < 32 || K % 32 != 0 || K > 2048 || max_iter < 1) return QMV_E_SHAPE;
     if (N / 32 > INT32_MAX) return QMV_E_SHAPE;
     if (!aligned(W_f16, 16) || !aligned(codes, 16) || !aligned(lut, 4)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_int8km(W_f16, N, K, max_iter, codes, lut, as_stream(stream)));
 }
 
@@ -205,6 +243,7 @@ qmv_status qmatvec_int8km(const uint8_t *codes, const uint16_t *lut, int64_t N, 
     qmv_status s = check_mv(codes, lut, 4, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
     if (N % 32 != 0) return QMV_E_SHAPE;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec(QMV_INT8KM, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
@@ -214,6 +253,7 @@ qmv_status qdequant(qmv_format fmt, const void *codes, const void *plane, int64_
     if (!codes || !plane || !W_hat) return QMV_E_NULL;
     if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K || !rows_fit(fmt, N)) return QMV_E_SHAPE;
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(W_hat, 16)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_dequant(fmt, codes, plane, N, K, W_hat, as_stream(stream)));
 }
 
@@ -221,6 +261,7 @@ qmv_status qmoe_route(const float *logits, int T, int E, int topk, int32_t *ids,
     if (!logits || !ids || !weights) return QMV_E_NULL;
     if (T < 1 || T > 64 || E < 1 || E > 4096 || topk < 1 || topk > 64 || topk > E) return QMV_E_SHAPE;
     if (!aligned(logits, 4) || !aligned(ids, 4) || !aligned(weights, 4)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_moe_route(logits, T, E, topk, ids, weights, as_stream(stream)));
 }
 
@@ -251,6 +292,7 @@ qmv_status gather_qmatvec(qmv_format fmt, const void *codes, const void *plane, 
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(ids, 4) ||
         !aligned(y, epi == QMV_EPI_SWIGLU ? 2 : 4) || (weights && !aligned(weights, 4)))
         return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_gather(fmt, codes, plane, E, N, K, x, xdt, x_per_slot, T, topk, ids, weights,
                                             epi, y, workspace, as_stream(stream)));
 }
@@ -269,6 +311,7 @@ qmv_status qmoe_ffn(qmv_format fmt, const void *gu_codes, const void *gu_plane, 
         !aligned(logits, 4) || !aligned(x, 16) || !aligned(ids, 4) || !aligned(weights, 4) || !aligned(h, 16) ||
         !aligned(y, 4))
         return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_moe_ffn(fmt, gu_codes, gu_plane, dn_codes, dn_plane, E, H, I, logits, x, T,
                                              topk, ids, weights, h, y, as_stream(stream)));
 }
@@ -288,6 +331,7 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
     if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(idx, 4) ||
         !aligned(val, 4) || !aligned(workspace, 8))
         return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_matvec_argmax(fmt, codes, plane, N, K, x, B, idx, val, workspace,
                                                    as_stream(stream)));
 }
@@ -298,6 +342,7 @@ qmv_status qpack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, i
     if (wdt != QMV_F16 && wdt != QMV_F32) return QMV_E_DTYPE;
     if (V < 1 || V > INT32_MAX || H < 1 || V > (int64_t(1) << 40) / H) return QMV_E_SHAPE;
     if (!aligned(W, wdt == QMV_F16 ? 2 : 4) || !aligned(scale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_pack_int8_rows(W, wdt, V, H, codes, scale, as_stream(stream)));
 }
 
@@ -308,6 +353,7 @@ qmv_status qembed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_
     if (T == 0) return QMV_OK;   // nothing to gather; ids and out may be NULL
     if (!ids || !out) return QMV_E_NULL;
     if (!aligned(codes, 8) || !aligned(scale, 2) || !aligned(ids, 4) || !aligned(out, 16)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_embed_gather_int8(codes, scale, V, H, ids, T, out, as_stream(stream)));
 }
 
@@ -317,6 +363,7 @@ qmv_status qmv_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *
     if (!buf || !sink) return QMV_E_NULL;
     if (bytes == 0 || bytes % 16 != 0) return QMV_E_SHAPE;
     if (!aligned(buf, 16) || !aligned(sink, 4)) return QMV_E_ALIGN;
+    forget_earlier_errors();
     return launch_status(qmv::launch_stream_read(buf, bytes, sink, as_stream(stream)));
 }
 

@@ -8,16 +8,16 @@ benchmark times (the same entry points on the same shapes):
   MoE         256 experts (gate/up 2 x 512 x 2048, down 2048 x 512, int4),
               top-8 routing, 1..8 tokens
 
-Where the oracle cannot do the whole tensor in seconds (k-means over 248320
-rows, the 256-expert slabs) it checks sampled rows / the routed experts one by
-one; everything else is compared in full."""
+The 256-expert slabs are checked on the routed experts one by one; everything
+else, the k-means packing of all 248320 lm_head rows included, is compared in
+full."""
 import numpy as np
 import pytest
 
 import oracle
 import quantized_decode_matvec_amd as qmv
 from quantized_decode_matvec_amd import workloads as wl
-from tests.gpu_helpers import RTOL, dev, host, rel_err, sample_rows
+from tests.gpu_helpers import RTOL, dev, host, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -46,26 +46,26 @@ def lm_head():
     c = wl.lm_head_km4()
     W = dev(c.W)
     codes, lut = qmv.qpack_km4(W)
-    return c, codes, lut
+    del W
+    # the oracle packs every row (OpenMP over rows on the host's cores)
+    oc, ol = oracle.pack_km4(c.W)
+    return c, codes, lut, oc, ol
 
 
-def test_km4_lm_head_pack_sampled_rows(lm_head):
-    c, codes, lut = lm_head
-    rows = sample_rows(c.W.shape[0], 256)
-    oc, ol = oracle.pack_km4(c.W[rows])
-    assert np.array_equal(oc, host(codes)[rows])
-    assert np.array_equal(ol, host(lut)[rows])
+def test_km4_lm_head_pack_all_rows(lm_head):
+    c, codes, lut, oc, ol = lm_head
+    gc, gl = host(codes), host(lut)
+    bad = np.nonzero(np.any(gc != oc, axis=1) | np.any(gl != ol, axis=1))[0]
+    assert bad.size == 0, "rows differing from the oracle: %s" % bad[:16]
 
 
 @pytest.mark.parametrize("B", [1, 8])
-def test_km4_lm_head_matvec_sampled_rows(lm_head, B):
-    c, codes, lut = lm_head
+def test_km4_lm_head_matvec_all_rows(lm_head, B):
+    c, codes, lut, oc, ol = lm_head
     x = c.x[:B]
     y = host(qmv.qmatvec_km4(codes, lut, dev(x)))
-    rows = sample_rows(c.W.shape[0], 512, seed=B)
-    oc, ol = oracle.pack_km4(c.W[rows])
     want = oracle.matvec("km4", oc, ol, x)
-    assert rel_err(y[:, rows], want) <= RTOL
+    assert rel_err(y, want) <= RTOL
 
 
 def test_int8_head_full_and_high_rows():
