@@ -286,6 +286,22 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
                           const void *x, int B, int32_t *idx, float *val,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* qmatvec_argmax without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and kernels as
+ * qmatvec_argmax; the workspace is a fixed device array of
+ * qmatvec_argmax_noalloc_max_bytes() bytes (16 MiB) inside the library, one
+ * copy per GPU, held until the process ends. Sizes whose workspace
+ * (qmatvec_argmax_workspace_bytes(N, B)) would not fit return
+ * QMV_E_WORKSPACE before anything is launched (the 248320-row head fits up
+ * to B = 8). Nothing is allocated or freed. Every call on one GPU uses that
+ * GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialized by the caller. The first call on a
+ * device looks up the array's address (QMV_E_LAUNCH if that fails). */
+qmv_status qmatvec_argmax_noalloc(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
+                                  const void *x, int B, int32_t *idx, float *val, void *stream);
+size_t qmatvec_argmax_noalloc_max_bytes(void);
+
 /* Embedding table packer: W [V][H] (fp16 or fp32) -> codes int8 [V][H] and
  * one fp16 scale per row: s = fp16(amax / 127), q = clamp(rint(w / s),
  * -127, 127) (an all-zero row has s = 0, q = 0). */

@@ -28,7 +28,8 @@ EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_
            "qpack_int8km", "qmatvec_int4", "qmatvec_fp4", "qmatvec_int8", "qmatvec_km4", "qmatvec_int4aff",
            "qmatvec_int8km", "qpack_km4o", "qmatvec_km4o", "qdequant",
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
-           "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qpack_int8_rows", "qembed_gather_int8",
+           "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qmatvec_argmax_noalloc",
+           "qmatvec_argmax_noalloc_max_bytes", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read")
 
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "qmoe_ffn": ([ci, P, P, P, P, ci, i64, i64, P, P, ci, ci, P, P, P, P, P], ci),
             "qmatvec_argmax_workspace_bytes": ([i64, ci], sz),
             "qmatvec_argmax": ([ci, P, P, i64, i64, P, ci, P, P, P, sz, P], ci),
+            "qmatvec_argmax_noalloc": ([ci, P, P, i64, i64, P, ci, P, P, P], ci),
+            "qmatvec_argmax_noalloc_max_bytes": ([], sz),
             "qpack_int8_rows": ([P, ci, i64, i64, P, P, P], ci),
             "qembed_gather_int8": ([P, P, i64, i64, P, i64, P, P], ci),
             "qmv_stream_read_sink_words": ([sz], sz),
@@ -536,6 +539,26 @@ def qmatvec_argmax(fmt, codes, plane, x, idx=None, val=None, workspace=None, str
     _check("qmatvec_argmax", lib().qmatvec_argmax(
         FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(x2), B, _ptr(idx), _ptr(val),
         _ptr(workspace), ws_bytes, _stream(stream)))
+    return idx, val
+
+
+def qmatvec_argmax_noalloc(fmt, codes, plane, x, idx=None, val=None, stream=None):
+    """qmatvec_argmax with its workspace in the library's fixed device array
+    (no device allocation by the library; idx and val may be passed in so the
+    call allocates nothing at all). Overlapping calls on one GPU race."""
+    torch = _torch()
+    fn = "qmatvec_argmax_noalloc"
+    if fmt not in FORMATS:
+        raise ValueError("%s: unknown format %r" % (fn, fmt))
+    N, K = _codes2d(fn, fmt, codes)
+    _dense_plane(fn, fmt, plane, N, K)
+    x2 = _as_batch(fn, x, K, allow_f32=False)
+    B = x2.shape[0]
+    idx = _y_out(fn, idx, (B,), torch.int32, codes, "idx")
+    val = _y_out(fn, val, (B,), torch.float32, codes, "val")
+    _on_gpu(fn, codes, plane, x2, idx, val)
+    _check(fn, lib().qmatvec_argmax_noalloc(FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(x2), B, _ptr(idx),
+                                            _ptr(val), _stream(stream)))
     return idx, val
 
 

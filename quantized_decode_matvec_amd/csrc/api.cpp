@@ -336,6 +336,24 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
                                                    as_stream(stream)));
 }
 
+qmv_status qmatvec_argmax_noalloc(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
+                                  const void *x, int B, int32_t *idx, float *val, void *stream) {
+    if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;
+    if (!codes || !plane || !x || !idx || !val) return QMV_E_NULL;
+    if (N < 1 || N > INT32_MAX || K < 32 || K % 32 != 0 || B < 1 || B > 8 || !rows_fit(fmt, N)) return QMV_E_SHAPE;
+    if (N > (int64_t(1) << 40) / K || !qmv::argmax_supported(fmt, K, B)) return QMV_E_SHAPE;
+    if (qmv::argmax_workspace_bytes(N, B) > qmv::scratch_bytes()) return QMV_E_WORKSPACE;
+    if (!aligned(codes, 16) || !aligned(plane, plane_alignment(fmt)) || !aligned(x, 16) || !aligned(idx, 4) ||
+        !aligned(val, 4))
+        return QMV_E_ALIGN;
+    void *ws = nullptr;
+    forget_earlier_errors();
+    if (qmv::scratch_address(&ws) != hipSuccess) return QMV_E_LAUNCH;
+    return launch_status(qmv::launch_matvec_argmax(fmt, codes, plane, N, K, x, B, idx, val, ws, as_stream(stream)));
+}
+
+size_t qmatvec_argmax_noalloc_max_bytes(void) { return qmv::scratch_bytes(); }
+
 qmv_status qpack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, int8_t *codes, uint16_t *scale,
                            void *stream) {
     if (!W || !codes || !scale) return QMV_E_NULL;

@@ -25,6 +25,9 @@ bool argmax_supported(int fmt, int64_t K, int B);
 size_t argmax_workspace_bytes(int64_t N, int B);
 hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,
                                 int B, int32_t *idx, float *val, void *workspace, hipStream_t st);
+// the fixed device scratch of the allocation-free argmax (scratch.hip)
+size_t scratch_bytes();
+hipError_t scratch_address(void **out);
 hipError_t launch_pack_int8_rows(const void *W, qmv_dtype wdt, int64_t V, int64_t H, int8_t *codes, uint16_t *scale,
                                  hipStream_t st);
 hipError_t launch_embed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H,
