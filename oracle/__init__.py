@@ -288,12 +288,12 @@ def pack_int8_rows(W):
 
 
 def embed_gather_int8(codes, scale, ids):
-    """out [T, H] fp16 bits (uint16) = fp16(codes[ids] * scale[ids])."""
+    """out [T, H] fp16 bits (uint16) = fp16(codes[ids] * scale[ids]); an id
+    outside [0, V) gives a zero row."""
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scale = np.ascontiguousarray(scale, dtype=np.uint16)
     ids = np.ascontiguousarray(np.asarray(ids).reshape(-1), dtype=np.int32)
     V, H = codes.shape
-    assert ids.min() >= 0 and ids.max() < V
     out = np.zeros((len(ids), H), np.uint16)
     lib().orc_embed_gather_int8(_p(codes), _p(scale), V, H, _p(ids), len(ids), _p(out))
     return out

@@ -325,13 +325,19 @@ void orc_pack_int8_rows(const float *W, int64_t V, int64_t H, int8_t *codes, uin
 }
 
 /* out[t][h] = fp16(q[ids[t]][h] * scale[ids[t]]): the product of an int8 and
-   an fp16 number is exact in fp64, so this is one rounding to fp16. */
+   an fp16 number is exact in fp64, so this is one rounding to fp16. Reading
+   (the pages do not cover it): an id outside [0, V) names no row and gives a
+   zero row. */
 void orc_embed_gather_int8(const int8_t *codes, const uint16_t *scale, int64_t V, int64_t H, const int32_t *ids,
                            int64_t T, uint16_t *out)
 {
-    (void)V;
     for (int64_t t = 0; t < T; t++) {
         const int64_t v = ids[t];
+        if (v < 0 || v >= V) {
+            for (int64_t h = 0; h < H; h++)
+                out[t * H + h] = 0;
+            continue;
+        }
         const double s = orc_f16_to_f64(scale[v]);
         for (int64_t h = 0; h < H; h++)
             out[t * H + h] = orc_f64_to_f16((double)codes[v * H + h] * s);

@@ -146,7 +146,7 @@ def test_embed_gather_bit_exact_and_out_of_range_ids():
     bad = np.array([5, -1, 1000, 7], np.int32)
     out = qmv.qembed_gather_int8(dq, ds, dev(bad))
     o = host(out).view(np.uint16)
-    assert np.array_equal(o[[0, 3]], oracle.embed_gather_int8(q, s, bad[[0, 3]]))
+    assert np.array_equal(o, oracle.embed_gather_int8(q, s, bad))   # ids outside [0, V): zero rows
     assert not o[[1, 2]].any()
     empty = qmv.qembed_gather_int8(dq, ds, torch.empty((0,), dtype=torch.int32, device="cuda"))
     assert empty.shape == (0, H)

@@ -632,6 +632,11 @@ def test_embed_gather_equals_numpy_fp16_product():
     out = oracle.embed_gather_int8(q, s, ids)
     want = q[ids].astype(np.float16) * s.view(np.float16)[ids][:, None]
     assert np.array_equal(out, want.view(np.uint16))
+    # ids that name no row (below 0, at or past V) give zero rows, the others as above
+    bad = np.array([-1, 3, 70, 1 << 30, 69], np.int32)
+    out = oracle.embed_gather_int8(q, s, bad)
+    assert not out[[0, 2, 3]].any()
+    assert np.array_equal(out[[1, 4]], oracle.embed_gather_int8(q, s, bad[[1, 4]]))
 
 
 @pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff"])
