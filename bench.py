@@ -156,6 +156,18 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+_CASES = {}
+
+
+def workload(name):
+    """A seeded synthetic workload from quantized_decode_matvec_amd.workloads,
+    generated once per run (the MoE slabs take about 30 s of numpy)."""
+    if name not in _CASES:
+        from quantized_decode_matvec_amd import workloads as wl
+        _CASES[name] = getattr(wl, name)()
+    return _CASES[name]
+
+
 def traffic_from_profiles(key):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources (otherwise None)."""
@@ -202,6 +214,78 @@ def cpu_baseline(c, x1):
             "sample": "km4 matvec over the first %d of 248320 lm_head rows (batch 1), %d repetitions, %.1f s"
                       % (rows, reps, el)}, {"cpu_oracle_1thread_GBps": round(gbs1, 4),
                                             "cpu_oracle_1thread_reps": reps1}
+
+
+def cpu_configs(lm, quick):
+    """The oracle as it stands (untuned) on each workload, on all cores and on
+    one thread: packing time and matvec rate in GB/s of that workload's
+    algorithmic weight bytes. The lm_head and the int8 head are sampled by
+    rows (the first 4096 / 8192 rows; rows are independent); the MoE layer
+    runs one token through its 8 routed experts (packing only those). The
+    tiny int4 and the fp4 4096 x 4096 workloads run whole. With `quick`, the
+    int8 head and the MoE layer are left out (they are not generated)."""
+    import oracle
+
+    cores = oracle.num_threads()
+    out = {"cpu_cores": cores}
+
+    def timed_host(fn, min_s):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            r = fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return r, el / reps
+
+    def dense(name, fmt, W, x, note):
+        nb = algo_bytes(fmt, *W.shape)
+        for thr, tag in ((cores, "all"), (1, "1thr")):
+            oracle.set_num_threads(thr)
+            try:
+                (codes, plane), tp = timed_host(lambda: oracle.pack(fmt, W), 0.0)
+                _, tm = timed_host(lambda: oracle.matvec(fmt, codes, plane, x), 0.3)
+            finally:
+                oracle.set_num_threads(cores)
+            out["cpu_%s_%s_pack_ms" % (name, tag)] = round(tp * 1e3, 2)
+            out["cpu_%s_%s_matvec_ms" % (name, tag)] = round(tm * 1e3, 3)
+            out["cpu_%s_%s_matvec_GBps" % (name, tag)] = round(nb / tm / 1e9, 4)
+        out["cpu_%s_sample" % name] = note
+
+    c1 = workload("tiny_int4")
+    dense("tiny_int4", "int4", c1.W, c1.x, "whole 256x512, x fp32 [1, 512]")
+    c2 = workload("fp4_square")
+    dense("fp4_4096sq", "fp4", c2.W, c2.x[:1], "whole 4096x4096, batch 1")
+    dense("km4_lm_head", "km4", lm.W[:4096], lm.x[:1], "first 4096 of 248320 rows, batch 1")
+    if not quick:
+        c4 = workload("int8_head")
+        dense("int8_head", "int8", c4.W[:8192], c4.x, "first 8192 of 130560 rows, batch 1")
+        c5 = workload("moe")
+        ids, w = oracle.moe_route(c5.logits[:1], c5.topk)
+        E, I2, H = c5.W_gate_up.shape
+        I = I2 // 2
+        experts = sorted(set(int(e) for e in ids.reshape(-1)))
+        per_expert = algo_bytes("int4", I2, H) + algo_bytes("int4", H, I)
+        for thr, tag in ((cores, "all"), (1, "1thr")):
+            oracle.set_num_threads(thr)
+            try:
+                t0 = time.perf_counter()
+                guc = np.zeros((E, I2, H // 2), np.uint8)
+                gus = np.zeros((E, I2, H // 32), np.uint16)
+                dnc = np.zeros((E, H, I // 2), np.uint8)
+                dns = np.zeros((E, H, I // 32), np.uint16)
+                for e in experts:
+                    guc[e], gus[e] = oracle.pack_int4(c5.W_gate_up[e])
+                    dnc[e], dns[e] = oracle.pack_int4(c5.W_down[e])
+                tp = time.perf_counter() - t0
+                _, tm = timed_host(lambda: oracle.moe_ffn(guc, gus, dnc, dns, c5.x[:1], ids, w), 0.3)
+            finally:
+                oracle.set_num_threads(cores)
+            out["cpu_moe_int4_T1_%s_pack_ms" % tag] = round(tp * 1e3, 2)
+            out["cpu_moe_int4_T1_%s_ms" % tag] = round(tm * 1e3, 3)
+            out["cpu_moe_int4_T1_%s_GBps" % tag] = round(len(experts) * per_expert / tm / 1e9, 4)
+        out["cpu_moe_int4_T1_sample"] = "one token, its %d routed experts packed" % len(experts)
+    return out
 
 
 def main():
@@ -400,6 +484,8 @@ def main():
         log("cpu baseline (oracle)")
         result["cpu_baseline"], one = cpu_baseline(c, c.x[:1])
         extras.update(one)
+        log("cpu oracle on each workload")
+        extras.update(cpu_configs(c, args.quick))
     print(json.dumps(result), flush=True)
 
 
@@ -410,7 +496,7 @@ def bench_fp4_square(args):
     import torch
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
-    c = wl.fp4_square()
+    c = workload("fp4_square")
     W = torch.from_numpy(c.W).cuda()
     p0 = qmv.qpack_fp4(W)
     del W
@@ -431,7 +517,7 @@ def bench_int8_head(args):
     import torch
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
-    c = wl.int8_head()
+    c = workload("int8_head")
     W = torch.from_numpy(c.W).cuda()
     x = torch.from_numpy(c.x).cuda()
     p0 = qmv.qpack_int8(W)
@@ -494,7 +580,7 @@ def bench_moe(args, fmts=("int4", "int4aff", "int8km"), tokens=(1, 4, 8)):
     import torch
     import quantized_decode_matvec_amd as qmv
     from quantized_decode_matvec_amd import workloads as wl
-    c = wl.moe()
+    c = workload("moe")
     E, I2, H = c.W_gate_up.shape
     I = I2 // 2
     lg_all = np.random.default_rng(1).standard_normal((MOE_CALLS, max(tokens), E), dtype=np.float32)
