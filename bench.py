@@ -179,7 +179,7 @@ def traffic_from_profiles(key):
         rec = json.load(open(path)).get(key)
     except ValueError:
         return None
-    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256") != kernel_source_hash(rec.get("kernel_sources") or None):
         return None
     return rec["traffic_bytes"]
 

@@ -4,7 +4,8 @@
     python -m quantized_decode_matvec_amd.rocprof_summary grid KERNEL_TRACE_CSV [--match SUBSTR]
     python -m quantized_decode_matvec_amd.rocprof_summary traffic --kernel SUBSTR --key NAME \\
         --fetch FETCH_CSV --write WRITE_CSV --calib-fetch CF_CSV --calib-write CW_CSV \\
-        [--calib-kernel copyBuffer] [--calib-bytes 1073741824] [--out profiles/traffic.json]
+        [--grid THREADS] [--sources FILE ...] [--calib-kernel copyBuffer] [--calib-bytes 1073741824] \\
+        [--out profiles/traffic.json]
 
 `grid` groups a kernel trace by kernel and launch grid (one line per distinct
 launch shape, e.g. per token count of the MoE kernels) with the median and
@@ -26,22 +27,30 @@ import json
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ("csrc/matvec.hip", "csrc/qmv_device.h")
+KERNEL_SOURCES = ("csrc/matvec.hip", "csrc/qmv_device.h")   # the batch 1-2 matvec kernels
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """SHA-256 over the sources a kernel is built from (a counter record taken
+    on other sources no longer describes the kernel)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    sources = sources or KERNEL_SOURCES
+    for rel in sources:
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def _per_kernel(path, counter):
+def _per_kernel(path, counter, grid_size=None):
+    """Counter values per kernel name; with `grid_size`, only dispatches of that
+    total grid size (threads), e.g. one token count of the MoE kernels."""
     vals = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
-        if r["Counter_Name"] == counter:
-            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        if r["Counter_Name"] != counter:
+            continue
+        if grid_size is not None and int(r["Grid_Size"]) != grid_size:
+            continue
+        vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
     return vals
 
 
@@ -91,8 +100,8 @@ def window(path, match, last):
 
 
 def traffic(args):
-    fetch_name, fetch_kib, nf = _pick(_per_kernel(args.fetch, "FETCH_SIZE"), args.kernel)
-    write_name, write_kib, nw = _pick(_per_kernel(args.write, "WRITE_SIZE"), args.kernel)
+    fetch_name, fetch_kib, nf = _pick(_per_kernel(args.fetch, "FETCH_SIZE", args.grid), args.kernel)
+    write_name, write_kib, nw = _pick(_per_kernel(args.write, "WRITE_SIZE", args.grid), args.kernel)
     _, cf_kib, _ = _pick(_per_kernel(args.calib_fetch, "FETCH_SIZE"), args.calib_kernel)
     _, cw_kib, _ = _pick(_per_kernel(args.calib_write, "WRITE_SIZE"), args.calib_kernel)
     known_kib = args.calib_bytes / 1024.0
@@ -101,7 +110,9 @@ def traffic(args):
     write_b = write_kib / w_fac * 1024.0
     rec = {
         "kernel": fetch_name,
-        "kernel_source_sha256": kernel_source_hash(),
+        "grid_size": args.grid,
+        "kernel_sources": list(args.sources),
+        "kernel_source_sha256": kernel_source_hash(args.sources),
         "fetch_kib_per_dispatch": round(fetch_kib, 1), "fetch_dispatches": nf,
         "write_kib_per_dispatch": round(write_kib, 1), "write_dispatches": nw,
         "calibration": {"kernel": args.calib_kernel, "bytes": args.calib_bytes,
@@ -143,6 +154,9 @@ def main():
     t.add_argument("--calib-write", required=True)
     t.add_argument("--calib-kernel", default="copyBuffer")
     t.add_argument("--calib-bytes", type=int, default=1 << 30)
+    t.add_argument("--grid", type=int, help="only dispatches of this total grid size (threads)")
+    t.add_argument("--sources", nargs="+", default=list(KERNEL_SOURCES),
+                   help="sources the kernel is built from, relative to the package")
     t.add_argument("--out")
     a = ap.parse_args()
     if a.cmd == "stats":
