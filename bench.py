@@ -325,9 +325,11 @@ def main():
     copies = [(codes, lut)] + [(codes.clone(), lut.clone()) for _ in range(args.copies - 1)]
     y = torch.empty((8, N_ROWS), dtype=torch.float32, device="cuda")
 
+    # checked once; each call then only launches (a decode loop's hot path)
+    calls1 = [qmv.qmatvec_call("km4", cc, ll, x1, y=y[:1]) for cc, ll in copies]
+
     def step(i):
-        cc, ll = copies[i % len(copies)]
-        qmv.qmatvec_km4(cc, ll, x1, y=y[:1])
+        calls1[i % len(calls1)]()
 
     gpu_warm(step)
     ms = timed(step, args.steps, args.warmup)
@@ -341,19 +343,26 @@ def main():
     extras = {"km4_pack_ms": round(pack_ms, 3)}
     if p50 is not None:
         extras.update({"km4_B1_us_p10": p10, "km4_B1_us_p50": p50, "km4_B1_us_p90": p90})
-    if not args.only_metric:
-        # practical read ceiling over the same footprint
-        buf = torch.empty((len(copies), nbytes // 16 * 16), dtype=torch.uint8, device="cuda")
+    def stream_rate(nb):
+        """GB/s of the plain streaming read over `nb` bytes, cycling the same
+        number of buffers as the weight copies (the read each matvec is set
+        against: same bytes, same cache behaviour)."""
+        buf = torch.empty((len(copies), nb // 16 * 16), dtype=torch.uint8, device="cuda")
         buf.random_(0, 255)
         sink = torch.empty((int(qmv.lib().qmv_stream_read_sink_words(buf[0].numel())),), dtype=torch.int32,
                            device="cuda")
         ms_r = timed(lambda i: qmv.qmv_stream_read(buf[i % len(copies)], sink=sink), args.steps, args.warmup)
-        extras["stream_read_GBps"] = round(buf[0].numel() / (ms_r * 1e-3) / 1e9, 1)
-        del buf
-        log("stream read ceiling %.1f GB/s" % extras["stream_read_GBps"])
+        rate = buf[0].numel() / (ms_r * 1e-3) / 1e9
+        del buf, sink
+        return round(rate, 1)
 
-        ms8 = timed(lambda i: qmv.qmatvec_km4(copies[i % len(copies)][0], copies[i % len(copies)][1], x8, y=y),
-                    args.steps // 2, args.warmup)
+    if not args.only_metric:
+        # plain streaming read over the same footprint
+        extras["stream_read_GBps"] = stream_rate(nbytes)
+        log("stream read %.1f GB/s" % extras["stream_read_GBps"])
+
+        calls8 = [qmv.qmatvec_call("km4", cc, ll, x8, y=y) for cc, ll in copies]
+        ms8 = timed(lambda i: calls8[i % len(calls8)](), args.steps // 2, args.warmup)
         extras["km4_B8_us"] = round(ms8 * 1e3, 2)
         extras["km4_B8_GBps"] = round(nbytes / (ms8 * 1e-3) / 1e9, 1)
 
@@ -366,18 +375,18 @@ def main():
         for fmt in ("fp4", "int4", "int4aff", "int8km"):
             pk = [qmv.qpack(fmt, W)]
             pk += [(a.clone(), b.clone()) for a, b in [pk[0]] * (len(copies) - 1)]
-            msf = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x1, y=y[:1]),
-                        args.steps, args.warmup)
+            cf = [qmv.qmatvec_call(fmt, a, b, x1, y=y[:1]) for a, b in pk]
+            msf = timed(lambda i: cf[i % len(cf)](), args.steps, args.warmup)
             nb = algo_bytes(fmt, N_ROWS, K_DIM)
             extras["%s_B1_us" % fmt] = round(msf * 1e3, 2)
             extras["%s_B1_GBps" % fmt] = round(nb / (msf * 1e-3) / 1e9, 1)
+            extras["%s_stream_read_GBps" % fmt] = stream_rate(nb)
             for bb in (4, 8):
-                xb = x8[:bb]
-                msb = timed(lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], xb, y=y[:bb]),
-                            args.steps // 2, args.warmup)
+                cb = [qmv.qmatvec_call(fmt, a, b, x8[:bb], y=y[:bb]) for a, b in pk]
+                msb = timed(lambda i: cb[i % len(cb)](), args.steps // 2, args.warmup)
                 extras["%s_B%d_us" % (fmt, bb)] = round(msb * 1e3, 2)
                 extras["%s_B%d_GBps" % (fmt, bb)] = round(nb / (msb * 1e-3) / 1e9, 1)
-            del pk
+            del pk, cf, cb
         # km4 rows plus 16 int8 outliers per row (0.8% of the weights)
         e0.record()
         pko = qmv.qpack_km4o(W, 16)
@@ -440,6 +449,14 @@ def main():
                 extras["%s_%s_us" % (name, fmt)] = round(msq * 1e3, 2)
                 extras["%s_%s_GBps" % (name, fmt)] = round(algo_bytes(fmt, n, k) / (msq * 1e-3) / 1e9, 1)
                 del pk
+            # the floor for this size: the plain streaming read of the fp4
+            # footprint, 128 distinct buffers in the same graphs
+            nbq = algo_bytes("fp4", n, k) // 16 * 16
+            rb = torch.empty((128, nbq), dtype=torch.uint8, device="cuda")
+            rsink = torch.empty((int(qmv.lib().qmv_stream_read_sink_words(nbq)),), dtype=torch.int32, device="cuda")
+            msr = timed_graph(lambda i: qmv.qmv_stream_read(rb[i % 128], sink=rsink), 4 * args.steps, per_graph=128)
+            extras["%s_stream_read_fp4_bytes_us" % name] = round(msr * 1e3, 2)
+            del rb
         # one GPU's share of an lm_head split by rows over 8 GPUs (31040 x 2048):
         # the 32 distinct row slices of the weight copies, so no call finds its
         # codes in the cache; matvec and the fused argmax, in HIP graphs
@@ -460,6 +477,15 @@ def main():
             extras.update(bench_moe(args))
 
     traffic = traffic_from_profiles("km4_lm_head_b1")
+    if not args.only_metric:
+        # the fastest whole-HBM read of this run (the plain streaming read over
+        # each format's footprint, or a batch-1 matvec when one reads faster):
+        # the practical ceiling the batch-1 kernels are judged against
+        reads = {k: v for k, v in extras.items()
+                 if k.endswith("stream_read_GBps") or k.endswith("_B1_GBps") or k == "int8_head_GBps"}
+        best = max(reads, key=reads.get)
+        extras["best_read_GBps"], extras["best_read_kernel"] = reads[best], best
+        extras["km4_B1_frac_of_best_read"] = round(gbs / reads[best], 4)
     result = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -523,7 +549,8 @@ def bench_int8_head(args):
     p0 = qmv.qpack_int8(W)
     del W
     pk = [p0] + [(p0[0].clone(), p0[1].clone()) for _ in range(2)]
-    ms = timed(lambda i: qmv.qmatvec_int8(pk[i % 3][0], pk[i % 3][1], x), args.steps, args.warmup)
+    cs = [qmv.qmatvec_call("int8", a, b, x) for a, b in pk]
+    ms = timed(lambda i: cs[i % 3](), args.steps, args.warmup)
     nb = algo_bytes("int8", *c.W.shape)
     return {"int8_head_us": round(ms * 1e3, 2), "int8_head_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
 
@@ -557,7 +584,8 @@ def run_case(args):
             fn = lambda i: qmv.qmatvec_argmax(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x, idx=idx, val=val,
                                               workspace=ws)
         else:
-            fn = lambda i: qmv.qmatvec(fmt, pk[i % len(pk)][0], pk[i % len(pk)][1], x, y=y)
+            cs = [qmv.qmatvec_call(fmt, a, b, x, y=y) for a, b in pk]
+        fn = lambda i: cs[i % len(cs)]()
         gpu_warm(fn)
         ms = timed(fn, args.steps, args.warmup)
         res.update({"us": round(ms * 1e3, 2), "GBps": round(algo_bytes(fmt, N_ROWS, K_DIM) / (ms * 1e-3) / 1e9, 1)})

@@ -302,7 +302,8 @@ def _y_out(fn, y, shape, dtype, like, name="y"):
     return y
 
 
-def _matvec(name, fmt, codes, plane, x, y, stream):
+def _matvec_args(name, fmt, codes, plane, x, y):
+    """Checked arguments of a matvec call (all but the stream) and its output."""
     torch = _torch()
     N, K = _codes2d(name, fmt, codes)
     _dense_plane(name, fmt, plane, N, K)
@@ -310,9 +311,34 @@ def _matvec(name, fmt, codes, plane, x, y, stream):
     B = x2.shape[0]
     y = _y_out(name, y, (B, N), torch.float32, codes)
     _on_gpu(name, codes, plane, x2, y)
-    fn = getattr(lib(), name)
-    _check(name, fn(_ptr(codes), _ptr(plane), N, K, _ptr(x2), _dt(x2), B, _ptr(y), _stream(stream)))
+    return (_ptr(codes), _ptr(plane), N, K, _ptr(x2), _dt(x2), B, _ptr(y)), (codes, plane, x2), y
+
+
+def _matvec(name, fmt, codes, plane, x, y, stream):
+    args, _, y = _matvec_args(name, fmt, codes, plane, x, y)
+    _check(name, getattr(lib(), name)(*args, _stream(stream)))
     return y
+
+
+def qmatvec_call(fmt, codes, plane, x, y=None, stream=None):
+    """Check the arguments of qmatvec(fmt, codes, plane, x, y) once and return a
+    function of no arguments that launches that same matvec (same buffers,
+    output y) each time it is called, on `stream` or else on the current
+    stream: for a decode loop that calls one matvec many times, without the
+    per-call checks. The returned function keeps the tensors alive; their
+    contents may change between calls, their storage must not."""
+    name = "qmatvec_" + fmt
+    args, keep, y = _matvec_args(name, fmt, codes, plane, x, y)
+    fn = getattr(lib(), name)
+    st = None if stream is None else ctypes.c_void_p(stream)
+    torch = _torch()
+
+    def call():
+        _check(name, fn(*args, st if st is not None else ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        return y
+
+    call.tensors = keep + (y,)
+    return call
 
 
 def qmatvec_int4(codes, scale, x, y=None, stream=None):

@@ -72,6 +72,17 @@ def test_matvec_checks(fmt):
     raises(ValueError, "out has shape", qmv.qdequant, fmt, c, p, out=z(N, K - 1, dtype=f32))
 
 
+@pytest.mark.parametrize("fmt", ["km4", "int4"])
+def test_prepared_matvec_checks_once_like_matvec(fmt):
+    N, K = 64, 128
+    c, p = codes_for(fmt, N, K), PLANES[fmt](N, K)
+    x = z(2, K)
+    raises(ValueError, "GPU memory", qmv.qmatvec_call, fmt, c, p, x)
+    raises(ValueError, "plane holds", qmv.qmatvec_call, fmt, c, PLANES[fmt](N // 2, K), x)
+    raises(ValueError, "y has shape", qmv.qmatvec_call, fmt, c, p, x, y=z(2, N - 1, dtype=f32))
+    raises(ValueError, "x has shape", qmv.qmatvec_call, fmt, c, p, z(2, K - 32))
+
+
 def test_km4o_checks():
     N, K, P = 16, 64, 4
     c, l = codes_for("km4", N, K), PLANES["km4"](N, K)

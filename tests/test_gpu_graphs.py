@@ -90,3 +90,33 @@ def test_argmax_graph_replays_equal_eager(fmt):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(host(idx), want[0]) and np.array_equal(host(val), want[1])
+
+
+@pytest.mark.parametrize("fmt", ["km4", "fp4", "int8km"])
+@pytest.mark.parametrize("B", [1, 8])
+def test_prepared_call_equals_matvec(fmt, B):
+    """qmatvec_call checks once and relaunches the same matvec: each call equals
+    qmatvec on the same inputs bit for bit, also after x is rewritten in place
+    and when called on another stream."""
+    import torch
+    N, K = 8192, 2048
+    print("prepared", fmt, B, flush=True)
+    c = wl.small_dense("km4", N, K, batch=B, seed=7 + B)
+    codes, plane = qmv.qpack(fmt, dev(c.W))
+    x = dev(c.x[:B])
+    y = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    call = qmv.qmatvec_call(fmt, codes, plane, x, y=y)
+    for i in range(3):
+        x.copy_(dev(np.random.default_rng(i).standard_normal((B, K)).astype(np.float16)))
+        want = host(qmv.qmatvec(fmt, codes, plane, x))
+        y.fill_(float("nan"))
+        assert call() is y
+        assert np.array_equal(host(y), want), (fmt, B, i)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    y.fill_(float("nan"))
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), want)
