@@ -299,6 +299,109 @@ __global__ __launch_bounds__(64 * WAVES) void mv_fast(const uint8_t *__restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batch 2-8 on matrices short of the tall shape, scale formats (int4, fp4,
+// int8), rows of whole 64-chunk strides: x staged once per workgroup in LDS.
+// mv_fast holds every x slice a lane needs in registers (CPL * BT * XW words,
+// 128 at fp4 4096 x 4096 and B = 4, one wave per SIMD) and every wave loads
+// its own copy of x from L2, four times its code bytes there. Here the eight
+// waves of a workgroup share one LDS copy of x ([BT][chunk] slots of XW words
+// plus 4 words of padding, so the 16-byte reads of consecutive lanes hit
+// distinct banks), each wave owns one row, and a lane reads each x slice just
+// before the chunks that use it. The arithmetic and its order per row are
+// mv_fast's, so results are bit-identical to it.
+// ---------------------------------------------------------------------------
+constexpr int kXsWaves = 8;   // waves per workgroup, one row each
+
+template <int FMT>
+__host__ __device__ constexpr int xstage_pitch() { return ChunkTraits<FMT>::kXWords + 4; }   // words per x slot
+
+template <int FMT, int BT, int CPL>
+__global__ __launch_bounds__(64 * kXsWaves) void mv_xstage(const uint8_t *__restrict__ codes,
+                                                           const void *__restrict__ plane, int64_t N, int K,
+                                                           const _Float16 *__restrict__ x, int B,
+                                                           float *__restrict__ y, uint64_t *__restrict__ hdr) {
+    static_assert(FMT == INT4 || FMT == FP4 || FMT == INT8, "scale formats only");
+    extern __shared__ __align__(16) uint32_t xl[];
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    constexpr int PITCH = xstage_pitch<FMT>();
+    constexpr int CPR = 64 * CPL;   // chunks per row (the launch checks K)
+    const int nb = K / 32;
+    const uint32_t row_bytes = (FMT == INT8) ? (uint32_t)K : (uint32_t)K / 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (hdr != nullptr && blockIdx.x == 0 && tid < kArgmaxHeader) hdr[tid] = 0;
+    for (int i = tid; i < BT * CPR; i += 64 * kXsWaves) {
+        const int b = i / CPR, c = i - b * CPR;
+        uint32_t w[XW];
+        load_x_slice<FMT>(x + (size_t)(b < B ? b : 0) * K, c, b < B, w);   // rows b >= B are zero
+        uint4 *dst = reinterpret_cast<uint4 *>(xl + i * PITCH);
+#pragma unroll
+        for (int q = 0; q < XW / 4; q++) dst[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+    }
+    __syncthreads();
+    const int64_t row = (int64_t)blockIdx.x * kXsWaves + wave;
+    if (row >= N) return;
+    uint4 cw[CPL];
+    float sc[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+        const int c = lane + 64 * j;
+        cw[j] = load_stream16(codes + row * (int64_t)row_bytes + (uint32_t)c * 16u);
+        if constexpr (FMT == FP4)
+            sc[j] = e8m0_to_f32(reinterpret_cast<const uint8_t *>(plane)[row * nb + c]);
+        else
+            sc[j] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(plane)[row * nb + (FMT == INT8 ? c / 2 : c)]);
+    }
+    float acc[BT];
+#pragma unroll
+    for (int b = 0; b < BT; b++) acc[b] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+#pragma unroll
+        for (int b = 0; b < BT; b++) {
+            uint32_t xs[XW];
+            const uint4 *src = reinterpret_cast<const uint4 *>(xl + (b * CPR + lane + 64 * j) * PITCH);
+#pragma unroll
+            for (int q = 0; q < XW / 4; q++) {
+                const uint4 v = src[q];
+                xs[4 * q] = v.x;
+                xs[4 * q + 1] = v.y;
+                xs[4 * q + 2] = v.z;
+                xs[4 * q + 3] = v.w;
+            }
+            float d;
+            if constexpr (FMT == FP4) d = chunk_dot_fp4(cw[j], xs);
+            else if constexpr (FMT == INT4) d = chunk_dot_int4(cw[j], xs);
+            else d = chunk_dot_int8(cw[j], xs);
+            acc[b] = __builtin_fmaf(d, sc[j], acc[b]);
+        }
+    }
+    using Red = GroupReduce<BT, 64>;
+    Red::run(acc, lane);
+    if (Red::writer(lane)) {
+        const int base = Red::base(lane);
+#pragma unroll
+        for (int j = 0; j < Red::live; j++) {
+            const int b = base + j;
+            if (b < B) y[(size_t)b * N + row] = acc[j];
+        }
+    }
+}
+
+// LDS bytes of mv_xstage's x copy; 0 where the kernel does not take the shape
+// (formats with tables or a bias, rows not a whole number of 64-chunk strides,
+// more than 64 KiB of x).
+template <int FMT, int BT, int CPL>
+static size_t xstage_lds(int K) {
+    if constexpr (FMT != INT4 && FMT != FP4 && FMT != INT8) return 0;
+    else {
+        const int cpr = (FMT == INT8) ? K / 16 : K / 32;
+        if (cpr != 64 * CPL) return 0;
+        const size_t b = (size_t)BT * cpr * xstage_pitch<FMT>() * 4;
+        return b <= 64 * 1024 ? b : 0;
+    }
+}
+
 // Argmax over each batch row of y [B][N] -> (index, value). A grid of (G, B)
 // workgroups, G <= kArgmaxGroups: each takes every G-th stretch of
 // kArgmaxStretch values of its row, sixteen independent loads per thread in
@@ -569,6 +672,20 @@ static hipError_t launch_fast(const uint8_t *codes, const void *plane, int64_t N
         // Batch 5-8 (matrices the matrix-core path leaves here) takes 2 rows,
         // km4 4 from 4096 rows (4096 x 2048 at B = 8: 6.4 us against 7.2).
         if (N < kTallRows) {
+            // x staged in LDS (measured on MI355X in HIP graphs, against this
+            // function's register-x shapes below: fp4 4096 x 4096 at B = 2 / 3 / 4:
+            // 4.31 / 5.08 / 5.17 us against 4.77 / 5.96 / 6.12; int4 8192 x 4096
+            // at B = 4: 8.43 against 13.07; fp4 4096 x 2048 at B = 8: 4.80
+            // against 6.40; int8 within 2% either way at 2048 rows)
+            if constexpr (!OUTL && (CPL == 1 || CPL == 2 || CPL == 4) && (FMT == INT4 || FMT == FP4 || FMT == INT8)) {
+                const size_t lds = xstage_lds<FMT, BT, CPL>(K);
+                if (lds > 0) {
+                    const int64_t grid = (N + kXsWaves - 1) / kXsWaves;
+                    hipLaunchKernelGGL((mv_xstage<FMT, BT, CPL>), dim3((unsigned)grid), dim3(64 * kXsWaves), lds, st,
+                                       codes, plane, N, K, reinterpret_cast<const _Float16 *>(x), B, y, hdr);
+                    return hipGetLastError();
+                }
+            }
             if (N >= 4096 && ((!TABLE && BT <= 4) || (FMT == KM4 && BT == 8)))
                 return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 4, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);
             if (N >= 2048) return launch_shape<FMT, BT, LPR, CPL, OUTL, false, 2, 1>(codes, plane, N, K, x, B, y, st, hdr, ol);
