@@ -481,6 +481,11 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     // 7.4 against 8.3 / 8.9; km4 5.9 / 6.4 against 8.6 / 9.2; int8 k-means
     // 6.4 / 6.5 against 12.9 / 13.5)
     if (N <= 4096 && K > 1024 && K <= 2048) return false;
+    // the dot2 kernel with x staged in LDS (int4, fp4, int8 at K = 2048) is
+    // faster up to 8192 rows too (8192 x 2048 at B = 8, HIP graphs: fp4 6.7
+    // against 7.8 us, int4 7.4 against 8.9, int8 8.2 against 11.3; at 16384
+    // rows the matrix cores win: fp4 8.5 against 11.2)
+    if (N <= 8192 && B >= 5 && K == 2048 && (fmt == INT4 || fmt == FP4 || fmt == INT8)) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces

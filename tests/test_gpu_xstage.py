@@ -4,7 +4,8 @@ fp4, int8; rows of whole 64-chunk strides: 4-bit K = 2048, 4096, 8192, int8
 K = 1024, 2048, 4096; at most 64 KiB of staged x): full output against the
 oracle, row counts that leave a partial last workgroup, a single row, and the
 batch widths between the compiled ones (B = 3 runs the B = 4 kernel with a
-zero row, B = 5-7 the B = 8 one). The fused argmax on the same kernel zeroes
+zero row, B = 5-7 the B = 8 one; at K = 2048 B = 5-8 stays on this kernel up
+to 8192 rows instead of the matrix cores). The fused argmax on the same kernel zeroes
 its reduction header there; its result must equal the argmax of the matvec."""
 import numpy as np
 import pytest
@@ -17,7 +18,8 @@ from tests.gpu_helpers import RTOL, dev, host, rel_err
 pytestmark = pytest.mark.gpu
 
 CASES = [("int4", 4097, 4096), ("fp4", 4097, 4096), ("int4", 1, 4096), ("fp4", 2051, 8192), ("int4", 2051, 8192),
-         ("int8", 4097, 2048), ("int8", 2051, 4096), ("int8", 3, 1024), ("fp4", 4101, 2048), ("int4", 4101, 2048)]
+         ("int8", 4097, 2048), ("int8", 2051, 4096), ("int8", 3, 1024), ("fp4", 4101, 2048), ("int4", 4101, 2048),
+         ("fp4", 8191, 2048), ("int8", 8185, 2048)]
 
 
 @pytest.mark.parametrize("fmt,N,K", CASES)
