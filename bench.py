@@ -585,7 +585,7 @@ def run_case(args):
                                               workspace=ws)
         else:
             cs = [qmv.qmatvec_call(fmt, a, b, x, y=y) for a, b in pk]
-        fn = lambda i: cs[i % len(cs)]()
+            fn = lambda i: cs[i % len(cs)]()
         gpu_warm(fn)
         ms = timed(fn, args.steps, args.warmup)
         res.update({"us": round(ms * 1e3, 2), "GBps": round(algo_bytes(fmt, N_ROWS, K_DIM) / (ms * 1e-3) / 1e9, 1)})
