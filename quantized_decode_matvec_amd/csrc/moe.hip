@@ -620,8 +620,133 @@ static hipError_t launch_expert_major(GatherArgs a, int umax, hipStream_t st) {
     return launch_expert_major_r<FMT, LPR, CPL, EPI, FUSED, R>(a, umax, st);
 }
 
+// ---------------------------------------------------------------------------
+// Slot-split down projection + combine, topk <= kSplitSlots: a workgroup of
+// kSplitSlots waves owns ROWS rows of token t, wave s computes slot s's
+// weighted row sums w_s * (W_e h_{t,s}) for those rows (its own expert, its
+// own loads in flight), and the per-row partials meet in LDS, where they are
+// summed in slot order. The token-major kernel above runs one wave per row
+// tile and loads all slots of a batch in that wave: at a few tokens that is
+// half a wave per SIMD. Deterministic: the order of every sum is fixed.
+// ---------------------------------------------------------------------------
+constexpr int kSplitSlots = 8;
+
+template <int FMT, int LPR, int CPL, int R>
+__global__ __launch_bounds__(64 * kSplitSlots) void combine_split_kernel(GatherArgs a) {
+    constexpr int RPW = kWave / LPR;
+    constexpr int XW = ChunkTraits<FMT>::kXWords;
+    constexpr int ROWS = R * RPW;
+    constexpr bool AFF = (FMT == INT4AFF);
+    constexpr bool KM8 = (FMT == INT8KM);
+    static_assert(!KM8 || 32 % ROWS == 0, "int8km: a workgroup's rows within one group");
+    constexpr int LUT_HALVES = (FMT == KM4) ? ROWS * 16 : (KM8 ? 256 : 1);   // per wave (slot)
+    __shared__ _Float16 lut_lds[kSplitSlots * LUT_HALVES];
+    __shared__ float part[kSplitSlots][ROWS];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane % LPR;
+    const int rsub = lane / LPR;
+    const int t = blockIdx.y;
+    const int K = a.K;
+    const int cpr = (FMT == INT8 || KM8) ? K / 16 : K / 32;
+    const int nb = K / 32;
+    const uint32_t row_bytes = (uint32_t)code_row_bytes<FMT>(K);
+    const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+    if (row0 >= a.N) return;   // uniform over the workgroup
+    const int last = (int)((a.N - 1 - row0) < ROWS - 1 ? (a.N - 1 - row0) : ROWS - 1);
+    // waves past topk repeat the last slot; their partials are not summed
+    const int s = wave < a.topk ? wave : a.topk - 1;
+    const int e0 = a.ids[t * a.topk + s];
+    const int e = e0 < 0 ? 0 : (e0 < a.E ? e0 : a.E - 1);   // clamped, as in the other gather kernels
+    const float ws = a.weights[t * a.topk + s];
+    const uint8_t *codes_e;
+    const void *plane_e;
+    expert_slabs<FMT>(a.codes, a.plane, e, a.N, K, codes_e, plane_e);
+    uint4 cw[R][CPL];
+    float sc[R][CPL];
+    float bi[AFF ? R : 1][AFF ? CPL : 1];
+#pragma unroll
+    for (int g = 0; g < R; g++) {
+        int rr = g * RPW + rsub;
+        rr = rr <= last ? rr : last;
+        const int64_t row = row0 + rr;
+#pragma unroll
+        for (int j = 0; j < CPL; j++) {
+            const int c = sub + LPR * j;
+            const int cc = c < cpr ? c : 0;
+            cw[g][j] = load_stream16(codes_e + row * (int64_t)row_bytes + (uint32_t)cc * 16u);
+            sc[g][j] = plane_scale<FMT>(plane_e, row, nb, cc);
+            if constexpr (AFF) bi[g][j] = plane_bias<FMT>(plane_e, row, nb, cc);
+        }
+    }
+    uint32_t xr[CPL][XW];
+    float xs[AFF ? CPL : 1];
+    const _Float16 *xp = a.x + (int64_t)(a.x_per_slot ? t * a.topk + s : t) * K;
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+        const int c = sub + LPR * j;
+        load_x_slice<FMT>(xp, c, c < cpr, xr[j]);
+        if constexpr (AFF) xs[j] = x_slice_sum<XW>(xr[j]);
+    }
+    _Float16 *lut_w = lut_lds + wave * LUT_HALVES;
+    if constexpr (FMT == KM4) {
+        for (int i = lane; i < ROWS * 8; i += kWave) {
+            int rr = i / 8;
+            rr = rr <= last ? rr : last;
+            reinterpret_cast<uint32_t *>(lut_w)[i] = reinterpret_cast<const uint32_t *>(plane_e)[(row0 + rr) * 8 + (i % 8)];
+        }
+        wave_fence();
+    } else if constexpr (KM8) {
+#pragma unroll
+        for (int q = 0; q < 2; q++)
+            reinterpret_cast<uint32_t *>(lut_w)[q * kWave + lane] =
+                reinterpret_cast<const uint32_t *>(plane_e)[(row0 / 32) * 128 + q * kWave + lane];
+        wave_fence();
+    }
+    float acc[R];
+#pragma unroll
+    for (int g = 0; g < R; g++) {
+        acc[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPL; j++) {
+            const float d = chunk_dot<FMT>(cw[g][j], xr[j], KM8 ? lut_w : lut_w + (g * RPW + rsub) * 16);
+            acc[g] = __builtin_fmaf(d, ws * sc[g][j], acc[g]);
+            if constexpr (AFF) acc[g] = __builtin_fmaf(xs[j], ws * bi[g][j], acc[g]);
+        }
+    }
+    using Red = GroupReduce<R, LPR>;
+    Red::run(acc, lane);
+    if (Red::writer(lane)) {
+        const int base = Red::base(lane);
+#pragma unroll
+        for (int j = 0; j < Red::live; j++) part[wave][(base + j) * RPW + rsub] = acc[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < ROWS && threadIdx.x <= last) {
+        float y = 0.f;
+        for (int w = 0; w < a.topk; w++) y += part[w][threadIdx.x];   // slot order
+        reinterpret_cast<float *>(a.out)[(int64_t)t * a.N + row0 + threadIdx.x] = y;
+    }
+}
+
+template <int FMT, int LPR, int CPL, int ROWS>
+static void launch_combine_split(GatherArgs a, hipStream_t st) {
+    constexpr int R = ROWS / (kWave / LPR);
+    const int tiles = (int)((a.N + ROWS - 1) / ROWS);
+    hipLaunchKernelGGL((combine_split_kernel<FMT, LPR, CPL, R>), dim3(tiles, a.T), dim3(64 * kSplitSlots), 0, st, a);
+}
+
 template <int FMT, int LPR, int CPL>
 static hipError_t launch_token_major(GatherArgs a, hipStream_t st) {
+    if (CPL == 1 && a.topk <= kSplitSlots) {   // longer rows keep the token-major kernel (registers)
+        // measured on MI355X, int4 down 2048 x 512, top-8 of 256, HIP graphs:
+        // T = 1 3.5 us (8 rows per workgroup) against 5.0 for the token-major
+        // kernel, T = 4 5.8 (16 rows) against 8.4, T = 8 8.4 (16 rows) against 12.8
+        constexpr int ROWS_FEW = (LPR == 64) ? 4 : 8, ROWS_MANY = (LPR == 64) ? 4 : 16;
+        if (a.T <= 2) launch_combine_split<FMT, LPR, CPL, ROWS_FEW>(a, st);
+        else launch_combine_split<FMT, LPR, CPL, ROWS_MANY>(a, st);
+        return hipGetLastError();
+    }
     constexpr int R = (LPR == 64) ? 4 : 1;
     constexpr int ROWS = R * (kWave / LPR);
     // few tokens: few waves, so each takes as many slots per round trip as

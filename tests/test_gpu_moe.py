@@ -33,6 +33,12 @@ CASES = [
     (10, 2048, 512, 1, 8),
     (12, 1536, 256, 1, 6),
     (8, 1280, 1024, 1, 4),
+    # the down projection's two combine kernels: slot-split (topk <= 8, rows of
+    # one chunk per lane, 8 or 16 rows per workgroup by token count, ragged row
+    # tiles) and token-major (more slots, or longer rows)
+    (16, 224, 64, 3, 8),
+    (32, 256, 128, 3, 12),
+    (4, 96, 4096, 2, 3),
 ]
 
 
@@ -97,6 +103,34 @@ def test_gather_none_and_combine_with_shared_input(fmt):
             assert rel_err(y[t, s], want) <= RTOL
             acc += np.float64(np.float32(ow[t, s])) * want
         assert rel_err(yc[t], acc) <= RTOL
+
+
+@pytest.mark.parametrize("fmt", ["int4", "fp4", "int8", "km4", "int4aff"])
+@pytest.mark.parametrize("K", [96, 1024])
+def test_combine_on_ragged_rows(fmt, K):
+    """The weighted combine over 100 rows (a partial last row tile for both
+    combine kernels) at T = 1, 2 and 5 tokens and 3, 8 and 11 slots, with one
+    input per slot and one per token: every output row against the oracle's
+    per-slot matvecs summed in fp64."""
+    E, N = 12, 100
+    rng = np.random.default_rng(K)
+    W = (rng.standard_normal((E * N, K)) * 0.02).astype(np.float16)
+    codes, plane = oracle.pack(fmt, W)
+    codes, plane = codes.reshape(E, N, -1), plane.reshape(E, N, -1)
+    for T in (1, 2, 5):
+        for topk in (3, 8, 11):
+            ids = np.stack([rng.choice(E, topk, replace=False) for _ in range(T)]).astype(np.int32)
+            w = rng.random((T, topk)).astype(np.float32)
+            for per_slot in (False, True):
+                x = rng.standard_normal((T, topk, K) if per_slot else (T, K)).astype(np.float16)
+                y = host(qmv.gather_qmatvec(fmt, dev(codes), dev(plane), dev(x), dev(ids), weights=dev(w),
+                                            epi="combine", x_per_slot=per_slot))
+                for t in range(T):
+                    acc = np.zeros(N)
+                    for s in range(topk):
+                        xs = x[t, s] if per_slot else x[t]
+                        acc += np.float64(w[t, s]) * oracle.matvec(fmt, codes[ids[t, s]], plane[ids[t, s]], xs[None])[0]
+                    assert rel_err(y[t], acc) <= RTOL, (fmt, K, T, topk, per_slot)
 
 
 @pytest.mark.parametrize("E,T", [(256, 64), (300, 37), (1500, 5), (4096, 3)])
