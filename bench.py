@@ -361,10 +361,15 @@ def main():
         extras["stream_read_GBps"] = stream_rate(nbytes)
         log("stream read %.1f GB/s" % extras["stream_read_GBps"])
 
+        calls4 = [qmv.qmatvec_call("km4", cc, ll, x8[:4], y=y[:4]) for cc, ll in copies]
+        ms4 = timed(lambda i: calls4[i % len(calls4)](), args.steps // 2, args.warmup)
+        extras["km4_B4_us"] = round(ms4 * 1e3, 2)
+        extras["km4_B4_GBps"] = round(nbytes / (ms4 * 1e-3) / 1e9, 1)
         calls8 = [qmv.qmatvec_call("km4", cc, ll, x8, y=y) for cc, ll in copies]
         ms8 = timed(lambda i: calls8[i % len(calls8)](), args.steps // 2, args.warmup)
         extras["km4_B8_us"] = round(ms8 * 1e3, 2)
         extras["km4_B8_GBps"] = round(nbytes / (ms8 * 1e-3) / 1e9, 1)
+        del calls4
 
         e0.record()
         pk8 = qmv.qpack_int8km(W)

@@ -459,6 +459,202 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void mv_mfma(const uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// km4 at batch 3-4 on 4x4x4 matrix-core blocks (v_mfma_f32_4x4x4_16b_f16:
+// 16 independent 4 x 4 x 4 products per instruction). Lane 4b + j belongs to
+// block b: it supplies row j of the block's A (tokens x 4 k), column j of its
+// B (4 k x weight rows) and receives column j of its D (tokens x weight rows,
+// token i in register i). Block b takes the 32-code chunks b, 16 + b, 32 + b,
+// ... of every weight row, so one instruction spans only 4 weight rows: their
+// 16-entry fp16 tables (4 x 32 bytes) cover the 32 LDS banks once and every
+// lane looks its codes up in LDS without bank conflicts, where the 16 rows of
+// a 16 x 16 operand meet in the banks (the register-table decode above costs
+// 3 VALU per code; this one about 2 plus one LDS read). Per code the VALU
+// puts the code's byte offset into the lane's row-table base (one SDWA OR of
+// a pre-masked code word) and pairs two fp16 values for the B operand. The
+// 16 block sums of a row are added across lanes at the end.
+// x is staged once per workgroup in LDS as [token][chunk][36 halfs] with 16
+// more halfs after each token row: the 64 lanes of an A-operand read (16
+// chunks x 4 tokens, 8 bytes each) then fall on distinct bank pairs, where an
+// unpadded token stride (a multiple of 32 dwords) put the four tokens of a
+// chunk on the same banks and doubled the LDS time at batch 8.
+// Each wave owns Q quads of 4 rows per group and strides over the groups;
+// an x read serves the Q quads of its step.
+// Measured on MI355X (HIP graphs, 248320 x 2048 cycling 4 weight copies):
+// B = 3 / 4 59.2 / 60.3 us against 76.0 / 78.2 us for mv_mfma; at 16384 to
+// 124160 rows 8-25% faster. At B = 8 (two token quads, twice the MFMAs and x
+// reads) it only matched mv_mfma (72.2-76.8 against 74.9-77.4 us), and at
+// B = 2 the dot2 kernel is as fast, so it takes B = 3, 4 only.
+// ---------------------------------------------------------------------------
+typedef _Float16 h4q __attribute__((ext_vector_type(4)));
+constexpr int kQuadWaves = 8;       // waves per workgroup, sharing one x stage
+constexpr int kQuadXChunk = 36;     // halfs per staged 32-element x chunk
+constexpr int kQuadXRowPad = 16;    // halfs after each staged token row
+
+// base | (byte S of m): the table byte address of one pre-masked code, one SDWA OR
+template <int S>
+__device__ __forceinline__ uint32_t or_code_byte(uint32_t base, uint32_t m) {
+    uint32_t r;
+    if constexpr (S == 0)
+        asm("v_or_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(base), "v"(m));
+    else if constexpr (S == 1)
+        asm("v_or_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(base), "v"(m));
+    else if constexpr (S == 2)
+        asm("v_or_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(base), "v"(m));
+    else
+        asm("v_or_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(base), "v"(m));
+    return r;
+}
+__device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t *>((size_t)addr);
+}
+__device__ __forceinline__ h4q lds_h4(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) h4q *>((size_t)addr);
+}
+__host__ __device__ constexpr int quad_x_row(int K) { return (K / 32) * kQuadXChunk + kQuadXRowPad; }
+
+template <int Q, int KC>   // K = 512 * KC
+__global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__restrict__ codes,
+                                                               const uint16_t *__restrict__ lut, int64_t N,
+                                                               const _Float16 *__restrict__ x, int B,
+                                                               float *__restrict__ y, uint64_t *__restrict__ hdr) {
+    constexpr int K = 512 * KC, ROWS = 4 * Q, XROW = quad_x_row(K);
+    constexpr int TW = (ROWS * 8 + 63) / 64;   // table dwords per lane per group
+    extern __shared__ __align__(16) uint8_t qlds[];
+    // fused argmax: the first workgroup zeroes the reduction header
+    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
+    _Float16 *xs = reinterpret_cast<_Float16 *>(qlds);
+    for (int i = threadIdx.x; i < 4 * (K / 4); i += 64 * kQuadWaves) {
+        const int b = i / (K / 4), k = 4 * (i - b * (K / 4));
+        uint2 v = make_uint2(0u, 0u);   // tokens >= B read zeros
+        if (b < B) v = *reinterpret_cast<const uint2 *>(x + (size_t)b * K + k);
+        *reinterpret_cast<uint2 *>(xs + b * XROW + (k >> 5) * kQuadXChunk + (k & 31)) = v;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = lane >> 2, j = lane & 3;
+    // per-wave tables [ROWS][16] fp16 (32-byte aligned: the code offsets are OR-ed in)
+    uint8_t *tab = qlds + 4 * XROW * 2 + wave * (ROWS * 32);
+    const uint32_t rb = (uint32_t)(uintptr_t)tab + 32u * j;   // row j of quad 0
+    const uint32_t xa = (uint32_t)(uintptr_t)xs + (uint32_t)((j * XROW + blk * kQuadXChunk) * 2);
+    const int64_t ngroups = (N + ROWS - 1) / ROWS;
+    for (int64_t g = (int64_t)blockIdx.x * kQuadWaves + wave; g < ngroups; g += (int64_t)gridDim.x * kQuadWaves) {
+        const int64_t row0 = g * ROWS;
+        // rows past N read row N - 1 and are never stored
+        uint32_t tv[TW];
+#pragma unroll
+        for (int q = 0; q < TW; q++) {
+            const int i = q * 64 + lane;
+            const int64_t r = row0 + (i >> 3) < N ? row0 + (i >> 3) : N - 1;
+            tv[q] = reinterpret_cast<const uint32_t *>(lut)[r * 8 + (i & 7)];
+        }
+        uint4 cw[Q][KC];
+#pragma unroll
+        for (int u = 0; u < Q; u++) {
+            const int64_t r = row0 + 4 * u + j < N ? row0 + 4 * u + j : N - 1;
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++)
+                cw[u][kc] = load_stream16(codes + r * (K / 2) + (uint32_t)(16 * kc + blk) * 16u);
+        }
+#pragma unroll
+        for (int q = 0; q < TW; q++) {
+            const int i = q * 64 + lane;
+            if (i < ROWS * 8) reinterpret_cast<uint32_t *>(tab)[i] = tv[q];
+        }
+        wave_sync_lds();
+        f4 acc[Q];
+#pragma unroll
+        for (int u = 0; u < Q; u++) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                // codes 8d .. 8d + 7 of the chunk: two k-steps of 4
+                const h4q x0 = lds_h4(xa + (uint32_t)((16 * kc * kQuadXChunk + 8 * d) * 2));
+                const h4q x1 = lds_h4(xa + (uint32_t)((16 * kc * kQuadXChunk + 8 * d + 4) * 2));
+#pragma unroll
+                for (int u = 0; u < Q; u++) {
+                    const uint32_t w = (d == 0) ? cw[u][kc].x : (d == 1) ? cw[u][kc].y : (d == 2) ? cw[u][kc].z : cw[u][kc].w;
+                    // byte offsets 2c of the even (low nibble) and odd codes
+                    const uint32_t ml = (w << 1) & 0x1E1E1E1Eu, mh = (w >> 3) & 0x1E1E1E1Eu;
+                    const uint32_t ub = rb + 128u * u;
+                    const uint32_t t0 = lds_u16(or_code_byte<0>(ub, ml)), t1 = lds_u16(or_code_byte<0>(ub, mh));
+                    const uint32_t t2 = lds_u16(or_code_byte<1>(ub, ml)), t3 = lds_u16(or_code_byte<1>(ub, mh));
+                    const uint32_t t4 = lds_u16(or_code_byte<2>(ub, ml)), t5 = lds_u16(or_code_byte<2>(ub, mh));
+                    const uint32_t t6 = lds_u16(or_code_byte<3>(ub, ml)), t7 = lds_u16(or_code_byte<3>(ub, mh));
+                    const u2v b0 = {t0 | (t1 << 16), t2 | (t3 << 16)};
+                    const u2v b1 = {t4 | (t5 << 16), t6 | (t7 << 16)};
+                    acc[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(x0, __builtin_bit_cast(h4q, b0), acc[u], 0, 0, 0);
+                    acc[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(x1, __builtin_bit_cast(h4q, b1), acc[u], 0, 0, 0);
+                }
+            }
+        }
+        wave_sync_lds();   // the next group rewrites the tables
+        // add the 16 block sums: v[4u + i] (token i, row 4u + j), halves
+        // exchanged across lane bit 5 and 4, then butterflies over bits 3, 2
+        constexpr int V = 4 * Q;
+        float v[V];
+#pragma unroll
+        for (int u = 0; u < Q; u++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[4 * u + i] = acc[u][i];
+#pragma unroll
+        for (int m = 0; m < V / 2; m++) v[m] = half_swap_add<32>(v[m], v[m + V / 2]);
+#pragma unroll
+        for (int m = 0; m < V / 4; m++) v[m] = half_swap_add<16>(v[m], v[m + V / 4]);
+#pragma unroll
+        for (int m = 0; m < V / 4; m++) {
+            v[m] += __shfl_xor(v[m], 8);
+            v[m] += __shfl_xor(v[m], 4);
+        }
+        if ((lane & 12) == 0) {
+            const int base = ((lane & 32) ? V / 2 : 0) + ((lane & 16) ? V / 4 : 0);
+#pragma unroll
+            for (int m = 0; m < V / 4; m++) {
+                const int idx = base + m, u = idx >> 2, i = idx & 3;
+                const int64_t row = row0 + 4 * u + j;
+                if (row < N && i < B) y[(size_t)i * N + row] = v[m];
+            }
+        }
+    }
+}
+
+template <int Q, int KC>
+static hipError_t launch_km4_quad_q(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
+                                    float *y, hipStream_t st, uint64_t *hdr) {
+    constexpr int K = 512 * KC;
+    const size_t lds = (size_t)4 * quad_x_row(K) * 2 + (size_t)kQuadWaves * Q * 128;
+    const int64_t groups = (N + 4 * Q - 1) / (4 * Q);
+    const int64_t want = (groups + kQuadWaves - 1) / kQuadWaves;
+    const int64_t cap = 2 * (int64_t)device_cu_count();   // two workgroups per CU stay resident
+    const int grid = (int)(want < cap ? want : cap);
+    hipLaunchKernelGGL((mv_km4_quad<Q, KC>), dim3(grid), dim3(64 * kQuadWaves), lds, st, codes,
+                       reinterpret_cast<const uint16_t *>(plane), N, reinterpret_cast<const _Float16 *>(x), B, y, hdr);
+    return hipGetLastError();
+}
+
+static bool km4_quad_takes(int64_t K, int B) {
+    return B >= 3 && B <= 4 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
+}
+
+// Quads per wave: four on the tallest heads, two below (248320 x 2048 at
+// B = 4: 60.3 against 63.5 us; 32768 rows: 11.7 against 13.8 us with four);
+// at most 16 code registers x 4 per lane.
+static hipError_t launch_km4_quad(const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                                  int B, float *y, hipStream_t st, uint64_t *hdr) {
+    const bool tall = N >= 196608;
+    switch (K) {
+    case 512: return tall ? launch_km4_quad_q<4, 1>(codes, plane, N, x, B, y, st, hdr)
+                          : launch_km4_quad_q<2, 1>(codes, plane, N, x, B, y, st, hdr);
+    case 1024: return tall ? launch_km4_quad_q<4, 2>(codes, plane, N, x, B, y, st, hdr)
+                           : launch_km4_quad_q<2, 2>(codes, plane, N, x, B, y, st, hdr);
+    case 2048: return tall ? launch_km4_quad_q<4, 4>(codes, plane, N, x, B, y, st, hdr)
+                           : launch_km4_quad_q<2, 4>(codes, plane, N, x, B, y, st, hdr);
+    default: return tall ? launch_km4_quad_q<2, 8>(codes, plane, N, x, B, y, st, hdr)
+                         : launch_km4_quad_q<1, 8>(codes, plane, N, x, B, y, st, hdr);
+    }
+}
+
 template <int FMT>
 static size_t mfma_lds_bytes(int64_t K, int B) {
     return (size_t)B * (size_t)(K + 8) * 2 + kZeroLds + (size_t)xsum_lds_bytes<FMT>((int)K) +
@@ -543,6 +739,7 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
                               int B, float *y, hipStream_t st, bool *handled, uint64_t *hdr) {
     *handled = mfma_eligible(fmt, plane, N, K, B);
     if (!*handled) return hipSuccess;
+    if (fmt == KM4 && km4_quad_takes(K, B)) return launch_km4_quad(codes, plane, N, K, x, B, y, st, hdr);
     switch (fmt) {
     case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st, hdr);
     case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st, hdr);
