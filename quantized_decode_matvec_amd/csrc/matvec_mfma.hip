@@ -633,6 +633,205 @@ static hipError_t launch_km4_quad_q(const uint8_t *codes, const void *plane, int
     return hipGetLastError();
 }
 
+// The scale formats (int4, affine int4) on the same 4x4x4 blocks, batch 3-8:
+// the codes decode by arithmetic (decode8: magic-number fp16, no lookups), x
+// is staged in the decoder's element order, every 32-code chunk (one block)
+// is accumulated by its own MFMA chain and added into the fp32 total with the
+// block scale (affine int4: plus bias x the block's x sum, from an LDS table
+// [chunk][token]). Batch 5-8 takes two token quads (BQ = 2: two MFMAs per
+// step on one decoded B operand). Measured on MI355X (HIP graphs,
+// 248320 x 2048): int4 B = 4 / 8 55.9 / 61.2 us against 63.5 / 64.5 us for
+// mv_mfma; affine int4 58.7 / 65.5 against 78.6 / 81.3. fp4 gained nothing
+// (53.4 against 53.0 us at B = 4, slower at B = 8) and keeps mv_mfma.
+template <int FMT, int Q, int KC, int BQ>
+__global__ __launch_bounds__(64 * kQuadWaves) void mv_quad_scaled(const uint8_t *__restrict__ codes,
+                                                                  const void *__restrict__ plane, int64_t N,
+                                                                  const _Float16 *__restrict__ x, int B,
+                                                                  float *__restrict__ y, uint64_t *__restrict__ hdr) {
+    constexpr int K = 512 * KC, CPR = K / 32, ROWS = 4 * Q, NT = 4 * BQ, XROW = quad_x_row(K);
+    constexpr bool AFF = (FMT == INT4AFF);
+    static_assert(FMT == INT4 || FMT == INT4AFF, "scale formats with 4-bit codes");
+    extern __shared__ __align__(16) uint8_t qlds[];
+    // fused argmax: the first workgroup zeroes the reduction header
+    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
+    _Float16 *xs = reinterpret_cast<_Float16 *>(qlds);
+    float *xsum = reinterpret_cast<float *>(qlds + NT * XROW * 2);   // affine int4: [CPR][NT]
+    for (int i = threadIdx.x; i < NT * (K / 8); i += 64 * kQuadWaves) {
+        const int b = i / (K / 8), g8 = i - b * (K / 8), k = 8 * g8;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);   // tokens >= B read zeros
+        if (b < B) v = stage_group<FMT>(x + (size_t)b * K, g8);
+        // a chunk starts 72 bytes after the previous one: two 8-byte stores
+        uint2 *d = reinterpret_cast<uint2 *>(xs + b * XROW + (k >> 5) * kQuadXChunk + (k & 31));
+        d[0] = make_uint2(v.x, v.y);
+        d[1] = make_uint2(v.z, v.w);
+    }
+    if constexpr (AFF) {
+        for (int i = threadIdx.x; i < NT * CPR; i += 64 * kQuadWaves) {
+            const int b = i / CPR, c = i - b * CPR;
+            float sum = 0.f;
+            if (b < B) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(x + (size_t)b * K + 32 * c);
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint4 v = p[u];
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; e++) sum = dot2(as_h2(w4[e]), as_h2(0x3C003C00u), sum);
+                }
+            }
+            xsum[c * NT + b] = sum;
+        }
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int blk = lane >> 2, j = lane & 3;
+    const uint32_t xa = (uint32_t)(uintptr_t)xs + (uint32_t)((j * XROW + blk * kQuadXChunk) * 2);
+    const int64_t ngroups = (N + ROWS - 1) / ROWS;
+    for (int64_t g = (int64_t)blockIdx.x * kQuadWaves + wave; g < ngroups; g += (int64_t)gridDim.x * kQuadWaves) {
+        const int64_t row0 = g * ROWS;
+        // rows past N read row N - 1 and are never stored
+        uint4 cw[Q][KC];
+        uint32_t sw[Q][KC];   // block scale (affine int4: scale | bias << 16)
+#pragma unroll
+        for (int u = 0; u < Q; u++) {
+            const int64_t r = row0 + 4 * u + j < N ? row0 + 4 * u + j : N - 1;
+#pragma unroll
+            for (int kc = 0; kc < KC; kc++) {
+                const int c = 16 * kc + blk;
+                cw[u][kc] = load_stream16(codes + r * (K / 2) + (uint32_t)c * 16u);
+                if constexpr (AFF) sw[u][kc] = reinterpret_cast<const uint32_t *>(plane)[r * CPR + c];
+                else sw[u][kc] = reinterpret_cast<const uint16_t *>(plane)[r * CPR + c];
+            }
+        }
+        f4 acc[Q][BQ];
+#pragma unroll
+        for (int u = 0; u < Q; u++)
+#pragma unroll
+            for (int p = 0; p < BQ; p++) acc[u][p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; kc++) {
+            f4 ca[Q][BQ];   // this chunk's sums, before the block scale
+#pragma unroll
+            for (int u = 0; u < Q; u++)
+#pragma unroll
+                for (int p = 0; p < BQ; p++) ca[u][p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int d = 0; d < 4; d++) {
+                h4q xv[BQ][2];
+#pragma unroll
+                for (int p = 0; p < BQ; p++)
+#pragma unroll
+                    for (int h = 0; h < 2; h++)
+                        xv[p][h] = lds_h4(xa + (uint32_t)((p * 4 * XROW + 16 * kc * kQuadXChunk + 8 * d + 4 * h) * 2));
+#pragma unroll
+                for (int u = 0; u < Q; u++) {
+                    const uint32_t w = (d == 0) ? cw[u][kc].x : (d == 1) ? cw[u][kc].y : (d == 2) ? cw[u][kc].z : cw[u][kc].w;
+                    typedef uint32_t u4q __attribute__((ext_vector_type(4)));
+                    const u4q dv = __builtin_bit_cast(u4q, decode8<FMT>(w, 0u));
+                    const u2v b0 = {dv[0], dv[1]}, b1 = {dv[2], dv[3]};
+#pragma unroll
+                    for (int p = 0; p < BQ; p++) {
+                        ca[u][p] = __builtin_amdgcn_mfma_f32_4x4x4f16(xv[p][0], __builtin_bit_cast(h4q, b0), ca[u][p], 0, 0, 0);
+                        ca[u][p] = __builtin_amdgcn_mfma_f32_4x4x4f16(xv[p][1], __builtin_bit_cast(h4q, b1), ca[u][p], 0, 0, 0);
+                    }
+                }
+            }
+            const int c = 16 * kc + blk;
+#pragma unroll
+            for (int u = 0; u < Q; u++) {
+                const float scl = f16_bits_to_f32((uint16_t)(sw[u][kc] & 0xFFFFu));
+#pragma unroll
+                for (int p = 0; p < BQ; p++) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) acc[u][p][i] = __builtin_fmaf(ca[u][p][i], scl, acc[u][p][i]);
+                    if constexpr (AFF) {
+                        const float bia = f16_bits_to_f32((uint16_t)(sw[u][kc] >> 16));
+                        const f4 xsm = *reinterpret_cast<const f4 *>(xsum + c * NT + 4 * p);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[u][p][i] = __builtin_fmaf(xsm[i], bia, acc[u][p][i]);
+                    }
+                }
+            }
+        }
+        // add the 16 block sums: v[(u * BQ + p) * 4 + i] (token 4p + i, row 4u + j)
+        constexpr int V = Q * BQ * 4;
+        float v[V];
+#pragma unroll
+        for (int u = 0; u < Q; u++)
+#pragma unroll
+            for (int p = 0; p < BQ; p++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) v[(u * BQ + p) * 4 + i] = acc[u][p][i];
+#pragma unroll
+        for (int m = 0; m < V / 2; m++) v[m] = half_swap_add<32>(v[m], v[m + V / 2]);
+#pragma unroll
+        for (int m = 0; m < V / 4; m++) v[m] = half_swap_add<16>(v[m], v[m + V / 4]);
+#pragma unroll
+        for (int m = 0; m < V / 4; m++) {
+            v[m] += __shfl_xor(v[m], 8);
+            v[m] += __shfl_xor(v[m], 4);
+        }
+        if ((lane & 12) == 0) {
+            const int base = ((lane & 32) ? V / 2 : 0) + ((lane & 16) ? V / 4 : 0);
+#pragma unroll
+            for (int m = 0; m < V / 4; m++) {
+                const int idx = base + m, u = idx / (4 * BQ), p = (idx / 4) % BQ, i = idx % 4;
+                const int64_t row = row0 + 4 * u + j;
+                const int b = 4 * p + i;
+                if (row < N && b < B) y[(size_t)b * N + row] = v[m];
+            }
+        }
+    }
+}
+
+template <int FMT, int Q, int KC, int BQ>
+static hipError_t launch_quad_scaled_q(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
+                                       float *y, hipStream_t st, uint64_t *hdr) {
+    constexpr int K = 512 * KC, NT = 4 * BQ;
+    const size_t lds = (size_t)NT * quad_x_row(K) * 2 + (FMT == INT4AFF ? (size_t)NT * (K / 32) * 4 : 0);
+    const int64_t groups = (N + 4 * Q - 1) / (4 * Q);
+    const int64_t want = (groups + kQuadWaves - 1) / kQuadWaves;
+    const int64_t cap = 2 * (int64_t)device_cu_count();   // two workgroups per CU stay resident
+    const int grid = (int)(want < cap ? want : cap);
+    if (lds > 64 * 1024) {
+        // K = 4096 with two token quads: 74 KiB, two workgroups still fit a CU's 160 KiB
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mv_quad_scaled<FMT, Q, KC, BQ>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((mv_quad_scaled<FMT, Q, KC, BQ>), dim3(grid), dim3(64 * kQuadWaves), lds, st, codes, plane, N,
+                       reinterpret_cast<const _Float16 *>(x), B, y, hdr);
+    return hipGetLastError();
+}
+
+// Two row quads per wave (one at K = 4096, keeping 32 code registers per
+// quad); one token quad up to B = 4, two above.
+template <int FMT>
+static hipError_t launch_quad_scaled(const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
+                                     int B, float *y, hipStream_t st, uint64_t *hdr) {
+    const bool two = B > 4;
+    switch (K) {
+    case 512: return two ? launch_quad_scaled_q<FMT, 2, 1, 2>(codes, plane, N, x, B, y, st, hdr)
+                         : launch_quad_scaled_q<FMT, 2, 1, 1>(codes, plane, N, x, B, y, st, hdr);
+    case 1024: return two ? launch_quad_scaled_q<FMT, 2, 2, 2>(codes, plane, N, x, B, y, st, hdr)
+                          : launch_quad_scaled_q<FMT, 2, 2, 1>(codes, plane, N, x, B, y, st, hdr);
+    case 2048: return two ? launch_quad_scaled_q<FMT, 2, 4, 2>(codes, plane, N, x, B, y, st, hdr)
+                          : launch_quad_scaled_q<FMT, 2, 4, 1>(codes, plane, N, x, B, y, st, hdr);
+    default:
+        if constexpr (FMT == INT4)
+            return two ? launch_quad_scaled_q<FMT, 1, 8, 2>(codes, plane, N, x, B, y, st, hdr)
+                       : launch_quad_scaled_q<FMT, 1, 8, 1>(codes, plane, N, x, B, y, st, hdr);
+        return hipErrorInvalidValue;
+    }
+}
+
+static bool quad_scaled_takes(int fmt, int64_t K, int B) {
+    if (B < 3 || B > 8) return false;
+    if (fmt == INT4) return K == 512 || K == 1024 || K == 2048 || K == 4096;
+    if (fmt == INT4AFF) return K == 512 || K == 1024 || K == 2048;
+    return false;
+}
+
 static bool km4_quad_takes(int64_t K, int B) {
     return B >= 3 && B <= 4 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
 }
@@ -686,6 +885,8 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
+    // the 4x4x4 kernels stage x alone (at most 74 KiB, two workgroups per CU)
+    if ((fmt == KM4 && km4_quad_takes(K, B)) || quad_scaled_takes(fmt, K, B)) return true;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
                  : (fmt == INT4AFF) ? mfma_lds_bytes<INT4AFF>(K, B)
                  : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
@@ -740,6 +941,9 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
     *handled = mfma_eligible(fmt, plane, N, K, B);
     if (!*handled) return hipSuccess;
     if (fmt == KM4 && km4_quad_takes(K, B)) return launch_km4_quad(codes, plane, N, K, x, B, y, st, hdr);
+    if (quad_scaled_takes(fmt, K, B))
+        return fmt == INT4 ? launch_quad_scaled<INT4>(codes, plane, N, K, x, B, y, st, hdr)
+                           : launch_quad_scaled<INT4AFF>(codes, plane, N, K, x, B, y, st, hdr);
     switch (fmt) {
     case INT4: return launch_mfma_fmt<INT4>(codes, plane, N, (int)K, x, B, y, st, hdr);
     case INT4AFF: return launch_mfma_fmt<INT4AFF>(codes, plane, N, (int)K, x, B, y, st, hdr);
