@@ -825,8 +825,13 @@ static hipError_t launch_quad_scaled(const uint8_t *codes, const void *plane, in
     }
 }
 
-static bool quad_scaled_takes(int fmt, int64_t K, int B) {
-    if (B < 3 || B > 8) return false;
+// Batch 2 too from 16384 rows (int4) and 32768 (affine int4): against the
+// dot2 kernel, int4 16384 / 248320 x 2048: 6.8 / 52.3 us against 7.3 / 56.5;
+// affine int4 32768 / 248320: 9.8 / 57.1 against 11.7 / 61.9, but 7.6 against
+// 6.4 at 16384.
+static bool quad_scaled_takes(int fmt, int64_t N, int64_t K, int B) {
+    if (B < 2 || B > 8) return false;
+    if (B == 2 && N < (fmt == INT4 ? 16384 : 32768)) return false;
     if (fmt == INT4) return K == 512 || K == 1024 || K == 2048 || K == 4096;
     if (fmt == INT4AFF) return K == 512 || K == 1024 || K == 2048;
     return false;
@@ -866,6 +871,8 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
 // scale plane, and staging that fits in 64 KiB of LDS (affine int4: 80 KiB,
 // two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
+    // batch 2 reaches the matrix cores only on the 4x4x4 scale-format kernel
+    if (B == 2) return quad_scaled_takes(fmt, N, K, B) && reinterpret_cast<uintptr_t>(plane) % 16 == 0;
     if (B < 3 || B > 8 || N < 16) return false;
     // below 16384 rows the dot2 path is as fast at B = 3, 4 (fp4 4096 x 2048:
     // 6.8 us against 7.4 us); from B = 5 the matrix cores win at any size
@@ -886,7 +893,7 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     // a group's scales (tables) are read as 16-byte pieces
     if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
     // the 4x4x4 kernels stage x alone (at most 74 KiB, two workgroups per CU)
-    if ((fmt == KM4 && km4_quad_takes(K, B)) || quad_scaled_takes(fmt, K, B)) return true;
+    if ((fmt == KM4 && km4_quad_takes(K, B)) || quad_scaled_takes(fmt, N, K, B)) return true;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
                  : (fmt == INT4AFF) ? mfma_lds_bytes<INT4AFF>(K, B)
                  : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
@@ -941,7 +948,7 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
     *handled = mfma_eligible(fmt, plane, N, K, B);
     if (!*handled) return hipSuccess;
     if (fmt == KM4 && km4_quad_takes(K, B)) return launch_km4_quad(codes, plane, N, K, x, B, y, st, hdr);
-    if (quad_scaled_takes(fmt, K, B))
+    if (quad_scaled_takes(fmt, N, K, B))
         return fmt == INT4 ? launch_quad_scaled<INT4>(codes, plane, N, K, x, B, y, st, hdr)
                            : launch_quad_scaled<INT4AFF>(codes, plane, N, K, x, B, y, st, hdr);
     switch (fmt) {

@@ -2,7 +2,8 @@
 (at least 16384 rows at batch 3-4): km4 at batch 3 and 4 (K of 512, 1024,
 2048 or 4096; two row quads per wave below 196608 rows, one at K = 4096, and
 four above, two at K = 4096) and int4 / affine int4 at batch 3 to 8 (one
-token quad up to batch 4, two above; K of 512, 1024, 2048, and 4096 for int4).
+token quad up to batch 4, two above; K of 512, 1024, 2048, and 4096 for int4;
+batch 2 from 16384 rows for int4 and 32768 for affine int4).
 Every instantiation runs on a ragged matrix (rows not a multiple of the
 wave's rows; K = 1024 for the scale formats in test_gpu_parity.py). The GPU
 packs and multiplies the whole matrix; the oracle packs and multiplies
@@ -62,6 +63,7 @@ SCALED_CASES = [
     ("int4", 16384 + 1, 4096),
     ("int4aff", 16384 + 5, 512),
     ("int4aff", 16384 + 3, 2048),
+    ("int4aff", 32768 + 7, 1024),   # batch 2 takes the 4x4x4 kernel from 32768 rows
 ]
 
 
@@ -72,7 +74,7 @@ def test_scaled_quad_kernel_on_sampled_rows(fmt, N, K):
     codes, plane = qmv.qpack(fmt, dev(c.W))
     rows = np.unique(np.concatenate([sample_rows(N, n=64, seed=K), np.arange(N - 16, N)]))
     oc, op = oracle.pack(fmt, c.W[rows])
-    for B in (3, 4, 5, 8):
+    for B in (2, 3, 4, 5, 8):
         y = host(qmv.qmatvec(fmt, codes, plane, dev(c.x[:B])))
         assert y.shape == (B, N)
         assert np.all(np.isfinite(y))
