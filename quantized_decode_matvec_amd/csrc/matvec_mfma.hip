@@ -804,23 +804,31 @@ static hipError_t launch_quad_scaled_q(const uint8_t *codes, const void *plane, 
     return hipGetLastError();
 }
 
-// Two row quads per wave (one at K = 4096, keeping 32 code registers per
-// quad); one token quad up to B = 4, two above.
+// One token quad up to B = 4, two above. Row quads per wave by size, so the
+// grid fills the CUs: one below 32768 rows (below 65536 at B <= 4), two above
+// (one at K = 4096, keeping 32 code registers per quad). Measured (HIP graphs,
+// K = 2048): int4 B = 3 at 16384 / 24576 / 49152 rows 6.05 / 7.40 / 12.55 us
+// with one quad against 6.97 / 8.81 / 13.44 with two; B = 8 at 49152 rows
+// 16.90 against 15.37; at 8192 rows two quads leave half the CUs idle.
+template <int FMT, int KC>
+static hipError_t launch_quad_scaled_k(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
+                                       float *y, hipStream_t st, uint64_t *hdr) {
+    const bool two_tok = B > 4;
+    const bool two_rows = KC < 8 && N >= (two_tok ? 32768 : 65536);
+    if (two_tok) return two_rows ? launch_quad_scaled_q<FMT, (KC < 8 ? 2 : 1), KC, 2>(codes, plane, N, x, B, y, st, hdr)
+                                 : launch_quad_scaled_q<FMT, 1, KC, 2>(codes, plane, N, x, B, y, st, hdr);
+    return two_rows ? launch_quad_scaled_q<FMT, (KC < 8 ? 2 : 1), KC, 1>(codes, plane, N, x, B, y, st, hdr)
+                    : launch_quad_scaled_q<FMT, 1, KC, 1>(codes, plane, N, x, B, y, st, hdr);
+}
 template <int FMT>
 static hipError_t launch_quad_scaled(const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
                                      int B, float *y, hipStream_t st, uint64_t *hdr) {
-    const bool two = B > 4;
     switch (K) {
-    case 512: return two ? launch_quad_scaled_q<FMT, 2, 1, 2>(codes, plane, N, x, B, y, st, hdr)
-                         : launch_quad_scaled_q<FMT, 2, 1, 1>(codes, plane, N, x, B, y, st, hdr);
-    case 1024: return two ? launch_quad_scaled_q<FMT, 2, 2, 2>(codes, plane, N, x, B, y, st, hdr)
-                          : launch_quad_scaled_q<FMT, 2, 2, 1>(codes, plane, N, x, B, y, st, hdr);
-    case 2048: return two ? launch_quad_scaled_q<FMT, 2, 4, 2>(codes, plane, N, x, B, y, st, hdr)
-                          : launch_quad_scaled_q<FMT, 2, 4, 1>(codes, plane, N, x, B, y, st, hdr);
+    case 512: return launch_quad_scaled_k<FMT, 1>(codes, plane, N, x, B, y, st, hdr);
+    case 1024: return launch_quad_scaled_k<FMT, 2>(codes, plane, N, x, B, y, st, hdr);
+    case 2048: return launch_quad_scaled_k<FMT, 4>(codes, plane, N, x, B, y, st, hdr);
     default:
-        if constexpr (FMT == INT4)
-            return two ? launch_quad_scaled_q<FMT, 1, 8, 2>(codes, plane, N, x, B, y, st, hdr)
-                       : launch_quad_scaled_q<FMT, 1, 8, 1>(codes, plane, N, x, B, y, st, hdr);
+        if constexpr (FMT == INT4) return launch_quad_scaled_k<FMT, 8>(codes, plane, N, x, B, y, st, hdr);
         return hipErrorInvalidValue;
     }
 }
@@ -829,33 +837,45 @@ static hipError_t launch_quad_scaled(const uint8_t *codes, const void *plane, in
 // dot2 kernel, int4 16384 / 248320 x 2048: 6.8 / 52.3 us against 7.3 / 56.5;
 // affine int4 32768 / 248320: 9.8 / 57.1 against 11.7 / 61.9, but 7.6 against
 // 6.4 at 16384.
+// Batch 3-8 from 8192 rows (affine int4 at B >= 5 from 4096, where the
+// alternative is the register-x dot2 kernel: 5.8 against 7.2 us at B = 8);
+// against the x-staged dot2 kernel at 8192 x 2048: int4 B = 4 / 8 4.6 / 5.4 us
+// against 5.2 / 7.6, affine int4 4.9 / 6.2 against 6.1 / 7.7; at 4096 rows
+// the dot2 kernels are as fast or faster.
 static bool quad_scaled_takes(int fmt, int64_t N, int64_t K, int B) {
     if (B < 2 || B > 8) return false;
     if (B == 2 && N < (fmt == INT4 ? 16384 : 32768)) return false;
+    if (B >= 3 && N < ((fmt == INT4AFF && B >= 5) ? 4096 : 8192)) return false;
     if (fmt == INT4) return K == 512 || K == 1024 || K == 2048 || K == 4096;
     if (fmt == INT4AFF) return K == 512 || K == 1024 || K == 2048;
     return false;
 }
 
-static bool km4_quad_takes(int64_t K, int B) {
-    return B >= 3 && B <= 4 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
+// from 8192 rows: 8192 x 2048 at B = 4 5.8 us against 7.1 for the dot2 kernel
+// (4096 rows: 5.2 against 4.8)
+static bool km4_quad_takes(int64_t N, int64_t K, int B) {
+    return B >= 3 && B <= 4 && N >= 8192 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
 }
 
-// Quads per wave: four on the tallest heads, two below (248320 x 2048 at
-// B = 4: 60.3 against 63.5 us; 32768 rows: 11.7 against 13.8 us with four);
-// at most 16 code registers x 4 per lane.
+// Quads per wave: four on the tallest heads, two from 32768 rows, one below
+// (248320 x 2048 at B = 4: 60.3 against 63.5 us with two; 32768 rows: 11.7
+// against 13.8 us with four; 16384 / 24576 rows at B = 3: 7.5 / 9.0 us with
+// one against 8.6 / 10.9 with two); at most 16 code registers x 4 per lane.
+template <int KC>
+static hipError_t launch_km4_quad_k(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
+                                    float *y, hipStream_t st, uint64_t *hdr) {
+    constexpr int QT = (KC < 8) ? 4 : 2, QM = (KC < 8) ? 2 : 1;
+    if (N >= 196608) return launch_km4_quad_q<QT, KC>(codes, plane, N, x, B, y, st, hdr);
+    if (N >= 32768) return launch_km4_quad_q<QM, KC>(codes, plane, N, x, B, y, st, hdr);
+    return launch_km4_quad_q<1, KC>(codes, plane, N, x, B, y, st, hdr);
+}
 static hipError_t launch_km4_quad(const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
                                   int B, float *y, hipStream_t st, uint64_t *hdr) {
-    const bool tall = N >= 196608;
     switch (K) {
-    case 512: return tall ? launch_km4_quad_q<4, 1>(codes, plane, N, x, B, y, st, hdr)
-                          : launch_km4_quad_q<2, 1>(codes, plane, N, x, B, y, st, hdr);
-    case 1024: return tall ? launch_km4_quad_q<4, 2>(codes, plane, N, x, B, y, st, hdr)
-                           : launch_km4_quad_q<2, 2>(codes, plane, N, x, B, y, st, hdr);
-    case 2048: return tall ? launch_km4_quad_q<4, 4>(codes, plane, N, x, B, y, st, hdr)
-                           : launch_km4_quad_q<2, 4>(codes, plane, N, x, B, y, st, hdr);
-    default: return tall ? launch_km4_quad_q<2, 8>(codes, plane, N, x, B, y, st, hdr)
-                         : launch_km4_quad_q<1, 8>(codes, plane, N, x, B, y, st, hdr);
+    case 512: return launch_km4_quad_k<1>(codes, plane, N, x, B, y, st, hdr);
+    case 1024: return launch_km4_quad_k<2>(codes, plane, N, x, B, y, st, hdr);
+    case 2048: return launch_km4_quad_k<4>(codes, plane, N, x, B, y, st, hdr);
+    default: return launch_km4_quad_k<8>(codes, plane, N, x, B, y, st, hdr);
     }
 }
 
@@ -871,8 +891,11 @@ static size_t mfma_lds_bytes(int64_t K, int B) {
 // scale plane, and staging that fits in 64 KiB of LDS (affine int4: 80 KiB,
 // two workgroups per CU).
 static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int B) {
-    // batch 2 reaches the matrix cores only on the 4x4x4 scale-format kernel
-    if (B == 2) return quad_scaled_takes(fmt, N, K, B) && reinterpret_cast<uintptr_t>(plane) % 16 == 0;
+    // a group's scales (tables) are read as 16-byte pieces
+    if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
+    // the 4x4x4 kernels have their own size rules and stage x alone (at most
+    // 74 KiB, two workgroups per CU)
+    if ((fmt == KM4 && km4_quad_takes(N, K, B)) || quad_scaled_takes(fmt, N, K, B)) return true;
     if (B < 3 || B > 8 || N < 16) return false;
     // below 16384 rows the dot2 path is as fast at B = 3, 4 (fp4 4096 x 2048:
     // 6.8 us against 7.4 us); from B = 5 the matrix cores win at any size
@@ -890,10 +913,6 @@ static bool mfma_eligible(int fmt, const void *plane, int64_t N, int64_t K, int 
     if (N <= 8192 && B >= 5 && K == 2048 && (fmt == INT4 || fmt == FP4 || fmt == INT8)) return false;
     if (fmt == INT4AFF && K > 2048) return false;   // its scale + bias stretch fits four pieces per lane
     if (K % ((fmt == INT8 || fmt == INT8KM) ? 256 : 512) != 0 || K > 4096) return false;
-    // a group's scales (tables) are read as 16-byte pieces
-    if (reinterpret_cast<uintptr_t>(plane) % 16 != 0) return false;
-    // the 4x4x4 kernels stage x alone (at most 74 KiB, two workgroups per CU)
-    if ((fmt == KM4 && km4_quad_takes(K, B)) || quad_scaled_takes(fmt, N, K, B)) return true;
     size_t lds = (fmt == INT4) ? mfma_lds_bytes<INT4>(K, B)
                  : (fmt == INT4AFF) ? mfma_lds_bytes<INT4AFF>(K, B)
                  : (fmt == FP4) ? mfma_lds_bytes<FP4>(K, B)
@@ -947,7 +966,7 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
                               int B, float *y, hipStream_t st, bool *handled, uint64_t *hdr) {
     *handled = mfma_eligible(fmt, plane, N, K, B);
     if (!*handled) return hipSuccess;
-    if (fmt == KM4 && km4_quad_takes(K, B)) return launch_km4_quad(codes, plane, N, K, x, B, y, st, hdr);
+    if (fmt == KM4 && km4_quad_takes(N, K, B)) return launch_km4_quad(codes, plane, N, K, x, B, y, st, hdr);
     if (quad_scaled_takes(fmt, N, K, B))
         return fmt == INT4 ? launch_quad_scaled<INT4>(codes, plane, N, K, x, B, y, st, hdr)
                            : launch_quad_scaled<INT4AFF>(codes, plane, N, K, x, B, y, st, hdr);

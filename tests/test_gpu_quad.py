@@ -1,14 +1,15 @@
-"""The 4x4x4-block matrix-core kernels on matrices the matrix-core path takes
-(at least 16384 rows at batch 3-4): km4 at batch 3 and 4 (K of 512, 1024,
-2048 or 4096; two row quads per wave below 196608 rows, one at K = 4096, and
-four above, two at K = 4096) and int4 / affine int4 at batch 3 to 8 (one
-token quad up to batch 4, two above; K of 512, 1024, 2048, and 4096 for int4;
-batch 2 from 16384 rows for int4 and 32768 for affine int4).
-Every instantiation runs on a ragged matrix (rows not a multiple of the
-wave's rows; K = 1024 for the scale formats in test_gpu_parity.py). The GPU
-packs and multiplies the whole matrix; the oracle packs and multiplies
-sampled rows, the last 16 rows of the ragged tail included. The 248320 x 2048
-km4 head at batch 4 is compared on every row in test_gpu_configs.py."""
+"""The 4x4x4-block matrix-core kernels: km4 at batch 3 and 4 (K of 512,
+1024, 2048 or 4096) and int4 / affine int4 at batch 2 to 8 (one token quad up
+to batch 4, two above; K of 512, 1024, 2048, and 4096 for int4). They take
+matrices from 8192 rows at batch 3-8 (affine int4 from 4096 rows at batch
+5-8) and at batch 2 from 16384 (int4) or 32768 rows (affine int4); rows per
+wave grow with the matrix (one row quad per wave below 32768 rows, two above,
+four for km4 from 196608 rows; scale formats at batch <= 4 take two from
+65536). Every launch branch runs on a ragged matrix (rows not a multiple of the
+wave's rows). The GPU packs and multiplies the whole matrix; the oracle packs
+and multiplies sampled rows, the last 16 rows of the ragged tail included.
+The 248320 x 2048 km4 head at batch 4 is compared on every row in
+test_gpu_configs.py."""
 import numpy as np
 import pytest
 
@@ -20,8 +21,10 @@ from tests.gpu_helpers import RTOL, dev, host, rel_err, sample_rows
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    (16384 + 13, 512),     # two quads, one chunk per lane
-    (16384 + 2, 2048),     # two quads, four chunks
+    (8192 + 7, 1024),      # one quad, two chunks per lane
+    (32768 + 9, 2048),     # two quads, four chunks
+    (16384 + 13, 512),     # one quad, one chunk per lane
+    (16384 + 2, 2048),     # one quad, four chunks
     (16384 + 1, 4096),     # one quad, eight chunks
     (196608 + 37, 512),    # four quads, one chunk
     (196608 + 6, 1024),    # four quads, two chunks
@@ -58,6 +61,9 @@ def test_km4_quad_argmax_matches_its_matvec():
 
 
 SCALED_CASES = [
+    ("int4", 8192 + 5, 2048),       # one row quad
+    ("int4", 65536 + 3, 512),       # two row quads at every batch
+    ("int4aff", 4096 + 3, 1024),    # batch 5-8 only (batch 2-4 keep the dot2 kernels)
     ("int4", 16384 + 13, 512),
     ("int4", 16384 + 2, 2048),
     ("int4", 16384 + 1, 4096),
