@@ -513,18 +513,18 @@ __device__ __forceinline__ h4q lds_h4(uint32_t addr) {
 }
 __host__ __device__ constexpr int quad_x_row(int K) { return (K / 32) * kQuadXChunk + kQuadXRowPad; }
 
-template <int Q, int KC>   // K = 512 * KC
+template <int Q, int KC, int BQ = 1>   // K = 512 * KC; BQ token quads
 __global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ lut, int64_t N,
                                                                const _Float16 *__restrict__ x, int B,
                                                                float *__restrict__ y, uint64_t *__restrict__ hdr) {
-    constexpr int K = 512 * KC, ROWS = 4 * Q, XROW = quad_x_row(K);
+    constexpr int K = 512 * KC, ROWS = 4 * Q, NT = 4 * BQ, XROW = quad_x_row(K);
     constexpr int TW = (ROWS * 8 + 63) / 64;   // table dwords per lane per group
     extern __shared__ __align__(16) uint8_t qlds[];
     // fused argmax: the first workgroup zeroes the reduction header
     if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
     _Float16 *xs = reinterpret_cast<_Float16 *>(qlds);
-    for (int i = threadIdx.x; i < 4 * (K / 4); i += 64 * kQuadWaves) {
+    for (int i = threadIdx.x; i < NT * (K / 4); i += 64 * kQuadWaves) {
         const int b = i / (K / 4), k = 4 * (i - b * (K / 4));
         uint2 v = make_uint2(0u, 0u);   // tokens >= B read zeros
         if (b < B) v = *reinterpret_cast<const uint2 *>(x + (size_t)b * K + k);
@@ -534,7 +534,7 @@ __global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int blk = lane >> 2, j = lane & 3;
     // per-wave tables [ROWS][16] fp16 (32-byte aligned: the code offsets are OR-ed in)
-    uint8_t *tab = qlds + 4 * XROW * 2 + wave * (ROWS * 32);
+    uint8_t *tab = qlds + NT * XROW * 2 + wave * (ROWS * 32);
     const uint32_t rb = (uint32_t)(uintptr_t)tab + 32u * j;   // row j of quad 0
     const uint32_t xa = (uint32_t)(uintptr_t)xs + (uint32_t)((j * XROW + blk * kQuadXChunk) * 2);
     const int64_t ngroups = (N + ROWS - 1) / ROWS;
@@ -562,16 +562,22 @@ __global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__
             if (i < ROWS * 8) reinterpret_cast<uint32_t *>(tab)[i] = tv[q];
         }
         wave_sync_lds();
-        f4 acc[Q];
+        f4 acc[Q][BQ];
 #pragma unroll
-        for (int u = 0; u < Q; u++) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < Q; u++)
+#pragma unroll
+            for (int p = 0; p < BQ; p++) acc[u][p] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kc = 0; kc < KC; kc++) {
 #pragma unroll
             for (int d = 0; d < 4; d++) {
                 // codes 8d .. 8d + 7 of the chunk: two k-steps of 4
-                const h4q x0 = lds_h4(xa + (uint32_t)((16 * kc * kQuadXChunk + 8 * d) * 2));
-                const h4q x1 = lds_h4(xa + (uint32_t)((16 * kc * kQuadXChunk + 8 * d + 4) * 2));
+                h4q x0[BQ], x1[BQ];
+#pragma unroll
+                for (int p = 0; p < BQ; p++) {
+                    x0[p] = lds_h4(xa + (uint32_t)((p * 4 * XROW + 16 * kc * kQuadXChunk + 8 * d) * 2));
+                    x1[p] = lds_h4(xa + (uint32_t)((p * 4 * XROW + 16 * kc * kQuadXChunk + 8 * d + 4) * 2));
+                }
 #pragma unroll
                 for (int u = 0; u < Q; u++) {
                     const uint32_t w = (d == 0) ? cw[u][kc].x : (d == 1) ? cw[u][kc].y : (d == 2) ? cw[u][kc].z : cw[u][kc].w;
@@ -584,20 +590,26 @@ __global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__
                     const uint32_t t6 = lds_u16(or_code_byte<3>(ub, ml)), t7 = lds_u16(or_code_byte<3>(ub, mh));
                     const u2v b0 = {t0 | (t1 << 16), t2 | (t3 << 16)};
                     const u2v b1 = {t4 | (t5 << 16), t6 | (t7 << 16)};
-                    acc[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(x0, __builtin_bit_cast(h4q, b0), acc[u], 0, 0, 0);
-                    acc[u] = __builtin_amdgcn_mfma_f32_4x4x4f16(x1, __builtin_bit_cast(h4q, b1), acc[u], 0, 0, 0);
+#pragma unroll
+                    for (int p = 0; p < BQ; p++) {
+                        acc[u][p] = __builtin_amdgcn_mfma_f32_4x4x4f16(x0[p], __builtin_bit_cast(h4q, b0), acc[u][p], 0, 0, 0);
+                        acc[u][p] = __builtin_amdgcn_mfma_f32_4x4x4f16(x1[p], __builtin_bit_cast(h4q, b1), acc[u][p], 0, 0, 0);
+                    }
                 }
             }
         }
         wave_sync_lds();   // the next group rewrites the tables
-        // add the 16 block sums: v[4u + i] (token i, row 4u + j), halves
-        // exchanged across lane bit 5 and 4, then butterflies over bits 3, 2
-        constexpr int V = 4 * Q;
+        // add the 16 block sums: v[(u * BQ + p) * 4 + i] (token 4p + i, row
+        // 4u + j), halves exchanged across lane bits 5 and 4, then butterflies
+        // over bits 3, 2
+        constexpr int V = 4 * Q * BQ;
         float v[V];
 #pragma unroll
         for (int u = 0; u < Q; u++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) v[4 * u + i] = acc[u][i];
+            for (int p = 0; p < BQ; p++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) v[(u * BQ + p) * 4 + i] = acc[u][p][i];
 #pragma unroll
         for (int m = 0; m < V / 2; m++) v[m] = half_swap_add<32>(v[m], v[m + V / 2]);
 #pragma unroll
@@ -611,24 +623,31 @@ __global__ __launch_bounds__(64 * kQuadWaves) void mv_km4_quad(const uint8_t *__
             const int base = ((lane & 32) ? V / 2 : 0) + ((lane & 16) ? V / 4 : 0);
 #pragma unroll
             for (int m = 0; m < V / 4; m++) {
-                const int idx = base + m, u = idx >> 2, i = idx & 3;
+                const int idx = base + m, u = idx / (4 * BQ), p = (idx / 4) % BQ, i = idx % 4;
                 const int64_t row = row0 + 4 * u + j;
-                if (row < N && i < B) y[(size_t)i * N + row] = v[m];
+                const int b = 4 * p + i;
+                if (row < N && b < B) y[(size_t)b * N + row] = v[m];
             }
         }
     }
 }
 
-template <int Q, int KC>
+template <int Q, int KC, int BQ = 1>
 static hipError_t launch_km4_quad_q(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
                                     float *y, hipStream_t st, uint64_t *hdr) {
     constexpr int K = 512 * KC;
-    const size_t lds = (size_t)4 * quad_x_row(K) * 2 + (size_t)kQuadWaves * Q * 128;
+    const size_t lds = (size_t)4 * BQ * quad_x_row(K) * 2 + (size_t)kQuadWaves * Q * 128;
+    if (lds > 64 * 1024) {
+        // K = 4096 with two token quads: 77 KiB, two workgroups still fit a CU's 160 KiB
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&mv_km4_quad<Q, KC, BQ>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
     const int64_t groups = (N + 4 * Q - 1) / (4 * Q);
     const int64_t want = (groups + kQuadWaves - 1) / kQuadWaves;
     const int64_t cap = 2 * (int64_t)device_cu_count();   // two workgroups per CU stay resident
     const int grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL((mv_km4_quad<Q, KC>), dim3(grid), dim3(64 * kQuadWaves), lds, st, codes,
+    hipLaunchKernelGGL((mv_km4_quad<Q, KC, BQ>), dim3(grid), dim3(64 * kQuadWaves), lds, st, codes,
                        reinterpret_cast<const uint16_t *>(plane), N, reinterpret_cast<const _Float16 *>(x), B, y, hdr);
     return hipGetLastError();
 }
@@ -852,9 +871,12 @@ static bool quad_scaled_takes(int fmt, int64_t N, int64_t K, int B) {
 }
 
 // from 8192 rows: 8192 x 2048 at B = 4 5.8 us against 7.1 for the dot2 kernel
-// (4096 rows: 5.2 against 4.8)
+// (4096 rows: 5.2 against 4.8). Batch 5-8 runs two token quads: against the
+// 16 x 16 x 32 register-table kernel at B = 8, 8192 / 65536 / 124160 rows
+// 7.1 / 21.0 / 37.7 us against 9.3 / 23.4 / 41.1, the 248320-row head 77.2
+// against 76.6 (72-77 against 75-77 in earlier runs).
 static bool km4_quad_takes(int64_t N, int64_t K, int B) {
-    return B >= 3 && B <= 4 && N >= 8192 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
+    return B >= 3 && B <= 8 && N >= 8192 && (K == 512 || K == 1024 || K == 2048 || K == 4096);
 }
 
 // Quads per wave: four on the tallest heads, two from 32768 rows, one below
@@ -865,6 +887,12 @@ template <int KC>
 static hipError_t launch_km4_quad_k(const uint8_t *codes, const void *plane, int64_t N, const void *x, int B,
                                     float *y, hipStream_t st, uint64_t *hdr) {
     constexpr int QT = (KC < 8) ? 4 : 2, QM = (KC < 8) ? 2 : 1;
+    if (B > 4) {
+        // two token quads: two row quads from 32768 rows (at B = 8 on the
+        // 248320-row head four measured 76 against 72 us), one below
+        if (N >= 32768) return launch_km4_quad_q<2, KC, 2>(codes, plane, N, x, B, y, st, hdr);
+        return launch_km4_quad_q<1, KC, 2>(codes, plane, N, x, B, y, st, hdr);
+    }
     if (N >= 196608) return launch_km4_quad_q<QT, KC>(codes, plane, N, x, B, y, st, hdr);
     if (N >= 32768) return launch_km4_quad_q<QM, KC>(codes, plane, N, x, B, y, st, hdr);
     return launch_km4_quad_q<1, KC>(codes, plane, N, x, B, y, st, hdr);

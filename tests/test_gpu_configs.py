@@ -61,8 +61,9 @@ def test_km4_lm_head_pack_all_rows(lm_head):
 
 @pytest.mark.parametrize("B", [1, 4, 8])
 def test_km4_lm_head_matvec_all_rows(lm_head, B):
-    """Batch 1 and 8 are the benchmarked calls; batch 4 runs the 4x4x4-block
-    kernel with four row quads per wave."""
+    """Batch 1 and 8 are the benchmarked calls; batch 4 and 8 run the
+    4x4x4-block kernel (four row quads per wave at batch 4, two row quads and
+    two token quads at batch 8)."""
     c, codes, lut, oc, ol = lm_head
     x = c.x[:B]
     y = host(qmv.qmatvec_km4(codes, lut, dev(x)))

@@ -1,11 +1,11 @@
-"""The 4x4x4-block matrix-core kernels: km4 at batch 3 and 4 (K of 512,
-1024, 2048 or 4096) and int4 / affine int4 at batch 2 to 8 (one token quad up
-to batch 4, two above; K of 512, 1024, 2048, and 4096 for int4). They take
+"""The 4x4x4-block matrix-core kernels: km4 at batch 3 to 8 (K of 512, 1024,
+2048 or 4096) and int4 / affine int4 at batch 2 to 8 (K of 512, 1024, 2048,
+and 4096 for int4); one token quad up to batch 4, two above. They take
 matrices from 8192 rows at batch 3-8 (affine int4 from 4096 rows at batch
 5-8) and at batch 2 from 16384 (int4) or 32768 rows (affine int4); rows per
 wave grow with the matrix (one row quad per wave below 32768 rows, two above,
-four for km4 from 196608 rows; scale formats at batch <= 4 take two from
-65536). Every launch branch runs on a ragged matrix (rows not a multiple of the
+four for km4 at batch <= 4 from 196608 rows; scale formats at batch <= 4 take
+two from 65536). Every launch branch runs on a ragged matrix (rows not a multiple of the
 wave's rows). The GPU packs and multiplies the whole matrix; the oracle packs
 and multiplies sampled rows, the last 16 rows of the ragged tail included.
 The 248320 x 2048 km4 head at batch 4 is compared on every row in
@@ -34,12 +34,12 @@ CASES = [
 
 @pytest.mark.parametrize("N,K", CASES)
 def test_km4_quad_kernel_on_sampled_rows(N, K):
-    c = wl.small_dense("km4", N, K, batch=4, seed=N + K)
+    c = wl.small_dense("km4", N, K, batch=8, seed=N + K)
     print("km4 quad", N, K, flush=True)
     codes, lut = qmv.qpack_km4(dev(c.W))
     rows = np.unique(np.concatenate([sample_rows(N, n=64, seed=K), np.arange(N - 16, N)]))
     oc, ol = oracle.pack_km4(c.W[rows])
-    for B in (3, 4):
+    for B in (3, 4, 5, 8):
         y = host(qmv.qmatvec_km4(codes, lut, dev(c.x[:B])))
         assert y.shape == (B, N)
         assert np.all(np.isfinite(y))
@@ -50,9 +50,9 @@ def test_km4_quad_argmax_matches_its_matvec():
     """The fused argmax runs the same matvec kernel, so its index is the
     argmax of the plain call's output and its value that output's maximum."""
     N, K = 16384 + 13, 2048
-    c = wl.small_dense("km4", N, K, batch=4, seed=5)
+    c = wl.small_dense("km4", N, K, batch=8, seed=5)
     codes, lut = qmv.qpack_km4(dev(c.W))
-    for B in (3, 4):
+    for B in (3, 4, 8):
         x = dev(c.x[:B])
         y = host(qmv.qmatvec_km4(codes, lut, x))
         idx, val = qmv.qmatvec_argmax("km4", codes, lut, x)
