@@ -156,6 +156,31 @@ qmv_status qmatvec_int8(const int8_t *codes, const uint16_t *scale, int64_t N, i
                         const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                        const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+/* ---------------------------------------------------------------------- */
+/* 4-bit k-means rows on a row-tiled code plane [S2 secs. 1, 8: the lm_head */
+/* is the largest per-token matvec, its int4km form read once per token;   */
+/* S3 "Palettization": one 16-entry table per output row]. The same bytes  */
+/* as qpack_km4's code plane, reordered once (at weight load) so that a    */
+/* kernel can give each lane its own row: tile t holds rows 64t..64t+63    */
+/* and chunk q (16 bytes = codes 32q..32q+31) of row 64t + r sits at byte  */
+/* ((t * (K/32) + q) * 64 + r) * 16. Rows past N in the last tile are zero.*/
+/* ---------------------------------------------------------------------- */
+
+/* Bytes of the row-tiled plane: ceil(N / 64) * 64 * K / 2 (0 for sizes
+ * qtile_km4 refuses). */
+size_t qtile_km4_bytes(int64_t N, int64_t K);
+
+/* codes [N][K/2] (as qpack_km4 writes them) -> tiled [qtile_km4_bytes(N, K)]
+ * bytes; K % 32 == 0; both 16-byte aligned; the two must not overlap. */
+qmv_status qtile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *tiled, void *stream);
+
+/* y[0][n] = sum_k lut[n][code(n, k)] * x[0][k], fp32 accumulation, from the
+ * tiled plane and qpack_km4's lut [N][16] (4-byte aligned). Batch 1, x fp16
+ * [1][K], K in {512, 1024, 2048, 4096} (QMV_E_SHAPE otherwise, QMV_E_DTYPE
+ * for fp32 x); y fp32 [1][N]. */
+qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K,
+                             const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+
 qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K,
                            const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 /* int8km: N % 32 == 0; lut as qpack_int8km writes it (4-byte aligned). */

@@ -30,7 +30,8 @@ EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_
            "qmoe_route", "gather_qmatvec_workspace_bytes", "gather_qmatvec", "qmoe_ffn",
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qmatvec_argmax_noalloc",
            "qmatvec_argmax_noalloc_max_bytes", "qpack_int8_rows", "qembed_gather_int8",
-           "qmv_stream_read_sink_words", "qmv_stream_read")
+           "qmv_stream_read_sink_words", "qmv_stream_read", "qtile_km4_bytes", "qtile_km4",
+           "qmatvec_km4_tiled")
 
 
 class QmvError(RuntimeError):
@@ -85,6 +86,9 @@ def lib() -> ctypes.CDLL:
             "qembed_gather_int8": ([P, P, i64, i64, P, i64, P, P], ci),
             "qmv_stream_read_sink_words": ([sz], sz),
             "qmv_stream_read": ([P, sz, P, P], ci),
+            "qtile_km4_bytes": ([i64, i64], sz),
+            "qtile_km4": ([P, i64, i64, P, P], ci),
+            "qmatvec_km4_tiled": ([P, P, i64, i64, P, ci, ci, P, P], ci),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -355,6 +359,71 @@ def qmatvec_int8(codes, scale, x, y=None, stream=None):
 
 def qmatvec_km4(codes, lut, x, y=None, stream=None):
     return _matvec("qmatvec_km4", "km4", codes, lut, x, y, stream)
+
+
+def qtile_km4_bytes(N, K):
+    """Bytes of the row-tiled km4 code plane: whole 64-row tiles of K/2 bytes
+    per row (the size qtile_km4_bytes in the C ABI returns)."""
+    if N < 1 or K < 32 or K % 32:
+        _bad("qtile_km4_bytes", "N = %d, K = %d is out of range" % (N, K))
+    return (N + 63) // 64 * 64 * (K // 2)
+
+
+def qtile_km4(codes, tiled=None, stream=None):
+    """km4 codes [N, K/2] -> the row-tiled plane (uint8, qtile_km4_bytes(N, K)
+    bytes) that qmatvec_km4_tiled reads."""
+    torch = _torch()
+    fn = "qtile_km4"
+    N, K = _codes2d(fn, "km4", codes)
+    nb = qtile_km4_bytes(N, K)
+    tiled = _empty((nb,), torch.uint8, codes) if tiled is None else tiled
+    _tensor(fn, "tiled", tiled, shape=(nb,), itemsize=1)
+    _on_gpu(fn, codes, tiled)
+    _check(fn, lib().qtile_km4(_ptr(codes), N, K, _ptr(tiled), _stream(stream)))
+    return tiled
+
+
+def _tiled_args(fn, tiled, lut, x, y):
+    torch = _torch()
+    _tensor(fn, "lut", lut, itemsize=2, ndim=2)
+    N = lut.shape[0]
+    _tensor(fn, "lut", lut, shape=(N, 16))
+    _fp(fn, "x", x, allow_f32=False)
+    x2 = x.view(1, -1) if x.dim() == 1 else x
+    if x2.dim() != 2 or x2.shape[0] != 1:
+        _bad(fn, "x must be [K] or [1, K], got shape %s" % (tuple(x.shape),))
+    K = x2.shape[1]
+    if K not in (512, 1024, 2048, 4096):
+        _bad(fn, "K = %d: the tiled kernel takes K in 512, 1024, 2048, 4096" % K)
+    _tensor(fn, "tiled", tiled, shape=(qtile_km4_bytes(N, K),), itemsize=1)
+    y = _y_out(fn, y, (1, N), torch.float32, tiled)
+    _on_gpu(fn, tiled, lut, x2, y)
+    return (_ptr(tiled), _ptr(lut), N, K, _ptr(x2), QMV_F16, 1, _ptr(y)), (tiled, lut, x2), y
+
+
+def qmatvec_km4_tiled(tiled, lut, x, y=None, stream=None):
+    """Batch-1 km4 matvec from the row-tiled plane: x fp16 [K] or [1, K] -> y fp32 [1, N]."""
+    fn = "qmatvec_km4_tiled"
+    args, _, y = _tiled_args(fn, tiled, lut, x, y)
+    _check(fn, lib().qmatvec_km4_tiled(*args, _stream(stream)))
+    return y
+
+
+def qmatvec_km4_tiled_call(tiled, lut, x, y=None, stream=None):
+    """qmatvec_km4_tiled with the argument checks done once: returns a function
+    of no arguments that launches the same call (see qmatvec_call)."""
+    fn = "qmatvec_km4_tiled"
+    args, keep, y = _tiled_args(fn, tiled, lut, x, y)
+    f = lib().qmatvec_km4_tiled
+    st = None if stream is None else ctypes.c_void_p(stream)
+    torch = _torch()
+
+    def call():
+        _check(fn, f(*args, st if st is not None else ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        return y
+
+    call.tensors = keep + (y,)
+    return call
 
 
 def qmatvec_int4aff(codes, plane, x, y=None, stream=None):

@@ -194,6 +194,30 @@ qmv_status qmatvec_km4(const uint8_t *codes, const uint16_t *lut, int64_t N, int
     return launch_status(qmv::launch_matvec(QMV_KM4, codes, lut, N, K, x, xdt, B, y, as_stream(stream)));
 }
 
+size_t qtile_km4_bytes(int64_t N, int64_t K) {
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K) return 0;
+    return qmv::km4_tiled_bytes(N, K);
+}
+
+qmv_status qtile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *tiled, void *stream) {
+    if (!codes || !tiled) return QMV_E_NULL;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > (int64_t(1) << 40) / K) return QMV_E_SHAPE;
+    if (!aligned(codes, 16) || !aligned(tiled, 16)) return QMV_E_ALIGN;
+    forget_earlier_errors();
+    return launch_status(qmv::launch_tile_km4(codes, N, K, tiled, as_stream(stream)));
+}
+
+qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K, const void *x,
+                             qmv_dtype xdt, int B, float *y, void *stream) {
+    qmv_status s = check_mv(tiled, lut, 4, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    if (xdt != QMV_F16) return QMV_E_DTYPE;
+    if (B != 1 || !qmv::km4_tiled_supported(K)) return QMV_E_SHAPE;
+    forget_earlier_errors();
+    return launch_status(qmv::launch_matvec_km4_tiled(tiled, lut, N, K, reinterpret_cast<const _Float16 *>(x), y,
+                                                      as_stream(stream)));
+}
+
 qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K, const void *x,
                            qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, plane, 4, N, K, x, xdt, B, y);

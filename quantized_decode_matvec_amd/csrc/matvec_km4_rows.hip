@@ -1,0 +1,198 @@
+// Batch-1 k-means palettized matvec on a row-tiled code plane, one row per
+// lane, two codes per table lookup ("Dense-path int4km coverage + flagship
+// Qwen3.6-35B - session findings & methods", sections 1 and 8: the lm_head is
+// the largest per-token matvec and its 4-bit palettized form is read once per
+// token; "coreai-optimization (coreai-opt) reference", "Palettization": a
+// 16-entry table per output row, 4-bit indices).
+//
+// A 16-entry table lookup per code costs an address, an LDS read and half of
+// a merge + v_dot2, which keeps the row-per-wave kernel bound by instruction
+// issue. Here every byte of codes (two indices) is looked up at once in a
+// 256-entry table of fp16 pairs:
+//   pair[e] = (lut[e & 15], lut[e >> 4])   (low nibble = even element)
+// so one lookup yields the half2 operand of one v_dot2. A 1 KiB pair table per
+// row cannot be shared by the lanes of a wave without bank conflicts, so each
+// lane owns one row: a 64-row tile's tables are stored transposed, entry e of
+// row r at dword 64 e + r, and lane r only touches LDS bank r mod 32 (64 KiB
+// per tile). The byte address 256 e + 4 r is one v_perm of the code word and
+// the lane's 4 r. Per code: half a v_perm, half an LDS read and half a v_dot2,
+// plus the table build (256 entries per row: one v_perm and one LDS write
+// each, 1/8 of the lookups).
+//
+// Work split: a 16-wave workgroup takes a 64-row tile; wave w takes the code
+// chunks (16 bytes = 32 codes of a row) CPW w .. CPW w + CPW - 1, so the x
+// slice it multiplies is the same for all of its lanes and is read with
+// scalar loads, the SGPR operand of v_dot2. Wave w builds the 16 table entries
+// with low nibble in 4a..4a+3 and high nibble in 4b..4b+3 (a = w & 3,
+// b = w >> 2), which needs 16 bytes of its row's table. The 16 partial sums of
+// a row are added in wave order through LDS (deterministic).
+//
+// Row-tiled code layout (tile t = rows 64 t .. 64 t + 63, Q = K / 32 chunks
+// per row): chunk q of row 64 t + r is the 16 bytes at ((t Q + q) 64 + r) 16,
+// so a wave-wide 16-byte load reads 1 KiB of consecutive bytes and a wave's
+// CPW chunks of a tile are CPW consecutive KiB. Rows past N in the last tile
+// are zero.
+//
+// Each workgroup takes TPW consecutive tiles; the table words of a tile are
+// issued before its codes, so the pair table is built while the codes are
+// still arriving, and tile i + 1's loads are in flight while tile i is built
+// and looked up.
+#include "qmv_device.h"
+#include "qmv_launch.h"
+
+namespace qmv {
+
+constexpr int kRowsTile = 64;                                    // rows per tile (one per lane)
+constexpr int kPairEntries = 256;                                // table entries per row
+constexpr int kTileWaves = 16;                                   // waves per workgroup
+
+// read-only memory in the constant address space: uniform loads from it are
+// scalar loads into SGPRs
+typedef __attribute__((address_space(4))) const uint32_t kconst_u32;
+
+// dword at byte offset `a` of LDS (a is 4-aligned and below the allocation)
+__device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t a) {
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + a);
+}
+
+template <int CPW, int TPW>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
+    float *__restrict__ y, int64_t tiles) {
+    constexpr int W = kTileWaves;
+    constexpr int Q = W * CPW;   // chunks per row
+    // pair tables at LDS address 0 (a static array: table addresses need no
+    // base added), then the W x 64 partial sums
+    __shared__ __align__(16) uint32_t lds[kPairEntries * kRowsTile + W * kRowsTile];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int la = (wave & 3) * 2, hb = (wave >> 2) * 2;   // table words of this wave's build share
+    const uint32_t roff = (uint32_t)lane * 4u;
+    float *part = reinterpret_cast<float *>(lds + kPairEntries * kRowsTile);
+
+    uint4 cw[TPW > 1 ? 2 : 1][CPW];
+    uint2 lo[TPW > 1 ? 2 : 1], hi[TPW > 1 ? 2 : 1];
+    // loads of tile t into buffer k; a tile past the end reads the first KiB of
+    // the plane and row 0's table (the same bytes for every wave: cache hits)
+    auto load = [&](int64_t t, int k) {
+        const bool past = t >= tiles;
+        const int64_t row = (past ? 0 : t) * kRowsTile + lane;
+        const uint32_t *lr = reinterpret_cast<const uint32_t *>(lut + (size_t)(row < N ? row : N - 1) * 16);
+        lo[k] = *reinterpret_cast<const uint2 *>(lr + la);
+        hi[k] = *reinterpret_cast<const uint2 *>(lr + hb);
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            const size_t off = past ? (size_t)lane * 16 : (((size_t)t * Q + CPW * wave + j) * kRowsTile + lane) * 16;
+            cw[k][j] = load_stream16(codes + off);
+        }
+    };
+    auto step = [&](int64_t t, int k) {
+        {
+            // entries (lo = 4a + l, hi = 4b + h): low half from the word pair
+            // lo[k], high half from hi[k]
+            const uint32_t lw[2] = {lo[k].x, lo[k].y}, hw[2] = {hi[k].x, hi[k].y};
+#pragma unroll
+            for (int h = 0; h < 4; h++)
+#pragma unroll
+                for (int l = 0; l < 4; l++) {
+                    const uint32_t sel =
+                        ((l & 1) ? 0x00000706u : 0x00000504u) | ((h & 1) ? 0x03020000u : 0x01000000u);
+                    const int e = ((hb * 2 + h) << 4) + (la * 2 + l);
+                    lds[e * kRowsTile + lane] = __builtin_amdgcn_perm(lw[l >> 1], hw[h >> 1], sel);
+                }
+        }
+        __syncthreads();
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < CPW; j++) {
+            const kconst_u32 *xq = (const kconst_u32 *)x + (size_t)(CPW * wave + j) * 16;   // wave-uniform
+            const uint32_t w4[4] = {cw[k][j].x, cw[k][j].y, cw[k][j].z, cw[k][j].w};
+#pragma unroll
+            for (int d = 0; d < 4; d++)
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    // byte b of code word d -> table address 256 * byte + 4 * lane
+                    const uint32_t a = __builtin_amdgcn_perm(w4[d], roff, 0x0C0C0000u | ((4u + b) << 8));
+                    const uint32_t v = lds_word(lds, a);
+                    if (b & 1) acc1 = dot2(as_h2(v), as_h2(xq[4 * d + b]), acc1);
+                    else acc0 = dot2(as_h2(v), as_h2(xq[4 * d + b]), acc0);
+                }
+        }
+        part[wave * kRowsTile + lane] = acc0 + acc1;
+        __syncthreads();
+        if (wave == 0) {
+            float s = part[lane];
+#pragma unroll
+            for (int w = 1; w < W; w++) s += part[w * kRowsTile + lane];
+            const int64_t row = t * kRowsTile + lane;
+            if (t < tiles && row < N) y[row] = s;
+        }
+    };
+    const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    load(t0, 0);
+    if constexpr (TPW == 1) {
+        step(t0, 0);
+    } else {
+        // straight-line code: in a loop the compiler waits for every
+        // outstanding load at the back edge, the prefetch included
+        load(t0 + 1, 1);
+        step(t0, 0);
+        step(t0 + 1, 1);
+    }
+}
+
+template <int CPW, int TPW>
+static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, float *y,
+                               hipStream_t st) {
+    const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
+    const int64_t grid = (tiles + TPW - 1) / TPW;
+    hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes, lut, N,
+                       x, y, tiles);
+    return hipGetLastError();
+}
+
+bool km4_tiled_supported(int64_t K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
+
+hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                                   const _Float16 *x, float *y, hipStream_t st) {
+    const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
+    // two tiles per workgroup once there are enough workgroups to keep two on
+    // every CU; fewer tiles spread one per workgroup
+    const bool two = tiles >= 4 * (int64_t)device_cu_count();
+    switch (K) {
+    case 512: return two ? launch_tiled<1, 2>(codes, lut, N, x, y, st) : launch_tiled<1, 1>(codes, lut, N, x, y, st);
+    case 1024: return two ? launch_tiled<2, 2>(codes, lut, N, x, y, st) : launch_tiled<2, 1>(codes, lut, N, x, y, st);
+    case 2048: return two ? launch_tiled<4, 2>(codes, lut, N, x, y, st) : launch_tiled<4, 1>(codes, lut, N, x, y, st);
+    case 4096: return launch_tiled<8, 1>(codes, lut, N, x, y, st);   // 32 code registers per tile
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// Row-tiled copy of a canonical [N][K/2] code plane (one thread per 16-byte
+// chunk of the destination; rows past N are zero).
+__global__ void tile_codes_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t N, int Q,
+                                  int64_t total) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // destination index
+    if (i >= total) return;
+    const int r = (int)(i % kRowsTile);
+    const int64_t tq = i / kRowsTile;
+    const int q = (int)(tq % Q);
+    const int64_t t = tq / Q;
+    const int64_t n = t * kRowsTile + r;
+    dst[i] = n < N ? src[n * Q + q] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+size_t km4_tiled_bytes(int64_t N, int64_t K) {
+    return (size_t)((N + kRowsTile - 1) / kRowsTile) * kRowsTile * (size_t)(K / 2);
+}
+
+hipError_t launch_tile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *out, hipStream_t st) {
+    const int Q = (int)(K / 32);
+    const int64_t total = (int64_t)km4_tiled_bytes(N, K) / 16;
+    const int64_t grid = (total + 255) / 256;
+    hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)grid), dim3(256), 0, st,
+                       reinterpret_cast<const uint4 *>(codes), reinterpret_cast<uint4 *>(out), N, Q, total);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

@@ -158,3 +158,19 @@ def test_argmax_and_embedding_validation(L):
     assert G(FAKE, FAKE, 100, 16, NUL, 0, NUL, S) == 0          # T = 0: nothing to do
     assert L.qpack_int8_rows(FAKE, 5, 10, 16, FAKE, FAKE, S) == E_DTYPE
     assert L.qpack_int8_rows(FAKE, 0, 0, 16, FAKE, FAKE, S) == E_SHAPE
+
+
+def test_tiled_km4_validation(L):
+    half = ctypes.c_void_p(0x10002)
+    assert L.qtile_km4_bytes(100, 2048) == 128 * 1024        # rows padded to whole 64-row tiles
+    assert L.qtile_km4_bytes(64, 512) == 64 * 256
+    assert L.qtile_km4_bytes(0, 2048) == 0 and L.qtile_km4_bytes(4, 48) == 0
+    assert L.qtile_km4(NUL, 4, 64, FAKE, S) == E_NULL
+    assert L.qtile_km4(FAKE, 4, 48, FAKE, S) == E_SHAPE
+    assert L.qtile_km4(FAKE, 4, 64, ODD, S) == E_ALIGN
+    assert L.qmatvec_km4_tiled(NUL, FAKE, 64, 2048, FAKE, 1, 1, FAKE, S) == E_NULL
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 0, 1, FAKE, S) == E_DTYPE   # fp32 x
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 2, FAKE, S) == E_SHAPE   # batch 1 only
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K not a tile width
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 8192, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4_tiled(FAKE, half, 64, 2048, FAKE, 1, 1, FAKE, S) == E_ALIGN   # 32-bit table words

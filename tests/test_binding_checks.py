@@ -145,3 +145,18 @@ def test_embedding_and_stream_checks():
     raises(ValueError, "scale has shape", qmv.qembed_gather_int8, q, z(99, dtype=u16), z(3, dtype=i32))
     raises(TypeError, "dtype", qmv.qembed_gather_int8, q, s, z(3, dtype=torch.int64))
     raises(ValueError, "out has shape", qmv.qembed_gather_int8, q, s, z(3, dtype=i32), out=z(3, 63))
+
+
+def test_tiled_km4_checks():
+    N, K = 100, 2048
+    t, lut, x = z(128 * K // 2, dtype=u8), z(N, 16, dtype=u16), z(1, K)
+    assert qmv.qtile_km4_bytes(N, K) == 128 * K // 2
+    raises(ValueError, "GPU memory", qmv.qmatvec_km4_tiled, t, lut, x)            # all right but the device
+    raises(ValueError, "tiled has shape", qmv.qmatvec_km4_tiled, z(N * K // 2, dtype=u8), lut, x)   # unpadded
+    raises(ValueError, "lut has shape", qmv.qmatvec_km4_tiled, t, z(N, 15, dtype=u16), x)
+    raises(TypeError, "dtype", qmv.qmatvec_km4_tiled, t, lut, z(1, K, dtype=f32))
+    raises(ValueError, r"\[K\] or \[1, K\]", qmv.qmatvec_km4_tiled, t, lut, z(2, K))
+    raises(ValueError, "K = 1536", qmv.qmatvec_km4_tiled, z(128 * 768, dtype=u8), lut, z(1, 1536))
+    raises(ValueError, "contiguous", qmv.qmatvec_km4_tiled, t, lut, z(1, 2 * K)[:, ::2])
+    raises(ValueError, "GPU memory", qmv.qtile_km4, z(N, K // 2, dtype=u8))
+    raises(ValueError, "tiled has shape", qmv.qtile_km4, z(N, K // 2, dtype=u8), tiled=z(N * K // 2, dtype=u8))

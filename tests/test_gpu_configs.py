@@ -71,6 +71,17 @@ def test_km4_lm_head_matvec_all_rows(lm_head, B):
     assert rel_err(y, want) <= RTOL
 
 
+def test_km4_lm_head_tiled_all_rows(lm_head):
+    """The benchmarked call: batch 1 from the row-tiled plane, every row."""
+    c, codes, lut, oc, ol = lm_head
+    tiled = qmv.qtile_km4(codes)
+    T = (oc.shape[0] + 63) // 64
+    want_t = oc.reshape(T, 64, -1, 16).transpose(0, 2, 1, 3).reshape(-1)   # 248320 rows: whole tiles
+    assert np.array_equal(host(tiled), want_t)
+    y = host(qmv.qmatvec_km4_tiled(tiled, lut, dev(c.x[:1])))
+    assert rel_err(y, oracle.matvec("km4", oc, ol, c.x[:1])) <= RTOL
+
+
 def test_int8_head_full_and_high_rows():
     c = wl.int8_head()
     codes, scale = oracle.pack_int8(c.W)
