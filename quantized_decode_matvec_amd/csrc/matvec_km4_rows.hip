@@ -72,19 +72,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 
     uint4 cw[TPW > 1 ? 2 : 1][CPW];
     uint2 lo[TPW > 1 ? 2 : 1], hi[TPW > 1 ? 2 : 1];
-    // loads of tile t into buffer k; a tile past the end reads the first KiB of
-    // the plane and row 0's table (the same bytes for every wave: cache hits)
+    // loads of tile t into buffer k; a tile past the end reads tile 0 again
+    // (read by the first workgroups: a cache hit, no HBM traffic)
     auto load = [&](int64_t t, int k) {
-        const bool past = t >= tiles;
-        const int64_t row = (past ? 0 : t) * kRowsTile + lane;
+        const int64_t tt = t < tiles ? t : 0;   // wave-uniform: a scalar select, no branch
+        const int64_t row = tt * kRowsTile + lane;
         const uint32_t *lr = reinterpret_cast<const uint32_t *>(lut + (size_t)(row < N ? row : N - 1) * 16);
         lo[k] = *reinterpret_cast<const uint2 *>(lr + la);
         hi[k] = *reinterpret_cast<const uint2 *>(lr + hb);
+        const uint8_t *tb = codes + ((size_t)tt * Q + CPW * wave) * (kRowsTile * 16) + lane * 16;
 #pragma unroll
-        for (int j = 0; j < CPW; j++) {
-            const size_t off = past ? (size_t)lane * 16 : (((size_t)t * Q + CPW * wave + j) * kRowsTile + lane) * 16;
-            cw[k][j] = load_stream16(codes + off);
-        }
+        for (int j = 0; j < CPW; j++) cw[k][j] = load_stream16(tb + j * (kRowsTile * 16));
     };
     auto step = [&](int64_t t, int k) {
         {
@@ -103,9 +101,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         }
         __syncthreads();
         float acc0 = 0.f, acc1 = 0.f;
+        // x is re-read per tile (scalar cache hits) rather than held in SGPRs
+        // from one tile to the next, which would spill them
+        const kconst_u32 *xw = (const kconst_u32 *)x;
+        asm volatile("" : "+s"(xw));
 #pragma unroll
         for (int j = 0; j < CPW; j++) {
-            const kconst_u32 *xq = (const kconst_u32 *)x + (size_t)(CPW * wave + j) * 16;   // wave-uniform
+            const kconst_u32 *xq = xw + (size_t)(CPW * wave + j) * 16;   // wave-uniform
             const uint32_t w4[4] = {cw[k][j].x, cw[k][j].y, cw[k][j].z, cw[k][j].w};
 #pragma unroll
             for (int d = 0; d < 4; d++)
