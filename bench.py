@@ -376,6 +376,18 @@ def main():
         extras["stream_read_GBps"] = stream_rate(nbytes)
         log("stream read %.1f GB/s" % extras["stream_read_GBps"])
 
+        # batch 2-4 from the row-tiled plane (one table lookup feeds B products)
+        for bb in (2, 3, 4):
+            ct = [qmv.qmatvec_km4_tiled_call(tt, ll, x8[:bb], y=y[:bb]) for tt, ll in tiled]
+            mst = timed(lambda i: ct[i % len(ct)](), args.steps // 2, args.warmup)
+            extras["km4_tiled_B%d_us" % bb] = round(mst * 1e3, 2)
+            extras["km4_tiled_B%d_GBps" % bb] = round(nbytes / (mst * 1e-3) / 1e9, 1)
+            del ct
+        cr2 = [qmv.qmatvec_call("km4", cc, ll, x8[:2], y=y[:2]) for cc, ll in copies]
+        ms2r = timed(lambda i: cr2[i % len(cr2)](), args.steps // 2, args.warmup)
+        extras["km4_B2_us"] = round(ms2r * 1e3, 2)
+        extras["km4_B2_GBps"] = round(nbytes / (ms2r * 1e-3) / 1e9, 1)
+        del cr2
         calls4 = [qmv.qmatvec_call("km4", cc, ll, x8[:4], y=y[:4]) for cc, ll in copies]
         ms4 = timed(lambda i: calls4[i % len(calls4)](), args.steps // 2, args.warmup)
         extras["km4_B4_us"] = round(ms4 * 1e3, 2)

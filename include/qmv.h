@@ -174,10 +174,10 @@ size_t qtile_km4_bytes(int64_t N, int64_t K);
  * bytes; K % 32 == 0; both 16-byte aligned; the two must not overlap. */
 qmv_status qtile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *tiled, void *stream);
 
-/* y[0][n] = sum_k lut[n][code(n, k)] * x[0][k], fp32 accumulation, from the
- * tiled plane and qpack_km4's lut [N][16] (4-byte aligned). Batch 1, x fp16
- * [1][K], K in {512, 1024, 2048, 4096} (QMV_E_SHAPE otherwise, QMV_E_DTYPE
- * for fp32 x); y fp32 [1][N]. */
+/* y[b][n] = sum_k lut[n][code(n, k)] * x[b][k], fp32 accumulation, from the
+ * tiled plane and qpack_km4's lut [N][16] (4-byte aligned). 1 <= B <= 4, x fp16
+ * [B][K], K in {512, 1024, 2048, 4096} (QMV_E_SHAPE otherwise, QMV_E_DTYPE
+ * for fp32 x); y fp32 [B][N]. */
 qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K,
                              const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 

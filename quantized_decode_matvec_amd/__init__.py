@@ -390,19 +390,19 @@ def _tiled_args(fn, tiled, lut, x, y):
     _tensor(fn, "lut", lut, shape=(N, 16))
     _fp(fn, "x", x, allow_f32=False)
     x2 = x.view(1, -1) if x.dim() == 1 else x
-    if x2.dim() != 2 or x2.shape[0] != 1:
-        _bad(fn, "x must be [K] or [1, K], got shape %s" % (tuple(x.shape),))
-    K = x2.shape[1]
+    if x2.dim() != 2 or not 1 <= x2.shape[0] <= 4:
+        _bad(fn, "x must be [K] or [B, K] with 1 <= B <= 4, got shape %s" % (tuple(x.shape),))
+    B, K = x2.shape
     if K not in (512, 1024, 2048, 4096):
         _bad(fn, "K = %d: the tiled kernel takes K in 512, 1024, 2048, 4096" % K)
     _tensor(fn, "tiled", tiled, shape=(qtile_km4_bytes(N, K),), itemsize=1)
-    y = _y_out(fn, y, (1, N), torch.float32, tiled)
+    y = _y_out(fn, y, (B, N), torch.float32, tiled)
     _on_gpu(fn, tiled, lut, x2, y)
-    return (_ptr(tiled), _ptr(lut), N, K, _ptr(x2), QMV_F16, 1, _ptr(y)), (tiled, lut, x2), y
+    return (_ptr(tiled), _ptr(lut), N, K, _ptr(x2), QMV_F16, B, _ptr(y)), (tiled, lut, x2), y
 
 
 def qmatvec_km4_tiled(tiled, lut, x, y=None, stream=None):
-    """Batch-1 km4 matvec from the row-tiled plane: x fp16 [K] or [1, K] -> y fp32 [1, N]."""
+    """km4 matvec from the row-tiled plane: x fp16 [K] or [B, K], 1 <= B <= 4 -> y fp32 [B, N]."""
     fn = "qmatvec_km4_tiled"
     args, _, y = _tiled_args(fn, tiled, lut, x, y)
     _check(fn, lib().qmatvec_km4_tiled(*args, _stream(stream)))

@@ -212,9 +212,9 @@ qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t 
     qmv_status s = check_mv(tiled, lut, 4, N, K, x, xdt, B, y);
     if (s != QMV_OK) return s;
     if (xdt != QMV_F16) return QMV_E_DTYPE;
-    if (B != 1 || !qmv::km4_tiled_supported(K)) return QMV_E_SHAPE;
+    if (!qmv::km4_tiled_supported(K, B)) return QMV_E_SHAPE;
     forget_earlier_errors();
-    return launch_status(qmv::launch_matvec_km4_tiled(tiled, lut, N, K, reinterpret_cast<const _Float16 *>(x), y,
+    return launch_status(qmv::launch_matvec_km4_tiled(tiled, lut, N, K, reinterpret_cast<const _Float16 *>(x), B, y,
                                                       as_stream(stream)));
 }
 

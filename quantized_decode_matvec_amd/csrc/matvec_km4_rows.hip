@@ -1,4 +1,4 @@
-// Batch-1 k-means palettized matvec on a row-tiled code plane, one row per
+// Batch 1-4 k-means palettized matvec on a row-tiled code plane, one row per
 // lane, two codes per table lookup ("Dense-path int4km coverage + flagship
 // Qwen3.6-35B - session findings & methods", sections 1 and 8: the lm_head is
 // the largest per-token matvec and its 4-bit palettized form is read once per
@@ -10,7 +10,7 @@
 // issue. Here every byte of codes (two indices) is looked up at once in a
 // 256-entry table of fp16 pairs:
 //   pair[e] = (lut[e & 15], lut[e >> 4])   (low nibble = even element)
-// so one lookup yields the half2 operand of one v_dot2. A 1 KiB pair table per
+// so one lookup yields the half2 operand of one v_dot2 per batch row. A 1 KiB pair table per
 // row cannot be shared by the lanes of a wave without bank conflicts, so each
 // lane owns one row: a 64-row tile's tables are stored transposed, entry e of
 // row r at dword 64 e + r, and lane r only touches LDS bank r mod 32 (64 KiB
@@ -25,7 +25,8 @@
 // scalar loads, the SGPR operand of v_dot2. Wave w builds the 16 table entries
 // with low nibble in 4a..4a+3 and high nibble in 4b..4b+3 (a = w & 3,
 // b = w >> 2), which needs 16 bytes of its row's table. The 16 partial sums of
-// a row are added in wave order through LDS (deterministic).
+// a row meet in LDS and are added by a fixed DPP tree, every wave taking 4 rows
+// (deterministic; no wave is left alone at the end of a workgroup's life).
 //
 // Row-tiled code layout (tile t = rows 64 t .. 64 t + 63, Q = K / 32 chunks
 // per row): chunk q of row 64 t + r is the 16 bytes at ((t Q + q) 64 + r) 16,
@@ -55,15 +56,22 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t a) {
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + a);
 }
 
-template <int CPW, int TPW>
+// BT batch rows (x [BT][K], y [BT][N]); two workgroups per CU need at most
+// 80 KiB of LDS each: 64 KiB of pair tables + 4 KiB of partial sums per batch
+// row.
+template <int CPW, int TPW, int BT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
     float *__restrict__ y, int64_t tiles) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
+    constexpr int K = Q * 32;
     // pair tables at LDS address 0 (a static array: table addresses need no
-    // base added), then the W x 64 partial sums
-    __shared__ __align__(16) uint32_t lds[kPairEntries * kRowsTile + W * kRowsTile];
+    // base added), then the partial sums [BT][W][64]: wave w's sum for row r
+    // at [w][r ^ w ^ 16 (r & 1)], so that both the writes (one wave, 64 rows)
+    // and the reads (16 waves' sums of two rows per half-wave) fall on
+    // distinct banks
+    __shared__ __align__(16) uint32_t lds[kPairEntries * kRowsTile + BT * W * kRowsTile];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int la = (wave & 3) * 2, hb = (wave >> 2) * 2;   // table words of this wave's build share
@@ -100,7 +108,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
                 }
         }
         __syncthreads();
-        float acc0 = 0.f, acc1 = 0.f;
+        float acc[BT][2];
+#pragma unroll
+        for (int bb = 0; bb < BT; bb++) acc[bb][0] = acc[bb][1] = 0.f;
         // x is re-read per tile (scalar cache hits) rather than held in SGPRs
         // from one tile to the next, which would spill them
         const kconst_u32 *xw = (const kconst_u32 *)x;
@@ -115,19 +125,24 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
                 for (int b = 0; b < 4; b++) {
                     // byte b of code word d -> table address 256 * byte + 4 * lane
                     const uint32_t a = __builtin_amdgcn_perm(w4[d], roff, 0x0C0C0000u | ((4u + b) << 8));
-                    const uint32_t v = lds_word(lds, a);
-                    if (b & 1) acc1 = dot2(as_h2(v), as_h2(xq[4 * d + b]), acc1);
-                    else acc0 = dot2(as_h2(v), as_h2(xq[4 * d + b]), acc0);
+                    const h2 v = as_h2(lds_word(lds, a));
+#pragma unroll
+                    for (int bb = 0; bb < BT; bb++)
+                        acc[bb][b & 1] = dot2(v, as_h2(xq[bb * (K / 2) + 4 * d + b]), acc[bb][b & 1]);
                 }
         }
-        part[wave * kRowsTile + lane] = acc0 + acc1;
-        __syncthreads();
-        if (wave == 0) {
-            float s = part[lane];
 #pragma unroll
-            for (int w = 1; w < W; w++) s += part[w * kRowsTile + lane];
-            const int64_t row = t * kRowsTile + lane;
-            if (t < tiles && row < N) y[row] = s;
+        for (int bb = 0; bb < BT; bb++)
+            part[(bb * W + wave) * kRowsTile + (lane ^ wave ^ ((lane & 1) << 4))] = acc[bb][0] + acc[bb][1];
+        __syncthreads();
+        // every wave sums 4 rows: lane l takes wave (l & 15)'s sum of row
+        // 4 wave + (l >> 4), then a fixed DPP tree over each 16-lane row
+        const int rr = 4 * wave + (lane >> 4), ww = lane & 15;
+        const int64_t row = t * kRowsTile + rr;
+#pragma unroll
+        for (int bb = 0; bb < BT; bb++) {
+            const float s = row16_sum(part[(bb * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))]);
+            if (ww == 0 && t < tiles && row < N) y[(size_t)bb * N + row] = s;
         }
     };
     const int64_t t0 = (int64_t)blockIdx.x * TPW;
@@ -143,29 +158,44 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     }
 }
 
-template <int CPW, int TPW>
+template <int CPW, int TPW, int BT>
 static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, float *y,
                                hipStream_t st) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const int64_t grid = (tiles + TPW - 1) / TPW;
-    hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes, lut, N,
-                       x, y, tiles);
+    hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes, lut,
+                       N, x, y, tiles);
     return hipGetLastError();
 }
 
-bool km4_tiled_supported(int64_t K) { return K == 512 || K == 1024 || K == 2048 || K == 4096; }
+// two tiles per workgroup once there are enough workgroups to keep two on
+// every CU; fewer tiles spread one per workgroup; K = 4096 holds 32 code
+// registers per tile and takes one
+template <int BT>
+static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
+                                 float *y, bool two, hipStream_t st) {
+    switch (K) {
+    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st);
+    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st);
+    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st);
+    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool km4_tiled_supported(int64_t K, int B) {
+    return (K == 512 || K == 1024 || K == 2048 || K == 4096) && B >= 1 && B <= 4;
+}
 
 hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
-                                   const _Float16 *x, float *y, hipStream_t st) {
+                                   const _Float16 *x, int B, float *y, hipStream_t st) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
-    // two tiles per workgroup once there are enough workgroups to keep two on
-    // every CU; fewer tiles spread one per workgroup
     const bool two = tiles >= 4 * (int64_t)device_cu_count();
-    switch (K) {
-    case 512: return two ? launch_tiled<1, 2>(codes, lut, N, x, y, st) : launch_tiled<1, 1>(codes, lut, N, x, y, st);
-    case 1024: return two ? launch_tiled<2, 2>(codes, lut, N, x, y, st) : launch_tiled<2, 1>(codes, lut, N, x, y, st);
-    case 2048: return two ? launch_tiled<4, 2>(codes, lut, N, x, y, st) : launch_tiled<4, 1>(codes, lut, N, x, y, st);
-    case 4096: return launch_tiled<8, 1>(codes, lut, N, x, y, st);   // 32 code registers per tile
+    switch (B) {
+    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st);
+    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st);
+    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st);
+    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st);
     default: return hipErrorInvalidValue;
     }
 }

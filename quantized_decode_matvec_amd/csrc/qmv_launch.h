@@ -21,12 +21,12 @@ hipError_t launch_matvec(int fmt, const void *codes, const void *plane, int64_t 
 constexpr int kArgmaxHeader = 16;
 hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, int64_t N, int64_t K, const void *x,
                               int B, float *y, hipStream_t st, bool *handled, uint64_t *hdr = nullptr);
-// km4 at batch 1 on the row-tiled code plane (matvec_km4_rows.hip)
-bool km4_tiled_supported(int64_t K);
+// km4 at batch 1-4 on the row-tiled code plane (matvec_km4_rows.hip)
+bool km4_tiled_supported(int64_t K, int B);
 size_t km4_tiled_bytes(int64_t N, int64_t K);
 hipError_t launch_tile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *out, hipStream_t st);
 hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
-                                   const _Float16 *x, float *y, hipStream_t st);
+                                   const _Float16 *x, int B, float *y, hipStream_t st);
 bool argmax_supported(int fmt, int64_t K, int B);
 size_t argmax_workspace_bytes(int64_t N, int B);
 hipError_t launch_matvec_argmax(int fmt, const void *codes, const void *plane, int64_t N, int64_t K, const void *x,

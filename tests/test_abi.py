@@ -170,7 +170,8 @@ def test_tiled_km4_validation(L):
     assert L.qtile_km4(FAKE, 4, 64, ODD, S) == E_ALIGN
     assert L.qmatvec_km4_tiled(NUL, FAKE, 64, 2048, FAKE, 1, 1, FAKE, S) == E_NULL
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 0, 1, FAKE, S) == E_DTYPE   # fp32 x
-    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 2, FAKE, S) == E_SHAPE   # batch 1 only
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 5, FAKE, S) == E_SHAPE   # batch 1..4
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 0, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K not a tile width
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 8192, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4_tiled(FAKE, half, 64, 2048, FAKE, 1, 1, FAKE, S) == E_ALIGN   # 32-bit table words

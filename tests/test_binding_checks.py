@@ -152,10 +152,11 @@ def test_tiled_km4_checks():
     t, lut, x = z(128 * K // 2, dtype=u8), z(N, 16, dtype=u16), z(1, K)
     assert qmv.qtile_km4_bytes(N, K) == 128 * K // 2
     raises(ValueError, "GPU memory", qmv.qmatvec_km4_tiled, t, lut, x)            # all right but the device
+    raises(ValueError, "GPU memory", qmv.qmatvec_km4_tiled, t, lut, z(4, K))      # batch 4 is accepted too
     raises(ValueError, "tiled has shape", qmv.qmatvec_km4_tiled, z(N * K // 2, dtype=u8), lut, x)   # unpadded
     raises(ValueError, "lut has shape", qmv.qmatvec_km4_tiled, t, z(N, 15, dtype=u16), x)
     raises(TypeError, "dtype", qmv.qmatvec_km4_tiled, t, lut, z(1, K, dtype=f32))
-    raises(ValueError, r"\[K\] or \[1, K\]", qmv.qmatvec_km4_tiled, t, lut, z(2, K))
+    raises(ValueError, r"1 <= B <= 4", qmv.qmatvec_km4_tiled, t, lut, z(5, K))
     raises(ValueError, "K = 1536", qmv.qmatvec_km4_tiled, z(128 * 768, dtype=u8), lut, z(1, 1536))
     raises(ValueError, "contiguous", qmv.qmatvec_km4_tiled, t, lut, z(1, 2 * K)[:, ::2])
     raises(ValueError, "GPU memory", qmv.qtile_km4, z(N, K // 2, dtype=u8))

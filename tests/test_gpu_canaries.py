@@ -144,10 +144,11 @@ def test_tiled_km4_writes_nothing_past_its_outputs():
     for N, K in ((37, 512), (1037, 2048), (66000 + 5, 1024)):
         codes = dev(rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8))
         lut = dev((rng.standard_normal((N, 16)) * 0.02).astype(np.float16).view(np.uint16))
-        x = dev(rng.standard_normal((1, K)).astype(np.float16))
         gt = Guarded((qmv.qtile_km4_bytes(N, K),), torch.uint8)
         qmv.qtile_km4(codes, tiled=gt.t)
         assert gt.intact(), ("tile", N, K)
-        gy = Guarded((1, N), torch.float32)
-        qmv.qmatvec_km4_tiled(gt.t, lut, x, y=gy.t)
-        assert gy.intact(), ("tiled matvec", N, K)
+        for B in (1, 2, 4):
+            xb = dev(rng.standard_normal((B, K)).astype(np.float16))
+            gy = Guarded((B, N), torch.float32)
+            qmv.qmatvec_km4_tiled(gt.t, lut, xb, y=gy.t)
+            assert gy.intact(), ("tiled matvec", N, K, B)

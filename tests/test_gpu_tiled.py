@@ -8,7 +8,7 @@ Codes are random bytes (every index pair occurs) and tables random fp16 values
 k-means. Shapes: every supported K (512 .. 4096), row counts that fill no tile,
 one tile, a ragged last tile, and enough tiles for the two-tiles-per-workgroup
 launch (including an odd tile count, whose last workgroup has a second tile
-past the end)."""
+past the end); batch 1 to 4."""
 import numpy as np
 import pytest
 
@@ -30,11 +30,11 @@ def tiled_reference(codes: np.ndarray) -> np.ndarray:
     return pad.reshape(T, 64, Q, 16).transpose(0, 2, 1, 3).reshape(-1)
 
 
-def case(N, K, seed):
+def case(N, K, seed, B=1):
     rng = np.random.default_rng(seed)
     codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
     lut = (rng.standard_normal((N, 16)) * 0.02).astype(np.float16).view(np.uint16)
-    x = rng.standard_normal((1, K)).astype(np.float16)
+    x = rng.standard_normal((B, K)).astype(np.float16)
     return codes, lut, x
 
 
@@ -55,6 +55,15 @@ def test_tiled_matvec_matches_oracle(N, K):
     gt = qmv.qtile_km4(dev(codes))
     assert np.array_equal(host(gt), tiled_reference(codes))
     y = host(qmv.qmatvec_km4_tiled(gt, dev(lut), dev(x)))
+    assert rel_err(y, oracle.matvec("km4", codes, lut, x)) <= RTOL
+
+
+@pytest.mark.parametrize("B", [2, 3, 4])
+@pytest.mark.parametrize("N,K", [(100, 512), (4097, 2048), (3000, 4096), (66001, 1024), (70000, 2048)])
+def test_tiled_matvec_batches_match_oracle(N, K, B):
+    print("tiled km4 N=%d K=%d B=%d" % (N, K, B), flush=True)
+    codes, lut, x = case(N, K, seed=N + K + B, B=B)
+    y = host(qmv.qmatvec_km4_tiled(qmv.qtile_km4(dev(codes)), dev(lut), dev(x)))
     assert rel_err(y, oracle.matvec("km4", codes, lut, x)) <= RTOL
 
 
