@@ -450,6 +450,10 @@ def main():
 
         ms2 = timed(two_step, args.steps, args.warmup)
         extras["km4_argmax_fused_us"] = round(msa * 1e3, 2)
+        # the same from the row-tiled plane
+        mst = timed(lambda i: qmv.qmatvec_argmax_km4_tiled(tiled[i % len(tiled)][0], tiled[i % len(tiled)][1], x1,
+                                                           idx=aidx, val=aval, workspace=ws), args.steps, args.warmup)
+        extras["km4_tiled_argmax_fused_us"] = round(mst * 1e3, 2)
         extras["km4_matvec_then_argmax_us"] = round(ms2 * 1e3, 2)
         # batch 8: the matrix-core matvec then the argmax launch
         ws8 = torch.empty((qmv.qmatvec_argmax_workspace_bytes(N_ROWS, 8),), dtype=torch.uint8, device="cuda")

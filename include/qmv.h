@@ -311,6 +311,14 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
                           const void *x, int B, int32_t *idx, float *val,
                           void *workspace, size_t ws_bytes, void *stream);
 
+/* qmatvec_argmax for a km4 head on the row-tiled code plane (qtile_km4):
+ * the qmatvec_km4_tiled kernel writes y into the workspace, then the same
+ * argmax launch. tiled/lut/x/B/K as qmatvec_km4_tiled (1 <= B <= 4, x fp16);
+ * idx, val, workspace and the tie and NaN rules as qmatvec_argmax. */
+qmv_status qmatvec_argmax_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K,
+                                    const void *x, int B, int32_t *idx, float *val,
+                                    void *workspace, size_t ws_bytes, void *stream);
+
 /* qmatvec_argmax without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). Same arguments, results and kernels as

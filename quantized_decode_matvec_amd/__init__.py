@@ -31,7 +31,7 @@ EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qmatvec_argmax_noalloc",
            "qmatvec_argmax_noalloc_max_bytes", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read", "qtile_km4_bytes", "qtile_km4",
-           "qmatvec_km4_tiled")
+           "qmatvec_km4_tiled", "qmatvec_argmax_km4_tiled")
 
 
 class QmvError(RuntimeError):
@@ -89,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "qtile_km4_bytes": ([i64, i64], sz),
             "qtile_km4": ([P, i64, i64, P, P], ci),
             "qmatvec_km4_tiled": ([P, P, i64, i64, P, ci, ci, P, P], ci),
+            "qmatvec_argmax_km4_tiled": ([P, P, i64, i64, P, ci, P, P, P, sz, P], ci),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -383,6 +384,9 @@ def qtile_km4(codes, tiled=None, stream=None):
     return tiled
 
 
+_NO_Y = object()   # _tiled_args: the caller has no y (the fused argmax)
+
+
 def _tiled_args(fn, tiled, lut, x, y):
     torch = _torch()
     _tensor(fn, "lut", lut, itemsize=2, ndim=2)
@@ -396,6 +400,9 @@ def _tiled_args(fn, tiled, lut, x, y):
     if K not in (512, 1024, 2048, 4096):
         _bad(fn, "K = %d: the tiled kernel takes K in 512, 1024, 2048, 4096" % K)
     _tensor(fn, "tiled", tiled, shape=(qtile_km4_bytes(N, K),), itemsize=1)
+    if y is _NO_Y:
+        _on_gpu(fn, tiled, lut, x2)
+        return (_ptr(tiled), _ptr(lut), N, K, _ptr(x2), QMV_F16, B, None), (tiled, lut, x2), None
     y = _y_out(fn, y, (B, N), torch.float32, tiled)
     _on_gpu(fn, tiled, lut, x2, y)
     return (_ptr(tiled), _ptr(lut), N, K, _ptr(x2), QMV_F16, B, _ptr(y)), (tiled, lut, x2), y
@@ -634,6 +641,24 @@ def qmatvec_argmax(fmt, codes, plane, x, idx=None, val=None, workspace=None, str
     _check("qmatvec_argmax", lib().qmatvec_argmax(
         FORMATS[fmt], _ptr(codes), _ptr(plane), N, K, _ptr(x2), B, _ptr(idx), _ptr(val),
         _ptr(workspace), ws_bytes, _stream(stream)))
+    return idx, val
+
+
+def qmatvec_argmax_km4_tiled(tiled, lut, x, idx=None, val=None, workspace=None, stream=None):
+    """qmatvec_argmax for km4 from the row-tiled plane (qtile_km4): x fp16 [K] or
+    [B, K], 1 <= B <= 4 -> (idx int32 [B], val fp32 [B])."""
+    torch = _torch()
+    fn = "qmatvec_argmax_km4_tiled"
+    (pt, pl, N, K, px, _, B, _), keep, _ = _tiled_args(fn, tiled, lut, x, _NO_Y)
+    idx = _y_out(fn, idx, (B,), torch.int32, tiled, "idx")
+    val = _y_out(fn, val, (B,), torch.float32, tiled, "val")
+    if workspace is None:
+        workspace = _empty((qmatvec_argmax_workspace_bytes(N, B),), torch.uint8, tiled)
+    _tensor(fn, "workspace", workspace)
+    _on_gpu(fn, tiled, idx, val, workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(fn, lib().qmatvec_argmax_km4_tiled(pt, pl, N, K, px, B, _ptr(idx), _ptr(val), _ptr(workspace), ws_bytes,
+                                              _stream(stream)))
     return idx, val
 
 

@@ -360,6 +360,21 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
                                                    as_stream(stream)));
 }
 
+qmv_status qmatvec_argmax_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K, const void *x,
+                                    int B, int32_t *idx, float *val, void *workspace, size_t ws_bytes,
+                                    void *stream) {
+    if (!tiled || !lut || !x || !idx || !val) return QMV_E_NULL;
+    if (N < 1 || N > INT32_MAX || N > (int64_t(1) << 40) / (K > 0 ? K : 1) || !qmv::km4_tiled_supported(K, B))
+        return QMV_E_SHAPE;
+    if (!workspace || ws_bytes < qmv::argmax_workspace_bytes(N, B)) return QMV_E_WORKSPACE;
+    if (!aligned(tiled, 16) || !aligned(lut, 4) || !aligned(x, 16) || !aligned(idx, 4) || !aligned(val, 4) ||
+        !aligned(workspace, 8))
+        return QMV_E_ALIGN;
+    forget_earlier_errors();
+    return launch_status(qmv::launch_argmax_km4_tiled(tiled, lut, N, K, reinterpret_cast<const _Float16 *>(x), B,
+                                                      idx, val, workspace, as_stream(stream)));
+}
+
 qmv_status qmatvec_argmax_noalloc(qmv_format fmt, const void *codes, const void *plane, int64_t N, int64_t K,
                                   const void *x, int B, int32_t *idx, float *val, void *stream) {
     if (fmt < QMV_INT4 || fmt > QMV_INT8KM) return QMV_E_DTYPE;

@@ -808,9 +808,14 @@ static hipError_t argmax_fmt(const uint8_t *codes, const void *plane, int64_t N,
     if (err != hipSuccess) return err;
     if (!handled) return hipErrorInvalidValue;
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    return launch_argmax_rows(yw, N, B, ws, idx, val, st);
+}
+
+hipError_t launch_argmax_rows(const float *y, int64_t N, int B, uint64_t *hdr, int32_t *idx, float *val,
+                              hipStream_t st) {
     const int64_t g = (N + kArgmaxStretch - 1) / kArgmaxStretch;
     const dim3 grid((unsigned)(g < 1 ? 1 : (g > kArgmaxGroups ? kArgmaxGroups : g)), (unsigned)B);
-    hipLaunchKernelGGL(argmax_rows_kernel, grid, dim3(1024), 0, st, yw, N, B, ws, idx, val);
+    hipLaunchKernelGGL(argmax_rows_kernel, grid, dim3(1024), 0, st, y, N, B, hdr, idx, val);
     return hipGetLastError();
 }
 

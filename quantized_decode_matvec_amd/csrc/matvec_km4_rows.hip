@@ -62,7 +62,7 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t a) {
 template <int CPW, int TPW, int BT>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
-    float *__restrict__ y, int64_t tiles) {
+    float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ hdr) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
     constexpr int K = Q * 32;
@@ -145,6 +145,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
             if (ww == 0 && t < tiles && row < N) y[(size_t)bb * N + row] = s;
         }
     };
+    // fused argmax: the first workgroup zeroes the reduction header the
+    // argmax launch that follows this kernel reads
+    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
     const int64_t t0 = (int64_t)blockIdx.x * TPW;
     load(t0, 0);
     if constexpr (TPW == 1) {
@@ -160,11 +163,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 
 template <int CPW, int TPW, int BT>
 static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, float *y,
-                               hipStream_t st) {
+                               hipStream_t st, uint64_t *hdr) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const int64_t grid = (tiles + TPW - 1) / TPW;
     hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes, lut,
-                       N, x, y, tiles);
+                       N, x, y, tiles, hdr);
     return hipGetLastError();
 }
 
@@ -173,12 +176,15 @@ static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_
 // registers per tile and takes one
 template <int BT>
 static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
-                                 float *y, bool two, hipStream_t st) {
+                                 float *y, bool two, hipStream_t st, uint64_t *hdr) {
     switch (K) {
-    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st);
-    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st);
-    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st) : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st);
-    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st);
+    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st, hdr)
+                         : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, hdr);
+    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, hdr)
+                          : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, hdr);
+    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, hdr)
+                          : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, hdr);
+    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, hdr);
     default: return hipErrorInvalidValue;
     }
 }
@@ -188,16 +194,26 @@ bool km4_tiled_supported(int64_t K, int B) {
 }
 
 hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
-                                   const _Float16 *x, int B, float *y, hipStream_t st) {
+                                   const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *hdr) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const bool two = tiles >= 4 * (int64_t)device_cu_count();
     switch (B) {
-    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st);
-    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st);
-    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st);
-    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st);
+    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, hdr);
+    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, hdr);
+    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, hdr);
+    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, hdr);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_argmax_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                                   const _Float16 *x, int B, int32_t *idx, float *val, void *workspace,
+                                   hipStream_t st) {
+    uint64_t *ws = reinterpret_cast<uint64_t *>(workspace);
+    float *yw = reinterpret_cast<float *>(ws + kArgmaxHeader);
+    hipError_t err = launch_matvec_km4_tiled(codes, lut, N, K, x, B, yw, st, ws);
+    if (err != hipSuccess) return err;
+    return launch_argmax_rows(yw, N, B, ws, idx, val, st);
 }
 
 // Row-tiled copy of a canonical [N][K/2] code plane (one thread per 16-byte

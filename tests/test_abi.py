@@ -175,3 +175,14 @@ def test_tiled_km4_validation(L):
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K not a tile width
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 8192, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4_tiled(FAKE, half, 64, 2048, FAKE, 1, 1, FAKE, S) == E_ALIGN   # 32-bit table words
+
+
+def test_tiled_argmax_validation(L):
+    ws = ctypes.c_size_t(1 << 20)
+    assert L.qmatvec_argmax_km4_tiled(NUL, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_NULL
+    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
+    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 5, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
+    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ctypes.c_size_t(64), S) \
+        == E_WORKSPACE
+    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, NUL, ws, S) == E_WORKSPACE
+    assert L.qmatvec_argmax_km4_tiled(ODD, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_ALIGN

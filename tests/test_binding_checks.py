@@ -161,3 +161,11 @@ def test_tiled_km4_checks():
     raises(ValueError, "contiguous", qmv.qmatvec_km4_tiled, t, lut, z(1, 2 * K)[:, ::2])
     raises(ValueError, "GPU memory", qmv.qtile_km4, z(N, K // 2, dtype=u8))
     raises(ValueError, "tiled has shape", qmv.qtile_km4, z(N, K // 2, dtype=u8), tiled=z(N * K // 2, dtype=u8))
+
+
+def test_tiled_argmax_checks():
+    N, K = 100, 2048
+    t, lut = z(128 * K // 2, dtype=u8), z(N, 16, dtype=u16)
+    raises(ValueError, "GPU memory", qmv.qmatvec_argmax_km4_tiled, t, lut, z(1, K))
+    raises(ValueError, "1 <= B <= 4", qmv.qmatvec_argmax_km4_tiled, t, lut, z(6, K))
+    raises(ValueError, "tiled has shape", qmv.qmatvec_argmax_km4_tiled, z(N * K // 2, dtype=u8), lut, z(1, K))

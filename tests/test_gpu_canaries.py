@@ -152,3 +152,7 @@ def test_tiled_km4_writes_nothing_past_its_outputs():
             gy = Guarded((B, N), torch.float32)
             qmv.qmatvec_km4_tiled(gt.t, lut, xb, y=gy.t)
             assert gy.intact(), ("tiled matvec", N, K, B)
+            gi, gv = Guarded((B,), torch.int32), Guarded((B,), torch.float32)
+            gw = Guarded((qmv.qmatvec_argmax_workspace_bytes(N, B),), torch.uint8)
+            qmv.qmatvec_argmax_km4_tiled(gt.t, lut, xb, idx=gi.t, val=gv.t, workspace=gw.t)
+            assert gi.intact() and gv.intact() and gw.intact(), ("tiled argmax", N, K, B)

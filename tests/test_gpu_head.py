@@ -163,3 +163,32 @@ def test_embed_gather_large_table():
     ids[0], ids[1] = 0, V - 1
     out = qmv.qembed_gather_int8(dev(q), dev(s), dev(ids))
     assert np.array_equal(host(out).view(np.uint16), oracle.embed_gather_int8(q, s, ids))
+
+
+@pytest.mark.parametrize("N,K,Bs", [(3000, 2048, (1, 2, 4)), (70000, 2048, (1, 3)), (517, 1024, (1,)),
+                                    (1, 512, (1, 2))])
+def test_argmax_km4_tiled_parity(N, K, Bs):
+    """The fused argmax from the row-tiled plane: same winner and value as the
+    argmax of qmatvec_km4_tiled's y, within tolerance of the oracle maximum,
+    planted winners exact, identical winners to the lowest row."""
+    print("argmax km4 tiled", N, K, Bs, flush=True)
+    c = wl.small_dense("km4", N, K, batch=4, seed=N + K + 1)
+    W = c.W.copy()
+    x = c.x
+    if N >= 40:
+        W[N // 3] = (np.sign(x[0]) * 0.06).astype(W.dtype)
+        W[N - 7] = W[11] = (np.sign(x[1]) * 0.06).astype(W.dtype)
+    codes, lut = oracle.pack("km4", W)
+    dt, dl = qmv.qtile_km4(dev(codes)), dev(lut)
+    for B in Bs:
+        ref = oracle.matvec("km4", codes, lut, x[:B])
+        idx, val = qmv.qmatvec_argmax_km4_tiled(dt, dl, dev(x[:B]))
+        idx, val = host(idx), host(val)
+        _check_argmax(idx, val, ref)
+        if N >= 40:
+            assert idx[0] == N // 3
+            if B > 1:
+                assert idx[1] == 11
+        y = host(qmv.qmatvec_km4_tiled(dt, dl, dev(x[:B])))
+        assert np.array_equal(idx, np.argmax(y, axis=1))
+        assert np.array_equal(val, y[np.arange(B), idx])
