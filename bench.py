@@ -430,6 +430,12 @@ def main():
         mso = timed(lambda i: qmv.qmatvec_km4o(*pks[i % len(pks)], x1, y=y[:1]), args.steps, args.warmup)
         extras["km4o16_B1_us"] = round(mso * 1e3, 2)
         extras["km4o16_B1_GBps"] = round(nbo / (mso * 1e-3) / 1e9, 1)
+        # the same from the row-tiled codes
+        pkt = [(qmv.qtile_km4(p[0]),) + tuple(p[1:]) for p in pks]
+        msot = timed(lambda i: qmv.qmatvec_km4o_tiled(*pkt[i % len(pkt)], x1, y=y[:1]), args.steps, args.warmup)
+        extras["km4o16_tiled_B1_us"] = round(msot * 1e3, 2)
+        extras["km4o16_tiled_B1_GBps"] = round(nbo / (msot * 1e-3) / 1e9, 1)
+        del pkt
         del pks, pko
         # fp16 dense GEMV on the same shape (torch), for the per-op ratio against fp16
         wcp = [W] + [W.clone() for _ in range(1)]

@@ -212,6 +212,13 @@ qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_
                         const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
                         const void *x, qmv_dtype xdt, int B, float *y, void *stream);
 
+/* qmatvec_km4o from the row-tiled code plane (qtile_km4 of qpack_km4o's
+ * codes): the tables and outlier arrays as qmatvec_km4o, x fp16 [B][K],
+ * 1 <= B <= 4, K in {512, 1024, 2048, 4096}, 0 <= nout <= 256. */
+qmv_status qmatvec_km4o_tiled(const uint8_t *tiled, const uint16_t *lut, const uint16_t *ocol,
+                              const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
+                              const void *x, qmv_dtype xdt, int B, float *y, void *stream);
+
 /* Reconstruct W_hat [N][K] fp32 from codes and plane (every reconstructed
  * weight is exact in fp32, except affine int4, where s * u + b is rounded
  * once to the nearest fp32) [S3 "Theoretical size" for the plane shapes].

@@ -31,7 +31,7 @@ EXPORTS = ("qmv_status_string", "qpack_int4", "qpack_fp4", "qpack_int8", "qpack_
            "qmatvec_argmax_workspace_bytes", "qmatvec_argmax", "qmatvec_argmax_noalloc",
            "qmatvec_argmax_noalloc_max_bytes", "qpack_int8_rows", "qembed_gather_int8",
            "qmv_stream_read_sink_words", "qmv_stream_read", "qtile_km4_bytes", "qtile_km4",
-           "qmatvec_km4_tiled", "qmatvec_argmax_km4_tiled")
+           "qmatvec_km4_tiled", "qmatvec_argmax_km4_tiled", "qmatvec_km4o_tiled")
 
 
 class QmvError(RuntimeError):
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "qtile_km4": ([P, i64, i64, P, P], ci),
             "qmatvec_km4_tiled": ([P, P, i64, i64, P, ci, ci, P, P], ci),
             "qmatvec_argmax_km4_tiled": ([P, P, i64, i64, P, ci, P, P, P, sz, P], ci),
+            "qmatvec_km4o_tiled": ([P, P, P, P, P, i64, i64, ci, P, ci, ci, P, P], ci),
         }
         for name, (args, res) in sigs.items():
             f = getattr(L, name)
@@ -477,6 +478,22 @@ def qmatvec_km4o(codes, lut, ocol, oval, oscale, x, y=None, stream=None):
     _on_gpu(fn, codes, lut, ocol, oval, oscale, x2, y)
     _check("qmatvec_km4o", lib().qmatvec_km4o(_ptr(codes), _ptr(lut), _ptr(ocol), _ptr(oval), _ptr(oscale), N, K,
                                               int(nout), _ptr(x2), _dt(x2), B, _ptr(y), _stream(stream)))
+    return y
+
+
+def qmatvec_km4o_tiled(tiled, lut, ocol, oval, oscale, x, y=None, stream=None):
+    """qmatvec_km4o from the row-tiled plane (qtile_km4 of qpack_km4o's codes):
+    x fp16 [K] or [B, K], 1 <= B <= 4 -> y fp32 [B, N]."""
+    fn = "qmatvec_km4o_tiled"
+    (pt, pl, N, K, px, dt, B, py), _, y = _tiled_args(fn, tiled, lut, x, y)
+    _tensor(fn, "ocol", ocol, itemsize=2, ndim=2)
+    nout = ocol.shape[1]
+    _tensor(fn, "ocol", ocol, shape=(N, nout))
+    _tensor(fn, "oval", oval, shape=(N, nout), itemsize=1)
+    _tensor(fn, "oscale", oscale, shape=(N,), itemsize=2)
+    _on_gpu(fn, tiled, ocol, oval, oscale)
+    _check(fn, lib().qmatvec_km4o_tiled(pt, pl, _ptr(ocol), _ptr(oval), _ptr(oscale), N, K, int(nout), px, dt, B, py,
+                                        _stream(stream)))
     return y
 
 

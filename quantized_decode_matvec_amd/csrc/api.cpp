@@ -218,6 +218,22 @@ qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t 
                                                       as_stream(stream)));
 }
 
+qmv_status qmatvec_km4o_tiled(const uint8_t *tiled, const uint16_t *lut, const uint16_t *ocol, const int8_t *oval,
+                              const uint16_t *oscale, int64_t N, int64_t K, int nout, const void *x, qmv_dtype xdt,
+                              int B, float *y, void *stream) {
+    qmv_status s = check_mv(tiled, lut, 4, N, K, x, xdt, B, y);
+    if (s != QMV_OK) return s;
+    if (!oscale || (nout > 0 && (!ocol || !oval))) return QMV_E_NULL;
+    if (xdt != QMV_F16) return QMV_E_DTYPE;
+    if (!qmv::km4_tiled_supported(K, B) || nout < 0 || nout > 256 || nout > K) return QMV_E_SHAPE;
+    if (!aligned(ocol, 2) || !aligned(oscale, 2)) return QMV_E_ALIGN;
+    forget_earlier_errors();
+    const _Float16 *xh = reinterpret_cast<const _Float16 *>(x);
+    if (nout == 0) return launch_status(qmv::launch_matvec_km4_tiled(tiled, lut, N, K, xh, B, y, as_stream(stream)));
+    return launch_status(
+        qmv::launch_matvec_km4o_tiled(tiled, lut, ocol, oval, oscale, N, K, nout, xh, B, y, as_stream(stream)));
+}
+
 qmv_status qmatvec_int4aff(const uint8_t *codes, const uint32_t *plane, int64_t N, int64_t K, const void *x,
                            qmv_dtype xdt, int B, float *y, void *stream) {
     qmv_status s = check_mv(codes, plane, 4, N, K, x, xdt, B, y);

@@ -56,13 +56,25 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t a) {
     return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const char *>(base) + a);
 }
 
+// int8 outliers added to the rows (the 4-bit k-means + int8 outlier format):
+// per row, n columns (increasing), int8 values and one fp16 scale; the row's
+// weight at an outlier column is the table value plus scale * q.
+struct TiledOutliers {
+    const uint16_t *col = nullptr;   // [N][n]
+    const int8_t *val = nullptr;     // [N][n]
+    const uint16_t *scale = nullptr; // [N]
+    int n = 0;
+};
+
 // BT batch rows (x [BT][K], y [BT][N]); two workgroups per CU need at most
 // 80 KiB of LDS each: 64 KiB of pair tables + 4 KiB of partial sums per batch
-// row.
-template <int CPW, int TPW, int BT>
+// row. OUTL: add the int8 outliers; the 16 lanes that sum a row's partial
+// sums take its outliers ww, ww + 16, ... (the first one's column, value and
+// scale loaded with the codes, its x gathered after the table build).
+template <int CPW, int TPW, int BT, bool OUTL = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
-    float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ hdr) {
+    float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ hdr, TiledOutliers ol) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
     constexpr int K = Q * 32;
@@ -80,6 +92,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 
     uint4 cw[TPW > 1 ? 2 : 1][CPW];
     uint2 lo[TPW > 1 ? 2 : 1], hi[TPW > 1 ? 2 : 1];
+    // outliers: this lane sums row 4 wave + (lane >> 4) and takes its outlier
+    // lane & 15 (column, value, row scale), prefetched per tile
+    const int orr = 4 * wave + (lane >> 4), oww = lane & 15;
+    uint32_t ocol_r[OUTL ? (TPW > 1 ? 2 : 1) : 1], oval_r[OUTL ? (TPW > 1 ? 2 : 1) : 1],
+        osc_r[OUTL ? (TPW > 1 ? 2 : 1) : 1];
     // loads of tile t into buffer k; a tile past the end reads tile 0 again
     // (read by the first workgroups: a cache hit, no HBM traffic)
     auto load = [&](int64_t t, int k) {
@@ -91,6 +108,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         const uint8_t *tb = codes + ((size_t)tt * Q + CPW * wave) * (kRowsTile * 16) + lane * 16;
 #pragma unroll
         for (int j = 0; j < CPW; j++) cw[k][j] = load_stream16(tb + j * (kRowsTile * 16));
+        if constexpr (OUTL) {
+            const int64_t orow = tt * kRowsTile + orr;
+            const int64_t rc = orow < N ? orow : N - 1;
+            const int o = oww < ol.n ? oww : 0;   // a lane without an outlier reads outlier 0 and drops it
+            ocol_r[k] = ol.n > 0 ? ol.col[rc * ol.n + o] : 0u;
+            oval_r[k] = ol.n > 0 ? (uint32_t)(int32_t)ol.val[rc * ol.n + o] : 0u;
+            osc_r[k] = ol.scale[rc];
+        }
     };
     auto step = [&](int64_t t, int k) {
         {
@@ -108,6 +133,15 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
                 }
         }
         __syncthreads();
+        // outliers: x at this lane's outlier column, gathered now that the
+        // column has arrived (with the table words)
+        float oterm[BT];
+        if constexpr (OUTL) {
+            const float sc = f16_bits_to_f32((uint16_t)osc_r[k]);
+            const float tq = oww < ol.n ? (float)(int32_t)oval_r[k] * sc : 0.f;   // exact: 8 x 11 bits
+#pragma unroll
+            for (int bb = 0; bb < BT; bb++) oterm[bb] = tq * (float)x[(size_t)bb * K + ocol_r[k]];
+        }
         float acc[BT][2];
 #pragma unroll
         for (int bb = 0; bb < BT; bb++) acc[bb][0] = acc[bb][1] = 0.f;
@@ -139,9 +173,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         // 4 wave + (l >> 4), then a fixed DPP tree over each 16-lane row
         const int rr = 4 * wave + (lane >> 4), ww = lane & 15;
         const int64_t row = t * kRowsTile + rr;
+        if constexpr (OUTL) {
+            // outliers past the first 16 of a row (the prefetched one is ww)
+            const int64_t rc = row < N ? row : N - 1;
+            const float sc = f16_bits_to_f32(ol.scale[rc]);
+            for (int o = ww + 16; o < ol.n; o += 16) {
+                const float tq = (float)ol.val[rc * ol.n + o] * sc;
+                const int col = ol.col[rc * ol.n + o];
+#pragma unroll
+                for (int bb = 0; bb < BT; bb++) oterm[bb] = __builtin_fmaf(tq, (float)x[(size_t)bb * K + col], oterm[bb]);
+            }
+        }
 #pragma unroll
         for (int bb = 0; bb < BT; bb++) {
-            const float s = row16_sum(part[(bb * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))]);
+            float pv = part[(bb * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))];
+            if constexpr (OUTL) pv += oterm[bb];
+            const float s = row16_sum(pv);
             if (ww == 0 && t < tiles && row < N) y[(size_t)bb * N + row] = s;
         }
     };
@@ -287,11 +334,15 @@ hipError_t launch_km4_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int6
 
 template <int CPW, int TPW, int BT>
 static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, float *y,
-                               hipStream_t st, uint64_t *hdr) {
+                               hipStream_t st, uint64_t *hdr, const TiledOutliers *ol = nullptr) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const int64_t grid = (tiles + TPW - 1) / TPW;
-    hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes, lut,
-                       N, x, y, tiles, hdr);
+    if (ol != nullptr)
+        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT, true>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st,
+                           codes, lut, N, x, y, tiles, hdr, *ol);
+    else
+        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes,
+                           lut, N, x, y, tiles, hdr, TiledOutliers());
     return hipGetLastError();
 }
 
@@ -300,15 +351,15 @@ static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_
 // registers per tile and takes one
 template <int BT>
 static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
-                                 float *y, bool two, hipStream_t st, uint64_t *hdr) {
+                                 float *y, bool two, hipStream_t st, uint64_t *hdr, const TiledOutliers *ol) {
     switch (K) {
-    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st, hdr)
-                         : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, hdr);
-    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, hdr)
-                          : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, hdr);
-    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, hdr)
-                          : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, hdr);
-    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, hdr);
+    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
+                         : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
+    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
+                          : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
+    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
+                          : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
+    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
     default: return hipErrorInvalidValue;
     }
 }
@@ -325,10 +376,29 @@ hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, in
     // 248320 x 2048: 51 us against 61-70 us for B v_dot2 per lookup)
     if (B >= 3 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, hdr);
     switch (B) {
-    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, hdr);
-    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, hdr);
-    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, hdr);
-    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, hdr);
+    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
+    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
+    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
+    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
+                                    const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
+                                    const _Float16 *x, int B, float *y, hipStream_t st) {
+    TiledOutliers ol;
+    ol.col = ocol;
+    ol.val = oval;
+    ol.scale = oscale;
+    ol.n = nout;
+    const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
+    const bool two = tiles >= 4 * (int64_t)device_cu_count();
+    switch (B) {
+    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
+    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
+    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
+    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
     default: return hipErrorInvalidValue;
     }
 }

@@ -29,6 +29,10 @@ hipError_t launch_tile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *
 // argmax launch that follows reduces y into them)
 hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                                    const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *hdr = nullptr);
+// the same with the int8 outliers of the km4 + outlier format (nout >= 1)
+hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
+                                    const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
+                                    const _Float16 *x, int B, float *y, hipStream_t st);
 // the argmax of each batch row of y [B][N] into idx/val, reduced through the
 // zeroed header hdr (matvec.hip)
 hipError_t launch_argmax_rows(const float *y, int64_t N, int B, uint64_t *hdr, int32_t *idx, float *val,

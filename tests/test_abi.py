@@ -186,3 +186,13 @@ def test_tiled_argmax_validation(L):
         == E_WORKSPACE
     assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, NUL, ws, S) == E_WORKSPACE
     assert L.qmatvec_argmax_km4_tiled(ODD, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_ALIGN
+
+
+def test_tiled_km4o_validation(L):
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, NUL, 64, 2048, 4, FAKE, 1, 1, FAKE, S) == E_NULL
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, NUL, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 1, FAKE, S) == E_NULL
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 4, FAKE, 0, 1, FAKE, S) == E_DTYPE
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 300, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1536, 4, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 5, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, ODD, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 1, FAKE, S) == E_ALIGN

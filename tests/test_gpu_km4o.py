@@ -90,3 +90,18 @@ def test_gpu_pack_then_gpu_matvec_end_to_end():
     y = host(qmv.qmatvec_km4o(*packed, dev(x[:2])))
     want = oracle.matvec_km4o(*oracle.pack_km4o(W, 16), x[:2])
     assert rel_err(y, want) <= RTOL
+
+
+@pytest.mark.parametrize("N,K,nout,B", [(1037, 2048, 16, 1), (1037, 2048, 16, 2), (3000, 1024, 5, 4),
+                                        (700, 512, 40, 1), (66001, 2048, 16, 1), (100, 4096, 0, 3),
+                                        (257, 2048, 1, 2)])
+def test_km4o_tiled_matches_oracle(N, K, nout, B):
+    """The outlier format from the row-tiled codes: the 16 lanes that sum a
+    row take its outliers (one each, more past 16)."""
+    print("km4o tiled", N, K, nout, B, flush=True)
+    c = wl.small_dense("km4", N, K, batch=4, seed=N + nout)
+    packed = oracle.pack_km4o(c.W, nout, max_iter=4)
+    want = oracle.matvec_km4o(*packed, c.x[:B])
+    codes, lut, ocol, oval, oscale = (dev(a) for a in packed)
+    y = host(qmv.qmatvec_km4o_tiled(qmv.qtile_km4(codes), lut, ocol, oval, oscale, dev(c.x[:B])))
+    assert rel_err(y, want) <= RTOL
