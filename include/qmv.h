@@ -319,9 +319,12 @@ qmv_status qmatvec_argmax(qmv_format fmt, const void *codes, const void *plane, 
                           void *workspace, size_t ws_bytes, void *stream);
 
 /* qmatvec_argmax for a km4 head on the row-tiled code plane (qtile_km4):
- * the qmatvec_km4_tiled kernel writes y into the workspace, then the same
- * argmax launch. tiled/lut/x/B/K as qmatvec_km4_tiled (1 <= B <= 4, x fp16);
- * idx, val, workspace and the tie and NaN rules as qmatvec_argmax. */
+ * the qmatvec_km4_tiled kernels write no logits; each workgroup stores the
+ * largest (value, lowest row) key of its rows per batch row into the
+ * workspace (8 * B * ceil(N / 64) bytes at most), and one small launch takes
+ * the largest key. tiled/lut/x/B/K as qmatvec_km4_tiled (1 <= B <= 4, x
+ * fp16); idx, val, the workspace size and alignment, and the tie and NaN
+ * rules as qmatvec_argmax. */
 qmv_status qmatvec_argmax_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K,
                                     const void *x, int B, int32_t *idx, float *val,
                                     void *workspace, size_t ws_bytes, void *stream);

@@ -27,26 +27,7 @@ namespace qmv {
 // stretch of the code plane. The x slices are loaded once per wave, so ITERS
 // grows with the batch width to amortize them.
 // ---------------------------------------------------------------------------
-// Argmax keys: the fp32 value in order-preserving form above the complement
-// of the row index, so the largest key is the largest value and, among equal
-// values, the lowest row. Every finite value gives a key above 0.
 // argmax workspace: the kArgmaxHeader-word header, then y [B][N] fp32
-
-__device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
-    uint32_t b = __builtin_bit_cast(uint32_t, v);
-    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)k, m), hi = __shfl_xor((uint32_t)(k >> 32), m);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        k = o > k ? o : k;
-    }
-    return k;
-}
 
 // int8 outliers added to 4-bit k-means rows ("Kernel campaign - session
 // handoff", NEXT per lever, Stream D): per row, n columns (increasing), int8
@@ -446,10 +427,8 @@ __global__ __launch_bounds__(1024) void argmax_rows_kernel(const float *__restri
         const uint64_t done = __hip_atomic_fetch_add(&hdr[8 + b], (uint64_t)1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
         if (done + 1 == (uint64_t)G) {
             const uint64_t kk = __hip_atomic_load(&hdr[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t hi = (uint32_t)(kk >> 32);
-            const uint32_t bits = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
-            idx[b] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk);
-            val[b] = __builtin_bit_cast(float, bits);
+            idx[b] = argmax_key_row(kk);
+            val[b] = argmax_key_value(kk);
         }
     }
 }

@@ -71,10 +71,12 @@ struct TiledOutliers {
 // row. OUTL: add the int8 outliers; the 16 lanes that sum a row's partial
 // sums take its outliers ww, ww + 16, ... (the first one's column, value and
 // scale loaded with the codes, its x gathered after the table build).
-template <int CPW, int TPW, int BT, bool OUTL = false>
+// KEYS (greedy decoding): no y; the workgroup writes the largest argmax key
+// of its rows per batch row, keys[b][blockIdx.x], for argmax_keys_kernel.
+template <int CPW, int TPW, int BT, bool OUTL = false, bool KEYS = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
-    float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ hdr, TiledOutliers ol) {
+    float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ keys, TiledOutliers ol) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
     constexpr int K = Q * 32;
@@ -89,6 +91,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     const int la = (wave & 3) * 2, hb = (wave >> 2) * 2;   // table words of this wave's build share
     const uint32_t roff = (uint32_t)lane * 4u;
     float *part = reinterpret_cast<float *>(lds + kPairEntries * kRowsTile);
+    uint64_t kmax[BT];   // KEYS: this lane's largest key per batch row
+#pragma unroll
+    for (int bb = 0; bb < BT; bb++) kmax[bb] = 0;
 
     uint4 cw[TPW > 1 ? 2 : 1][CPW];
     uint2 lo[TPW > 1 ? 2 : 1], hi[TPW > 1 ? 2 : 1];
@@ -189,12 +194,16 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
             float pv = part[(bb * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))];
             if constexpr (OUTL) pv += oterm[bb];
             const float s = row16_sum(pv);
-            if (ww == 0 && t < tiles && row < N) y[(size_t)bb * N + row] = s;
+            if (ww == 0 && t < tiles && row < N) {
+                if constexpr (KEYS) {
+                    const uint64_t kk = argmax_key(s, row);
+                    kmax[bb] = kk > kmax[bb] ? kk : kmax[bb];
+                } else {
+                    y[(size_t)bb * N + row] = s;
+                }
+            }
         }
     };
-    // fused argmax: the first workgroup zeroes the reduction header the
-    // argmax launch that follows this kernel reads
-    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
     const int64_t t0 = (int64_t)blockIdx.x * TPW;
     load(t0, 0);
     if constexpr (TPW == 1) {
@@ -205,6 +214,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         load(t0 + 1, 1);
         step(t0, 0);
         step(t0 + 1, 1);
+    }
+    if constexpr (KEYS) {
+        // one key per wave and batch row, in the table region: the last
+        // tile's lookups are done (barrier before its partial sums were read)
+        uint64_t *kl = reinterpret_cast<uint64_t *>(lds);
+#pragma unroll
+        for (int bb = 0; bb < BT; bb++) {
+            const uint64_t k = wave_max_u64(kmax[bb]);
+            if (lane == 0) kl[bb * W + wave] = k;
+        }
+        __syncthreads();
+        if (threadIdx.x < BT) {
+            uint64_t k = 0;
+            for (int w = 0; w < W; w++) k = kl[threadIdx.x * W + w] > k ? kl[threadIdx.x * W + w] : k;
+            keys[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = k;
+        }
     }
 }
 
@@ -221,10 +246,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 // read serves fall on distinct banks); 64 KiB + K / 2 KiB <= 80 KiB keeps two
 // workgroups per CU, so K <= 2048, and the partial sums [4][W][64] go to the
 // table region once a tile's lookups are done (two more barriers per tile).
-template <int CPW>
+// KEYS: as in mv_km4_tiled (the wave keys go to the x stage, free by then).
+template <int CPW, bool KEYS = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled_mfma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
-    int B, float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ hdr) {
+    int B, float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ keys) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
     constexpr int K = Q * 32;
@@ -239,7 +265,6 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     const uint32_t roff = (uint32_t)lane * 4u;
     float *part = reinterpret_cast<float *>(lds);
     uint4 *xs = reinterpret_cast<uint4 *>(lds + kPairEntries * kRowsTile);
-    if (hdr != nullptr && blockIdx.x == 0 && threadIdx.x < kArgmaxHeader) hdr[threadIdx.x] = 0;
 
     const int64_t t = blockIdx.x;
     // loads: table words first, then the codes, then this thread's x units
@@ -306,43 +331,74 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     __syncthreads();
     const int rr = 4 * wave + (lane >> 4), ww = lane & 15;
     const int64_t orow = t * kRowsTile + rr;
+    uint64_t km[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         const float sum = row16_sum(part[(b * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))]);
-        if (ww == 0 && b < B && orow < N) y[(size_t)b * N + orow] = sum;
+        km[b] = 0;
+        if (ww == 0 && b < B && orow < N) {
+            if constexpr (KEYS) km[b] = argmax_key(sum, orow);
+            else y[(size_t)b * N + orow] = sum;
+        }
+    }
+    if constexpr (KEYS) {
+        uint64_t *kl = reinterpret_cast<uint64_t *>(xs);   // x is no longer read
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const uint64_t k = wave_max_u64(km[b]);
+            if (lane == 0) kl[b * W + wave] = k;
+        }
+        __syncthreads();
+        if (threadIdx.x < B) {
+            uint64_t k = 0;
+            for (int w = 0; w < W; w++) k = kl[threadIdx.x * W + w] > k ? kl[threadIdx.x * W + w] : k;
+            keys[(size_t)threadIdx.x * gridDim.x + blockIdx.x] = k;
+        }
     }
 }
 
+// The launchers below take `keys` (null: write y) and return the grid size
+// (the number of keys per batch row) in *grid when grid is not null.
 template <int CPW>
 static hipError_t launch_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, int B,
-                                    float *y, hipStream_t st, uint64_t *hdr) {
+                                    float *y, hipStream_t st, uint64_t *keys, int64_t *grid) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
-    hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW>), dim3((unsigned)tiles), dim3(64 * kTileWaves), 0, st, codes, lut, N,
-                       x, B, y, tiles, hdr);
+    if (grid != nullptr) *grid = tiles;
+    if (keys != nullptr)
+        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW, true>), dim3((unsigned)tiles), dim3(64 * kTileWaves), 0, st, codes,
+                           lut, N, x, B, y, tiles, keys);
+    else
+        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW>), dim3((unsigned)tiles), dim3(64 * kTileWaves), 0, st, codes, lut,
+                           N, x, B, y, tiles, nullptr);
     return hipGetLastError();
 }
 
-hipError_t launch_km4_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
-                                 int B, float *y, hipStream_t st, uint64_t *hdr) {
+static hipError_t launch_km4_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                                        const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *keys,
+                                        int64_t *grid) {
     switch (K) {
-    case 512: return launch_tiled_mfma<1>(codes, lut, N, x, B, y, st, hdr);
-    case 1024: return launch_tiled_mfma<2>(codes, lut, N, x, B, y, st, hdr);
-    case 2048: return launch_tiled_mfma<4>(codes, lut, N, x, B, y, st, hdr);
+    case 512: return launch_tiled_mfma<1>(codes, lut, N, x, B, y, st, keys, grid);
+    case 1024: return launch_tiled_mfma<2>(codes, lut, N, x, B, y, st, keys, grid);
+    case 2048: return launch_tiled_mfma<4>(codes, lut, N, x, B, y, st, keys, grid);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <int CPW, int TPW, int BT>
 static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, float *y,
-                               hipStream_t st, uint64_t *hdr, const TiledOutliers *ol = nullptr) {
+                               hipStream_t st, uint64_t *keys, int64_t *gridp, const TiledOutliers *ol) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const int64_t grid = (tiles + TPW - 1) / TPW;
+    if (gridp != nullptr) *gridp = grid;
+    const dim3 g((unsigned)grid), blk(64 * kTileWaves);
     if (ol != nullptr)
-        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT, true>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st,
-                           codes, lut, N, x, y, tiles, hdr, *ol);
+        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT, true>), g, blk, 0, st, codes, lut, N, x, y, tiles, nullptr, *ol);
+    else if (keys != nullptr)
+        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT, false, true>), g, blk, 0, st, codes, lut, N, x, y, tiles, keys,
+                           TiledOutliers());
     else
-        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), dim3((unsigned)grid), dim3(64 * kTileWaves), 0, st, codes,
-                           lut, N, x, y, tiles, hdr, TiledOutliers());
+        hipLaunchKernelGGL((mv_km4_tiled<CPW, TPW, BT>), g, blk, 0, st, codes, lut, N, x, y, tiles, nullptr,
+                           TiledOutliers());
     return hipGetLastError();
 }
 
@@ -351,15 +407,16 @@ static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_
 // registers per tile and takes one
 template <int BT>
 static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
-                                 float *y, bool two, hipStream_t st, uint64_t *hdr, const TiledOutliers *ol) {
+                                 float *y, bool two, hipStream_t st, uint64_t *keys, int64_t *grid,
+                                 const TiledOutliers *ol) {
     switch (K) {
-    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
-                         : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
-    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
-                          : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
-    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, hdr, ol)
-                          : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
-    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, hdr, ol);
+    case 512: return two ? launch_tiled<1, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
+                         : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
+                          : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
+                          : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
     default: return hipErrorInvalidValue;
     }
 }
@@ -368,20 +425,26 @@ bool km4_tiled_supported(int64_t K, int B) {
     return (K == 512 || K == 1024 || K == 2048 || K == 4096) && B >= 1 && B <= 4;
 }
 
-hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
-                                   const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *hdr) {
+static hipError_t launch_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                                   const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *keys,
+                                   int64_t *grid, const TiledOutliers *ol) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const bool two = tiles >= 4 * (int64_t)device_cu_count();
     // batch 3-4: products on the matrix cores (the x stage fits up to K = 2048;
     // 248320 x 2048: 51 us against 61-70 us for B v_dot2 per lookup)
-    if (B >= 3 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, hdr);
+    if (ol == nullptr && B >= 3 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, keys, grid);
     switch (B) {
-    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
-    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
-    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
-    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, hdr, nullptr);
+    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
+    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
+    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
+    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
+                                   const _Float16 *x, int B, float *y, hipStream_t st) {
+    return launch_km4_tiled(codes, lut, N, K, x, B, y, st, nullptr, nullptr, nullptr);
 }
 
 hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
@@ -392,25 +455,48 @@ hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, c
     ol.val = oval;
     ol.scale = oscale;
     ol.n = nout;
-    const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
-    const bool two = tiles >= 4 * (int64_t)device_cu_count();
-    switch (B) {
-    case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
-    case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
-    case 3: return launch_tiled_b<3>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
-    case 4: return launch_tiled_b<4>(codes, lut, N, K, x, y, two, st, nullptr, &ol);
-    default: return hipErrorInvalidValue;
+    return launch_km4_tiled(codes, lut, N, K, x, B, y, st, nullptr, nullptr, &ol);
+}
+
+// The greedy token from the workgroup keys: one workgroup per batch row takes
+// the largest of its G keys (order-independent, so the result does not depend
+// on which workgroup finished first).
+__global__ __launch_bounds__(1024) void argmax_keys_kernel(const uint64_t *__restrict__ keys, int G,
+                                                           int32_t *__restrict__ idx, float *__restrict__ val) {
+    const int b = blockIdx.x;
+    const uint64_t *kb = keys + (size_t)b * G;
+    uint64_t k = 0;
+    for (int i0 = threadIdx.x; i0 < G; i0 += 4 * 1024) {
+        uint64_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = i0 + 1024 * u < G ? kb[i0 + 1024 * u] : 0;
+#pragma unroll
+        for (int u = 0; u < 4; u++) k = v[u] > k ? v[u] : k;
     }
+    k = wave_max_u64(k);
+    __shared__ uint64_t red[16];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = k;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 0; w < 16; w++) k = red[w] > k ? red[w] : k;
+        idx[b] = argmax_key_row(k);
+        val[b] = argmax_key_value(k);
+    }
+}
+
+size_t km4_tiled_argmax_keys_bytes(int64_t N, int B) {
+    return (size_t)B * (size_t)((N + kRowsTile - 1) / kRowsTile) * sizeof(uint64_t);
 }
 
 hipError_t launch_argmax_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                                    const _Float16 *x, int B, int32_t *idx, float *val, void *workspace,
                                    hipStream_t st) {
-    uint64_t *ws = reinterpret_cast<uint64_t *>(workspace);
-    float *yw = reinterpret_cast<float *>(ws + kArgmaxHeader);
-    hipError_t err = launch_matvec_km4_tiled(codes, lut, N, K, x, B, yw, st, ws);
+    uint64_t *keys = reinterpret_cast<uint64_t *>(workspace);
+    int64_t grid = 0;
+    hipError_t err = launch_km4_tiled(codes, lut, N, K, x, B, nullptr, st, keys, &grid, nullptr);
     if (err != hipSuccess) return err;
-    return launch_argmax_rows(yw, N, B, ws, idx, val, st);
+    hipLaunchKernelGGL(argmax_keys_kernel, dim3((unsigned)B), dim3(1024), 0, st, keys, (int)grid, idx, val);
+    return hipGetLastError();
 }
 
 // Row-tiled copy of a canonical [N][K/2] code plane (one thread per 16-byte

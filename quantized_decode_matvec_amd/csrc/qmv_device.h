@@ -302,6 +302,34 @@ __device__ __forceinline__ float dpp_mov(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
+// Argmax keys: the fp32 value in order-preserving form above the complement
+// of the row index, so the largest key is the largest value and, among equal
+// values, the lowest row. Every finite value gives a key above 0.
+__device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+__device__ __forceinline__ int32_t argmax_key_row(uint64_t k) {
+    return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+__device__ __forceinline__ float argmax_key_value(uint64_t k) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    return __builtin_bit_cast(float, (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, m), hi = __shfl_xor((uint32_t)(k >> 32), m);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
 // Sum over each row of 16 lanes with DPP (quad swaps, half-row mirror, row
 // mirror); every lane of the row receives the sum.
 __device__ __forceinline__ float row16_sum(float v) {

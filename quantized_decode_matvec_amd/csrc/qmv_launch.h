@@ -25,10 +25,8 @@ hipError_t launch_matvec_mfma(int fmt, const uint8_t *codes, const void *plane, 
 bool km4_tiled_supported(int64_t K, int B);
 size_t km4_tiled_bytes(int64_t N, int64_t K);
 hipError_t launch_tile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *out, hipStream_t st);
-// hdr: if not null, the first workgroup zeroes kArgmaxHeader words there (the
-// argmax launch that follows reduces y into them)
 hipError_t launch_matvec_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
-                                   const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *hdr = nullptr);
+                                   const _Float16 *x, int B, float *y, hipStream_t st);
 // the same with the int8 outliers of the km4 + outlier format (nout >= 1)
 hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, const uint16_t *ocol,
                                     const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
@@ -37,7 +35,10 @@ hipError_t launch_matvec_km4o_tiled(const uint8_t *codes, const uint16_t *lut, c
 // zeroed header hdr (matvec.hip)
 hipError_t launch_argmax_rows(const float *y, int64_t N, int B, uint64_t *hdr, int32_t *idx, float *val,
                               hipStream_t st);
-// tiled km4 matvec into the argmax workspace, then the argmax launch
+// greedy token from the tiled km4 plane: the matvec writes one argmax key per
+// workgroup and batch row into the workspace (km4_tiled_argmax_keys_bytes at
+// most, no logits), then one small launch takes the largest
+size_t km4_tiled_argmax_keys_bytes(int64_t N, int B);
 hipError_t launch_argmax_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                                    const _Float16 *x, int B, int32_t *idx, float *val, void *workspace,
                                    hipStream_t st);

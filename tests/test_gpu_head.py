@@ -165,12 +165,14 @@ def test_embed_gather_large_table():
     assert np.array_equal(host(out).view(np.uint16), oracle.embed_gather_int8(q, s, ids))
 
 
-@pytest.mark.parametrize("N,K,Bs", [(3000, 2048, (1, 2, 4)), (70000, 2048, (1, 3)), (517, 1024, (1,)),
-                                    (1, 512, (1, 2))])
+@pytest.mark.parametrize("N,K,Bs", [(3000, 2048, (1, 2, 4)), (70000, 2048, (1, 2, 3)), (517, 1024, (1,)),
+                                    (1, 512, (1, 2)), (700, 4096, (1, 3, 4)), (66001, 1024, (2, 4))])
 def test_argmax_km4_tiled_parity(N, K, Bs):
-    """The fused argmax from the row-tiled plane: same winner and value as the
-    argmax of qmatvec_km4_tiled's y, within tolerance of the oracle maximum,
-    planted winners exact, identical winners to the lowest row."""
+    """The fused argmax from the row-tiled plane (one key per workgroup, then
+    the largest): same winner and value as the argmax of qmatvec_km4_tiled's
+    y, within tolerance of the oracle maximum, planted winners exact, identical
+    winners to the lowest row; one and two tiles per workgroup, the dot2 and
+    matrix-core kernels, a ragged last tile."""
     print("argmax km4 tiled", N, K, Bs, flush=True)
     c = wl.small_dense("km4", N, K, batch=4, seed=N + K + 1)
     W = c.W.copy()
