@@ -46,18 +46,24 @@ def test_km4_quad_kernel_on_sampled_rows(N, K):
         assert rel_err(y[:, rows], oracle.matvec("km4", oc, ol, c.x[:B])) <= RTOL, B
 
 
-def test_km4_quad_argmax_matches_its_matvec():
+@pytest.mark.parametrize("N,K", [(16384 + 13, 2048), (32768 + 5, 1024), (196608 + 3, 512), (65536 + 9, 2048)])
+def test_km4_quad_argmax_matches_its_matvec(N, K):
     """The fused argmax runs the same matvec kernel, so its index is the
-    argmax of the plain call's output and its value that output's maximum."""
-    N, K = 16384 + 13, 2048
+    argmax of the plain call's output and its value that output's maximum;
+    two identical planted rows tie and the lower wins. One, two and four row
+    quads per wave, one and two token quads."""
+    print("km4 quad argmax", N, K, flush=True)
     c = wl.small_dense("km4", N, K, batch=8, seed=5)
-    codes, lut = qmv.qpack_km4(dev(c.W))
-    for B in (3, 4, 8):
+    W = c.W.copy()
+    W[N - 3] = W[7] = (np.sign(c.x[0]) * 0.06).astype(W.dtype)
+    codes, lut = qmv.qpack_km4(dev(W))
+    for B in (3, 4, 5, 8):
         x = dev(c.x[:B])
         y = host(qmv.qmatvec_km4(codes, lut, x))
         idx, val = qmv.qmatvec_argmax("km4", codes, lut, x)
         assert host(idx).tolist() == np.argmax(y, axis=1).tolist()
         assert np.array_equal(host(val), y.max(axis=1))
+        assert host(idx)[0] == 7
 
 
 SCALED_CASES = [
