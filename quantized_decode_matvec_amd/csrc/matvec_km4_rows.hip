@@ -233,7 +233,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     }
 }
 
-// Batch 3-4 on the same tiles with the products on the matrix cores:
+// Batch 2-4 on the same tiles with the products on the matrix cores:
 // v_mfma_f32_4x4x4_16b_f16 runs 16 blocks of D[4 tokens][4 rows] +=
 // A[4 tokens][4 k] B[4 k][4 rows]; lane 4b + j supplies column j of block b's
 // B, i.e. 4 k-values of its own row 4b + j (the two pair-table lookups of two
@@ -430,9 +430,10 @@ static hipError_t launch_km4_tiled(const uint8_t *codes, const uint16_t *lut, in
                                    int64_t *grid, const TiledOutliers *ol) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     const bool two = tiles >= 4 * (int64_t)device_cu_count();
-    // batch 3-4: products on the matrix cores (the x stage fits up to K = 2048;
-    // 248320 x 2048: 51 us against 61-70 us for B v_dot2 per lookup)
-    if (ol == nullptr && B >= 3 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, keys, grid);
+    // batch 2-4: products on the matrix cores (the x stage fits up to K = 2048;
+    // 248320 x 2048: 51 us against 53 / 61-70 us for B = 2 / 3-4 v_dot2 per
+    // lookup)
+    if (ol == nullptr && B >= 2 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, keys, grid);
     switch (B) {
     case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
     case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
