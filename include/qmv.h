@@ -176,7 +176,7 @@ qmv_status qtile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *tiled,
 
 /* y[b][n] = sum_k lut[n][code(n, k)] * x[b][k], fp32 accumulation, from the
  * tiled plane and qpack_km4's lut [N][16] (4-byte aligned). 1 <= B <= 4, x fp16
- * [B][K], K in {512, 1024, 2048, 4096} (QMV_E_SHAPE otherwise, QMV_E_DTYPE
+ * [B][K], K a multiple of 512 up to 4096 (QMV_E_SHAPE otherwise, QMV_E_DTYPE
  * for fp32 x); y fp32 [B][N]. */
 qmv_status qmatvec_km4_tiled(const uint8_t *tiled, const uint16_t *lut, int64_t N, int64_t K,
                              const void *x, qmv_dtype xdt, int B, float *y, void *stream);
@@ -214,7 +214,7 @@ qmv_status qmatvec_km4o(const uint8_t *codes, const uint16_t *lut, const uint16_
 
 /* qmatvec_km4o from the row-tiled code plane (qtile_km4 of qpack_km4o's
  * codes): the tables and outlier arrays as qmatvec_km4o, x fp16 [B][K],
- * 1 <= B <= 4, K in {512, 1024, 2048, 4096}, 0 <= nout <= 256. */
+ * 1 <= B <= 4, K a multiple of 512 up to 4096, 0 <= nout <= 256. */
 qmv_status qmatvec_km4o_tiled(const uint8_t *tiled, const uint16_t *lut, const uint16_t *ocol,
                               const int8_t *oval, const uint16_t *oscale, int64_t N, int64_t K, int nout,
                               const void *x, qmv_dtype xdt, int B, float *y, void *stream);

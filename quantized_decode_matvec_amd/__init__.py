@@ -398,8 +398,8 @@ def _tiled_args(fn, tiled, lut, x, y):
     if x2.dim() != 2 or not 1 <= x2.shape[0] <= 4:
         _bad(fn, "x must be [K] or [B, K] with 1 <= B <= 4, got shape %s" % (tuple(x.shape),))
     B, K = x2.shape
-    if K not in (512, 1024, 2048, 4096):
-        _bad(fn, "K = %d: the tiled kernel takes K in 512, 1024, 2048, 4096" % K)
+    if K < 512 or K > 4096 or K % 512:
+        _bad(fn, "K = %d: the tiled kernel takes K a multiple of 512 up to 4096" % K)
     _tensor(fn, "tiled", tiled, shape=(qtile_km4_bytes(N, K),), itemsize=1)
     if y is _NO_Y:
         _on_gpu(fn, tiled, lut, x2)

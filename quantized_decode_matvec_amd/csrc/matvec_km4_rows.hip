@@ -379,6 +379,7 @@ static hipError_t launch_km4_tiled_mfma(const uint8_t *codes, const uint16_t *lu
     switch (K) {
     case 512: return launch_tiled_mfma<1>(codes, lut, N, x, B, y, st, keys, grid);
     case 1024: return launch_tiled_mfma<2>(codes, lut, N, x, B, y, st, keys, grid);
+    case 1536: return launch_tiled_mfma<3>(codes, lut, N, x, B, y, st, keys, grid);
     case 2048: return launch_tiled_mfma<4>(codes, lut, N, x, B, y, st, keys, grid);
     default: return hipErrorInvalidValue;
     }
@@ -402,9 +403,9 @@ static hipError_t launch_tiled(const uint8_t *codes, const uint16_t *lut, int64_
     return hipGetLastError();
 }
 
-// two tiles per workgroup once there are enough workgroups to keep two on
-// every CU; fewer tiles spread one per workgroup; K = 4096 holds 32 code
-// registers per tile and takes one
+// K = 512 CPW (CPW = 1..8). Two tiles per workgroup once there are enough
+// workgroups to keep two on every CU; fewer tiles spread one per workgroup;
+// from K = 2560 a tile holds 20 or more code registers and a workgroup takes one
 template <int BT>
 static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K, const _Float16 *x,
                                  float *y, bool two, hipStream_t st, uint64_t *keys, int64_t *grid,
@@ -414,15 +415,20 @@ static hipError_t launch_tiled_b(const uint8_t *codes, const uint16_t *lut, int6
                          : launch_tiled<1, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
     case 1024: return two ? launch_tiled<2, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
                           : launch_tiled<2, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 1536: return two ? launch_tiled<3, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
+                          : launch_tiled<3, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
     case 2048: return two ? launch_tiled<4, 2, BT>(codes, lut, N, x, y, st, keys, grid, ol)
                           : launch_tiled<4, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 2560: return launch_tiled<5, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 3072: return launch_tiled<6, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
+    case 3584: return launch_tiled<7, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
     case 4096: return launch_tiled<8, 1, BT>(codes, lut, N, x, y, st, keys, grid, ol);
     default: return hipErrorInvalidValue;
     }
 }
 
 bool km4_tiled_supported(int64_t K, int B) {
-    return (K == 512 || K == 1024 || K == 2048 || K == 4096) && B >= 1 && B <= 4;
+    return K >= 512 && K <= 4096 && K % 512 == 0 && B >= 1 && B <= 4;
 }
 
 static hipError_t launch_km4_tiled(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,

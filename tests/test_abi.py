@@ -172,7 +172,8 @@ def test_tiled_km4_validation(L):
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 0, 1, FAKE, S) == E_DTYPE   # fp32 x
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 5, FAKE, S) == E_SHAPE   # batch 1..4
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, 0, FAKE, S) == E_SHAPE
-    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K not a tile width
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 1280, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K not a tile width
+    assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 4608, FAKE, 1, 1, FAKE, S) == E_SHAPE   # K past 4096
     assert L.qmatvec_km4_tiled(FAKE, FAKE, 64, 8192, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4_tiled(FAKE, half, 64, 2048, FAKE, 1, 1, FAKE, S) == E_ALIGN   # 32-bit table words
 
@@ -180,7 +181,7 @@ def test_tiled_km4_validation(L):
 def test_tiled_argmax_validation(L):
     ws = ctypes.c_size_t(1 << 20)
     assert L.qmatvec_argmax_km4_tiled(NUL, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_NULL
-    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 1536, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
+    assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 1280, FAKE, 1, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
     assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 5, FAKE, FAKE, FAKE, ws, S) == E_SHAPE
     assert L.qmatvec_argmax_km4_tiled(FAKE, FAKE, 64, 2048, FAKE, 1, FAKE, FAKE, FAKE, ctypes.c_size_t(64), S) \
         == E_WORKSPACE
@@ -193,6 +194,6 @@ def test_tiled_km4o_validation(L):
     assert L.qmatvec_km4o_tiled(FAKE, FAKE, NUL, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 1, FAKE, S) == E_NULL
     assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 4, FAKE, 0, 1, FAKE, S) == E_DTYPE
     assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 300, FAKE, 1, 1, FAKE, S) == E_SHAPE
-    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1536, 4, FAKE, 1, 1, FAKE, S) == E_SHAPE
+    assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 1280, 4, FAKE, 1, 1, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4o_tiled(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 5, FAKE, S) == E_SHAPE
     assert L.qmatvec_km4o_tiled(FAKE, FAKE, ODD, FAKE, FAKE, 64, 2048, 4, FAKE, 1, 1, FAKE, S) == E_ALIGN

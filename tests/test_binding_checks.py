@@ -157,7 +157,7 @@ def test_tiled_km4_checks():
     raises(ValueError, "lut has shape", qmv.qmatvec_km4_tiled, t, z(N, 15, dtype=u16), x)
     raises(TypeError, "dtype", qmv.qmatvec_km4_tiled, t, lut, z(1, K, dtype=f32))
     raises(ValueError, r"1 <= B <= 4", qmv.qmatvec_km4_tiled, t, lut, z(5, K))
-    raises(ValueError, "K = 1536", qmv.qmatvec_km4_tiled, z(128 * 768, dtype=u8), lut, z(1, 1536))
+    raises(ValueError, "K = 1280", qmv.qmatvec_km4_tiled, z(128 * 640, dtype=u8), lut, z(1, 1280))
     raises(ValueError, "contiguous", qmv.qmatvec_km4_tiled, t, lut, z(1, 2 * K)[:, ::2])
     raises(ValueError, "GPU memory", qmv.qtile_km4, z(N, K // 2, dtype=u8))
     raises(ValueError, "tiled has shape", qmv.qtile_km4, z(N, K // 2, dtype=u8), tiled=z(N * K // 2, dtype=u8))

@@ -166,7 +166,8 @@ def test_embed_gather_large_table():
 
 
 @pytest.mark.parametrize("N,K,Bs", [(3000, 2048, (1, 2, 4)), (70000, 2048, (1, 2, 3)), (517, 1024, (1,)),
-                                    (1, 512, (1, 2)), (700, 4096, (1, 3, 4)), (66001, 1024, (2, 4))])
+                                    (1, 512, (1, 2)), (700, 4096, (1, 3, 4)), (66001, 1024, (2, 4)),
+                                    (1100, 1536, (1, 2, 4)), (800, 3072, (1, 3))])
 def test_argmax_km4_tiled_parity(N, K, Bs):
     """The fused argmax from the row-tiled plane (one key per workgroup, then
     the largest): same winner and value as the argmax of qmatvec_km4_tiled's

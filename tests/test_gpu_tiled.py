@@ -48,7 +48,8 @@ def test_tiled_reference_is_a_permutation():
 
 
 @pytest.mark.parametrize("N,K", [(1, 2048), (64, 512), (100, 1024), (4097, 2048), (3000, 4096),
-                                 (70000, 2048), (65600, 1024), (66000, 512)])
+                                 (70000, 2048), (65600, 1024), (66000, 512), (2000, 1536), (66000, 1536),
+                                 (1500, 2560), (700, 3072), (900, 3584)])
 def test_tiled_matvec_matches_oracle(N, K):
     print("tiled km4 N=%d K=%d" % (N, K), flush=True)
     codes, lut, x = case(N, K, seed=N + K)
@@ -59,7 +60,8 @@ def test_tiled_matvec_matches_oracle(N, K):
 
 
 @pytest.mark.parametrize("B", [2, 3, 4])
-@pytest.mark.parametrize("N,K", [(100, 512), (4097, 2048), (3000, 4096), (66001, 1024), (70000, 2048)])
+@pytest.mark.parametrize("N,K", [(100, 512), (4097, 2048), (3000, 4096), (66001, 1024), (70000, 2048),
+                                 (66001, 1536), (1500, 2560), (700, 3584)])
 def test_tiled_matvec_batches_match_oracle(N, K, B):
     print("tiled km4 N=%d K=%d B=%d" % (N, K, B), flush=True)
     codes, lut, x = case(N, K, seed=N + K + B, B=B)
