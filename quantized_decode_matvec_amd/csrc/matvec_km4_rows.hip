@@ -506,18 +506,21 @@ hipError_t launch_argmax_km4_tiled(const uint8_t *codes, const uint16_t *lut, in
     return hipGetLastError();
 }
 
-// Row-tiled copy of a canonical [N][K/2] code plane (one thread per 16-byte
-// chunk of the destination; rows past N are zero).
-__global__ void tile_codes_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst, int64_t N, int Q,
-                                  int64_t total) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // destination index
-    if (i >= total) return;
-    const int r = (int)(i % kRowsTile);
-    const int64_t tq = i / kRowsTile;
-    const int q = (int)(tq % Q);
-    const int64_t t = tq / Q;
-    const int64_t n = t * kRowsTile + r;
-    dst[i] = n < N ? src[n * Q + q] : make_uint4(0u, 0u, 0u, 0u);
+// Row-tiled copy of a canonical [N][K/2] code plane (rows past N are zero).
+// Workgroup b takes chunks 4 yb .. 4 yb + 3 of the 64 rows of tile t
+// (t, yb from b, one division per workgroup): lane r of each wave copies row
+// r's chunk, so a workgroup writes 4 KiB of consecutive destination bytes and
+// the next workgroup reads the rest of the same rows' cache lines.
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                         int64_t N, int Q, int nb) {
+    const uint32_t b = blockIdx.x;
+    const uint32_t t = b / (uint32_t)nb, yb = b - t * (uint32_t)nb;   // uniform
+    const int r = threadIdx.x & 63;
+    const int q = 4 * (int)yb + (threadIdx.x >> 6);
+    if (q >= Q) return;
+    const int64_t n = (int64_t)t * kRowsTile + r;
+    const uint4 v = n < N ? src[n * Q + q] : make_uint4(0u, 0u, 0u, 0u);
+    dst[((int64_t)t * Q + q) * kRowsTile + r] = v;
 }
 
 size_t km4_tiled_bytes(int64_t N, int64_t K) {
@@ -526,10 +529,12 @@ size_t km4_tiled_bytes(int64_t N, int64_t K) {
 
 hipError_t launch_tile_km4(const uint8_t *codes, int64_t N, int64_t K, uint8_t *out, hipStream_t st) {
     const int Q = (int)(K / 32);
-    const int64_t total = (int64_t)km4_tiled_bytes(N, K) / 16;
-    const int64_t grid = (total + 255) / 256;
+    const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
+    const int nb = (Q + 3) / 4;   // workgroups per tile
+    const int64_t grid = tiles * nb;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)grid), dim3(256), 0, st,
-                       reinterpret_cast<const uint4 *>(codes), reinterpret_cast<uint4 *>(out), N, Q, total);
+                       reinterpret_cast<const uint4 *>(codes), reinterpret_cast<uint4 *>(out), N, Q, nb);
     return hipGetLastError();
 }
 
