@@ -437,6 +437,9 @@ def main():
         msot = timed(lambda i: qmv.qmatvec_km4o_tiled(*pkt[i % len(pkt)], x1, y=y[:1]), args.steps, args.warmup)
         extras["km4o16_tiled_B1_us"] = round(msot * 1e3, 2)
         extras["km4o16_tiled_B1_GBps"] = round(nbo / (msot * 1e-3) / 1e9, 1)
+        msot4 = timed(lambda i: qmv.qmatvec_km4o_tiled(*pkt[i % len(pkt)], x8[:4], y=y[:4]), args.steps // 2,
+                      args.warmup)
+        extras["km4o16_tiled_B4_us"] = round(msot4 * 1e3, 2)
         del pkt
         del pks, pko
         # fp16 dense GEMV on the same shape (torch), for the per-op ratio against fp16

@@ -85,12 +85,22 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     // at [w][r ^ w ^ 16 (r & 1)], so that both the writes (one wave, 64 rows)
     // and the reads (16 waves' sums of two rows per half-wave) fall on
     // distinct banks
-    __shared__ __align__(16) uint32_t lds[kPairEntries * kRowsTile + BT * W * kRowsTile];
+    // OUTL: x [BT][K] after them where it fits in 80 KiB (the outliers'
+    // x values are read from there, not gathered from global memory)
+    constexpr bool XL = OUTL && (kPairEntries + BT * W) * kRowsTile * 4 + BT * K * 2 <= 80 * 1024;
+    __shared__ __align__(16) uint32_t lds[kPairEntries * kRowsTile + BT * W * kRowsTile + (XL ? BT * K / 2 : 0)];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int la = (wave & 3) * 2, hb = (wave >> 2) * 2;   // table words of this wave's build share
     const uint32_t roff = (uint32_t)lane * 4u;
     float *part = reinterpret_cast<float *>(lds + kPairEntries * kRowsTile);
+    // x[b][c] for the outliers: from the LDS copy where there is one
+    auto xval = [&](int b, int c) -> float {
+        if constexpr (XL)
+            return (float)reinterpret_cast<const _Float16 *>(lds + (kPairEntries + BT * W) * kRowsTile)[b * K + c];
+        else
+            return (float)x[(size_t)b * K + c];
+    };
     uint64_t kmax[BT];   // KEYS: this lane's largest key per batch row
 #pragma unroll
     for (int bb = 0; bb < BT; bb++) kmax[bb] = 0;
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
             const float sc = f16_bits_to_f32((uint16_t)osc_r[k]);
             const float tq = oww < ol.n ? (float)(int32_t)oval_r[k] * sc : 0.f;   // exact: 8 x 11 bits
 #pragma unroll
-            for (int bb = 0; bb < BT; bb++) oterm[bb] = tq * (float)x[(size_t)bb * K + ocol_r[k]];
+            for (int bb = 0; bb < BT; bb++) oterm[bb] = tq * xval(bb, (int)ocol_r[k]);
         }
         float acc[BT][2];
 #pragma unroll
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
                 const float tq = (float)ol.val[rc * ol.n + o] * sc;
                 const int col = ol.col[rc * ol.n + o];
 #pragma unroll
-                for (int bb = 0; bb < BT; bb++) oterm[bb] = __builtin_fmaf(tq, (float)x[(size_t)bb * K + col], oterm[bb]);
+                for (int bb = 0; bb < BT; bb++) oterm[bb] = __builtin_fmaf(tq, xval(bb, col), oterm[bb]);
             }
         }
 #pragma unroll
@@ -205,6 +215,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
         }
     };
     const int64_t t0 = (int64_t)blockIdx.x * TPW;
+    if constexpr (XL) {
+        // x into LDS (visible after the first tile's build barrier)
+        uint32_t *xl = lds + (kPairEntries + BT * W) * kRowsTile;
+        for (int i = threadIdx.x; i < BT * K / 2; i += 64 * W) xl[i] = reinterpret_cast<const uint32_t *>(x)[i];
+    }
     load(t0, 0);
     if constexpr (TPW == 1) {
         step(t0, 0);
@@ -247,10 +262,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 // workgroups per CU, so K <= 2048, and the partial sums [4][W][64] go to the
 // table region once a tile's lookups are done (two more barriers per tile).
 // KEYS: as in mv_km4_tiled (the wave keys go to the x stage, free by then).
-template <int CPW, bool KEYS = false>
+// OUTL: the int8 outliers, added as in mv_km4_tiled.
+template <int CPW, bool KEYS = false, bool OUTL = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) void mv_km4_tiled_mfma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ lut, int64_t N, const _Float16 *__restrict__ x,
-    int B, float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ keys) {
+    int B, float *__restrict__ y, int64_t tiles, uint64_t *__restrict__ keys, TiledOutliers ol) {
     constexpr int W = kTileWaves;
     constexpr int Q = W * CPW;   // chunks per row
     constexpr int K = Q * 32;
@@ -276,6 +292,18 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
     const uint8_t *tb = codes + ((size_t)t * Q + CPW * wave) * (kRowsTile * 16) + lane * 16;
 #pragma unroll
     for (int j = 0; j < CPW; j++) cw[j] = load_stream16(tb + j * (kRowsTile * 16));
+    // outliers: this lane sums row rr = 4 wave + (lane >> 4) below and takes
+    // its outlier ww = lane & 15 (column, value, row scale)
+    const int rr = 4 * wave + (lane >> 4), ww = lane & 15;
+    const int64_t orow = t * kRowsTile + rr;
+    uint32_t ocol = 0, oval = 0, osc = 0;
+    if constexpr (OUTL) {
+        const int64_t rc = orow < N ? orow : N - 1;
+        const int o = ww < ol.n ? ww : 0;   // a lane without an outlier reads outlier 0 and drops it
+        ocol = ol.n > 0 ? ol.col[rc * ol.n + o] : 0u;
+        oval = ol.n > 0 ? (uint32_t)(int32_t)ol.val[rc * ol.n + o] : 0u;
+        osc = ol.scale[rc];
+    }
     constexpr int XPT = (4 * XU + 1023) / 1024;   // x units per thread
     uint4 xv[XPT];
 #pragma unroll
@@ -302,6 +330,17 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
             }
     }
     __syncthreads();
+    // outliers: x at this lane's outlier column, read from the x stage
+    // (element c of token b at half 8 (b XU + ((c >> 3) ^ b)) + (c & 7); the
+    // rows past B are zero)
+    const _Float16 *xsh = reinterpret_cast<const _Float16 *>(xs);
+    auto xat = [&](int b, int c) { return (float)xsh[8 * (b * XU + ((c >> 3) ^ b)) + (c & 7)]; };
+    float oterm[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (OUTL) {
+        const float tq = ww < ol.n ? (float)(int32_t)oval * f16_bits_to_f32((uint16_t)osc) : 0.f;   // exact
+#pragma unroll
+        for (int b = 0; b < 4; b++) oterm[b] = tq * xat(b, (int)ocol);
+    }
     const int tj = lane & 3;   // this lane's token in the A operand
     const uint4 *xj = xs + tj * XU;
     f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -329,12 +368,21 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 #pragma unroll
     for (int b = 0; b < 4; b++) part[(b * W + wave) * kRowsTile + (lane ^ wave ^ ((lane & 1) << 4))] = acc[b];
     __syncthreads();
-    const int rr = 4 * wave + (lane >> 4), ww = lane & 15;
-    const int64_t orow = t * kRowsTile + rr;
+    if constexpr (OUTL) {
+        // outliers past the first 16 of a row
+        const int64_t rc = orow < N ? orow : N - 1;
+        const float sc = f16_bits_to_f32(ol.scale[rc]);
+        for (int o = ww + 16; o < ol.n; o += 16) {
+            const float tq = (float)ol.val[rc * ol.n + o] * sc;
+            const int col = ol.col[rc * ol.n + o];
+#pragma unroll
+            for (int b = 0; b < 4; b++) oterm[b] = __builtin_fmaf(tq, xat(b, col), oterm[b]);
+        }
+    }
     uint64_t km[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-        const float sum = row16_sum(part[(b * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))]);
+        const float sum = row16_sum(part[(b * W + ww) * kRowsTile + (rr ^ ww ^ ((rr & 1) << 4))] + oterm[b]);
         km[b] = 0;
         if (ww == 0 && b < B && orow < N) {
             if constexpr (KEYS) km[b] = argmax_key(sum, orow);
@@ -361,26 +409,30 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(8, 8))) vo
 // (the number of keys per batch row) in *grid when grid is not null.
 template <int CPW>
 static hipError_t launch_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int64_t N, const _Float16 *x, int B,
-                                    float *y, hipStream_t st, uint64_t *keys, int64_t *grid) {
+                                    float *y, hipStream_t st, uint64_t *keys, int64_t *grid, const TiledOutliers *ol) {
     const int64_t tiles = (N + kRowsTile - 1) / kRowsTile;
     if (grid != nullptr) *grid = tiles;
-    if (keys != nullptr)
-        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW, true>), dim3((unsigned)tiles), dim3(64 * kTileWaves), 0, st, codes,
-                           lut, N, x, B, y, tiles, keys);
+    const dim3 g((unsigned)tiles), blk(64 * kTileWaves);
+    if (ol != nullptr)
+        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW, false, true>), g, blk, 0, st, codes, lut, N, x, B, y, tiles, nullptr,
+                           *ol);
+    else if (keys != nullptr)
+        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW, true>), g, blk, 0, st, codes, lut, N, x, B, y, tiles, keys,
+                           TiledOutliers());
     else
-        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW>), dim3((unsigned)tiles), dim3(64 * kTileWaves), 0, st, codes, lut,
-                           N, x, B, y, tiles, nullptr);
+        hipLaunchKernelGGL((mv_km4_tiled_mfma<CPW>), g, blk, 0, st, codes, lut, N, x, B, y, tiles, nullptr,
+                           TiledOutliers());
     return hipGetLastError();
 }
 
 static hipError_t launch_km4_tiled_mfma(const uint8_t *codes, const uint16_t *lut, int64_t N, int64_t K,
                                         const _Float16 *x, int B, float *y, hipStream_t st, uint64_t *keys,
-                                        int64_t *grid) {
+                                        int64_t *grid, const TiledOutliers *ol) {
     switch (K) {
-    case 512: return launch_tiled_mfma<1>(codes, lut, N, x, B, y, st, keys, grid);
-    case 1024: return launch_tiled_mfma<2>(codes, lut, N, x, B, y, st, keys, grid);
-    case 1536: return launch_tiled_mfma<3>(codes, lut, N, x, B, y, st, keys, grid);
-    case 2048: return launch_tiled_mfma<4>(codes, lut, N, x, B, y, st, keys, grid);
+    case 512: return launch_tiled_mfma<1>(codes, lut, N, x, B, y, st, keys, grid, ol);
+    case 1024: return launch_tiled_mfma<2>(codes, lut, N, x, B, y, st, keys, grid, ol);
+    case 1536: return launch_tiled_mfma<3>(codes, lut, N, x, B, y, st, keys, grid, ol);
+    case 2048: return launch_tiled_mfma<4>(codes, lut, N, x, B, y, st, keys, grid, ol);
     default: return hipErrorInvalidValue;
     }
 }
@@ -439,7 +491,7 @@ static hipError_t launch_km4_tiled(const uint8_t *codes, const uint16_t *lut, in
     // batch 2-4: products on the matrix cores (the x stage fits up to K = 2048;
     // 248320 x 2048: 51 us against 53 / 61-70 us for B = 2 / 3-4 v_dot2 per
     // lookup)
-    if (ol == nullptr && B >= 2 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, keys, grid);
+    if (B >= 2 && K <= 2048) return launch_km4_tiled_mfma(codes, lut, N, K, x, B, y, st, keys, grid, ol);
     switch (B) {
     case 1: return launch_tiled_b<1>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
     case 2: return launch_tiled_b<2>(codes, lut, N, K, x, y, two, st, keys, grid, ol);
