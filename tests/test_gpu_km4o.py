@@ -94,7 +94,8 @@ def test_gpu_pack_then_gpu_matvec_end_to_end():
 
 @pytest.mark.parametrize("N,K,nout,B", [(1037, 2048, 16, 1), (1037, 2048, 16, 2), (3000, 1024, 5, 4),
                                         (700, 512, 40, 1), (66001, 2048, 16, 1), (100, 4096, 0, 3),
-                                        (257, 2048, 1, 2), (900, 1536, 16, 1), (500, 2560, 20, 2)])
+                                        (257, 2048, 1, 2), (900, 1536, 16, 1), (500, 2560, 20, 2),
+                                        (800, 1024, 40, 3), (66001, 2048, 16, 4)])
 def test_km4o_tiled_matches_oracle(N, K, nout, B):
     """The outlier format from the row-tiled codes: the 16 lanes that sum a
     row take its outliers (one each, more past 16)."""
