@@ -517,7 +517,18 @@ def main():
         extras["km4_shard8_%d_us" % ns] = round(mss * 1e3, 2)
         extras["km4_shard8_%d_GBps" % ns] = round(algo_bytes("km4", ns, K_DIM) / (mss * 1e-3) / 1e9, 1)
         extras["km4_shard8_%d_argmax_us" % ns] = round(msx * 1e3, 2)
-        del sl, wss
+        # the same shares of the row-tiled planes (31040 rows = 485 whole tiles)
+        tb = qmv.qtile_km4_bytes(ns, K_DIM)
+        slt = [(tc[s * tb:(s + 1) * tb], ll[s * ns:(s + 1) * ns]) for tc, ll in tiled for s in range(8)]
+        mst8 = timed_graph(lambda i: qmv.qmatvec_km4_tiled(slt[i % len(slt)][0], slt[i % len(slt)][1], x1,
+                                                           y=y[:1, :ns]), 4 * args.steps, per_graph=len(slt))
+        mstx = timed_graph(lambda i: qmv.qmatvec_argmax_km4_tiled(slt[i % len(slt)][0], slt[i % len(slt)][1], x1,
+                                                                  idx=aidx, val=aval, workspace=wss),
+                           4 * args.steps, per_graph=len(slt))
+        extras["km4_tiled_shard8_%d_us" % ns] = round(mst8 * 1e3, 2)
+        extras["km4_tiled_shard8_%d_GBps" % ns] = round(algo_bytes("km4", ns, K_DIM) / (mst8 * 1e-3) / 1e9, 1)
+        extras["km4_tiled_shard8_%d_argmax_us" % ns] = round(mstx * 1e3, 2)
+        del sl, slt, wss
         if not args.quick:
             extras.update(bench_fp4_square(args))
             extras.update(bench_int8_head(args))
